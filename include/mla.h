@@ -1,0 +1,184 @@
+/*
+ * mla.h -- C ABI of libmla: DeepSeek-V2-style Multi-head Latent Attention (MLA) decode over a
+ * paged latent KV cache with matrix absorption, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *  [P-vllm]   vLLM learning book ch. 07 "模型架构特异：MLA / Mamba / MoE 在 vLLM 源码层",
+ *             §2.1 算法核心, §2.2 vLLM 源码挂载点 (wrapper forward: down-projection, decoupled
+ *             RoPE, cache write by slot_mapping, attention), §2.3 (cache shape
+ *             (n_blocks, block, 1, latent_d + rope_d)), §2.4 Decoupled RoPE.
+ *  [P-mini]   mini-infer 17 "MLA Attention：从 KV Cache 压缩到矩阵吸收", sections
+ *             "MLA 的数学结构", 版本 1 (Naive), 版本 3 (矩阵吸收, _build_absorbed),
+ *             踩坑记录 坑 2 (causal mask) and 坑 3 (norm before absorption), 设计取舍.
+ *  [P-hybrid] bxzpzcl.cn, KV-cache management for hybrid models, §2.1 (block table maps
+ *             logical to physical pages; one cache per layer, pages shared by all requests).
+ *
+ * Conventions shared by every call
+ *  - Dimensions supported: kv_lora_rank (dc) 512, qk_rope_head_dim (dr) 64,
+ *    qk_nope_head_dim (dn) 128, v_head_dim (dv) 128, block_size 16, num_heads a multiple of 16.
+ *    Anything else returns MLA_EUNSUPPORTED.
+ *  - Storage dtype (mla_config.dtype) applies to q, c_kv, k_pe, the cache, the weights, gamma
+ *    and out.  MLA_BF16 computes scores and P*c_kv with bf16 MFMA inputs and fp32 accumulation;
+ *    MLA_F32 computes in fp32 throughout.  cache_write evaluates each row in fp64 and rounds once
+ *    (round to nearest even) in both modes.
+ *  - Every data pointer is DEVICE memory owned by the caller, borrowed until the work queued on
+ *    `stream` has completed.  `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *  - cache_write and decode are asynchronous: no host synchronisation, no allocation.
+ *  - Device-resident indices (positions, slot_mapping, block_table, seq_lens) are not read by
+ *    the host.  Out-of-range values are handled as documented per call, never by faulting.
+ *  - The context is not thread-safe: it owns one decode workspace.  Calls on one context must be
+ *    serialised on one stream.
+ *  - No C++ exception crosses this boundary; errors are returned as mla_status.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mla_ctx mla_ctx; /* opaque, library-owned */
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_EINVAL = -1,       /* null pointer, negative size, inconsistent argument */
+  MLA_EUNSUPPORTED = -2, /* dims or dtype outside the supported set */
+  MLA_ENOMEM = -3,       /* device allocation failed */
+  MLA_EHIP = -4,         /* a HIP runtime call or kernel launch failed */
+  MLA_ECAP = -5          /* a size exceeds the caps fixed at mla_absorb_weights */
+} mla_status;
+
+typedef struct {
+  int32_t num_heads;        /* H, multiple of 16 */
+  int32_t kv_lora_rank;     /* dc = 512 */
+  int32_t qk_nope_head_dim; /* dn = 128 */
+  int32_t qk_rope_head_dim; /* dr = 64 */
+  int32_t v_head_dim;       /* dv = 128 */
+  int32_t block_size;       /* 16 */
+  int32_t dtype;            /* mla_dtype */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(dn + dr) */
+  float rms_eps;            /* RMSNorm epsilon, e.g. 1e-6 */
+  float rope_theta;         /* RoPE base, e.g. 10000 */
+  int32_t max_q_tokens;     /* cap on batch * q_len per decode (sizes the workspace) */
+  int32_t max_batch;        /* cap on batch per decode */
+  int32_t max_position;     /* RoPE positions 0..max_position are supported */
+  int32_t max_seq_len;      /* cap on a context length (incl. new tokens) per decode */
+} mla_config;
+
+/*
+ * mla_absorb_weights -- S0 of the decode path: split kv_b_proj into the absorbed factors and
+ * build a context.  [P-mini] 版本 3 _build_absorbed views kv_b_proj as (H, dn + dv, dc): per
+ * head, the first dn rows form W_uk (folded into the query: q_lat = q_nope . W_uk) and the next
+ * dv rows form W_uv (applied last: out = o_lat . W_uv^T).  The copy is exact (no arithmetic);
+ * the library repacks both into its own kernel layouts.
+ *
+ *  cfg           host pointer, read during the call only.
+ *  kv_b_proj_w   device [H*(dn+dv), dc] row-major in the storage dtype, per-head row blocks of
+ *                dn nope rows then dv value rows.  May be freed after the call returns.
+ *  kv_norm_gamma device [dc] RMSNorm weight (kv_a_layernorm) in the storage dtype, or NULL for
+ *                all-ones.  Copied; may be freed after the call returns.
+ *  stream        hipStream_t; the call synchronises this stream once before returning.
+ *  out           receives the new context on MLA_OK, NULL otherwise.
+ * Returns MLA_EINVAL (null cfg/weights/out, non-positive caps), MLA_EUNSUPPORTED (dims, dtype),
+ * MLA_ENOMEM, MLA_EHIP.  The context owns W_uk/W_uv, gamma, an fp64 RoPE table for positions
+ * 0..max_position and the split-KV workspace (sized from the caps).
+ */
+mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, const void* kv_norm_gamma,
+                              void* stream, mla_ctx** out);
+
+/*
+ * mla_cache_write -- S1: [P-vllm] §2.2 steps 2-3 and §2.3.  For each new token j:
+ *   row = [ RMSNorm(c_kv[j]) * gamma  |  RoPE(k_pe[j], positions[j]) ]   (dc + dr values)
+ * stored at slot s = slot_mapping[j] = physical_block * 16 + offset, i.e. in
+ * kv_cache[s / 16][s % 16][0][:].  RMSNorm: x / sqrt(mean(x^2) + eps) ([P-mini] 坑 3, the
+ * kv_a_layernorm); RoPE: interleaved pairs (x[2i], x[2i+1]) rotated by p * theta^(-2i/dr)
+ * ([P-vllm] §2.4; the pairing is this library's reading, the pages leave it open).
+ * The row is evaluated in fp64 and rounded once to the storage dtype (round to nearest even).
+ *
+ *  c_kv, c_kv_row_stride  device [T, dc] raw (un-normed) latent; stride in elements (>= dc).
+ *  k_pe, k_pe_row_stride  device [T, dr] un-rotated rope key; stride in elements (>= dr).
+ *  positions              device int32 [T] RoPE position of each token.
+ *  slot_mapping           device int32 [T]; a negative slot skips the token (padding).
+ *  num_tokens             T >= 0 (0 is a no-op).
+ *  kv_cache, num_blocks   device [num_blocks, 16, 1, dc + dr] in the storage dtype.
+ * Device-side handling: a slot at or beyond num_blocks*16 is skipped; a position outside
+ * 0..max_position writes a row of NaN so that the error is visible downstream.
+ * Slots not named in slot_mapping are not touched.  Two tokens naming one slot race.
+ * Returns MLA_EINVAL (null ctx/pointers with T > 0, strides too small, num_blocks <= 0),
+ * MLA_EHIP on launch failure.
+ */
+mla_status mla_cache_write(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
+                           int64_t k_pe_row_stride, const int32_t* positions, const int32_t* slot_mapping,
+                           int32_t num_tokens, void* kv_cache, int32_t num_blocks, void* stream);
+
+/*
+ * mla_decode -- S2..S7: absorbed MLA attention over the paged latent cache ([P-mini] 版本 3
+ * reassociated; [P-hybrid] §2.1 paging).  For query i of sequence b (row n = b*q_len + i),
+ * position p = seq_lens[b] - q_len + i, and head h:
+ *   q_lat   = q[n,h,:dn] . W_uk[h]                         (dc values)
+ *   q_pe'   = RoPE(q[n,h,dn:], p)
+ *   s_t     = scale * (q_lat . c_t + q_pe' . k_pe_t)        for cache tokens t <= p, else masked
+ *             ([P-mini] 设计取舍 two-part score, 坑 2 causal mask)
+ *   o_lat   = softmax(s) . C                                 (dc values)
+ *   out[n,h]= o_lat . W_uv[h]^T                             (dv values)
+ * Cache token t of sequence b is the row kv_cache[block_table[b*stride + t/16]][t%16][0].
+ * The context is cut into splits processed in parallel; their (max, sum, acc) partials are
+ * merged by a log-sum-exp combine.  Results are deterministic for fixed inputs and split count.
+ *
+ *  q                    device [batch*q_len, H, dn + dr], per head [nope | rope] (rope un-rotated).
+ *  batch, q_len         batch >= 1, 1 <= q_len; batch <= max_batch, batch*q_len <= max_q_tokens.
+ *  kv_cache, num_blocks device [num_blocks, 16, 1, dc + dr] (already written for every t < ctx).
+ *  block_table, stride  device int32 [batch, stride]; entries for t >= ctx are not read.
+ *  seq_lens             device int32 [batch]: context length ctx_b INCLUDING the q_len new
+ *                       tokens (which must already be in the cache), q_len <= ctx_b <= max_seq_len.
+ *  max_seq_len          host int: an upper bound of every seq_lens[b] (sizes the launch).
+ *  out                  device [batch*q_len, H, dv] in the storage dtype (round to nearest even).
+ * Device-side handling: a block_table entry outside [0, num_blocks) reads as a block of zeros;
+ * seq_lens[b] is clamped to [q_len, max_seq_len].
+ * Returns MLA_EINVAL (null pointers, batch < 1, q_len < 1, max_seq_len < q_len, stride smaller
+ * than ceil(max_seq_len/16)), MLA_ECAP (batch, batch*q_len or max_seq_len above the caps, or
+ * max_seq_len - 1 above max_position), MLA_EHIP.
+ */
+mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+                      int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                      const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
+
+/*
+ * mla_free -- synchronises the device, then releases everything the context owns.
+ * NULL is accepted.  Using the context afterwards is undefined.
+ */
+void mla_free(mla_ctx* ctx);
+
+/* ------------------------------------------------------------------------------------------
+ * Inspection and tuning helpers (not part of the compute path).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_string(int32_t status);
+
+/* Force the split size in 16-token blocks for subsequent decodes (0 = automatic choice).
+ * Returns MLA_EINVAL for a negative value. */
+mla_status mla_set_split_blocks(mla_ctx* ctx, int32_t split_blocks);
+
+/* Launch shape of the most recent decode: split size in blocks, number of splits launched
+ * (grid x) and waves per workgroup.  Any pointer may be NULL. */
+mla_status mla_last_decode_shape(const mla_ctx* ctx, int32_t* split_blocks, int32_t* n_split,
+                                 int32_t* waves_per_group);
+
+/* Kernel timing with HIP events recorded on the launch stream around each kernel.
+ * enable != 0 starts recording (clears the totals); 0 stops.  Kernel ids: */
+enum { MLA_K_CACHE_WRITE = 0, MLA_K_Q_ABSORB = 1, MLA_K_DECODE = 2, MLA_K_COMBINE = 3, MLA_K_COUNT = 4 };
+mla_status mla_profile_enable(mla_ctx* ctx, int32_t enable);
+/* Synchronises the recorded events and returns the summed milliseconds and launch count of
+ * kernel `kernel_id` since profiling was enabled. */
+mla_status mla_profile_read(mla_ctx* ctx, int32_t kernel_id, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

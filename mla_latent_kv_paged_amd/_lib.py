@@ -1,0 +1,209 @@
+"""ctypes binding of libmla (include/mla.h): argument marshalling only.
+
+Every step of the path runs in the HIP library.  PyTorch supplies device memory and the
+current stream; this module checks tensor shapes/dtypes on the host and forwards raw
+pointers.  There is no fallback: if libmla.so is missing or fails to load, the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla.so")
+
+MLA_F32, MLA_BF16 = 0, 1
+MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2, -3, -4, -5
+K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
+
+EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_free", "mla_status_string",
+           "mla_set_split_blocks", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read")
+
+
+class MLAConfig(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
+                ("qk_nope_head_dim", ctypes.c_int32), ("qk_rope_head_dim", ctypes.c_int32),
+                ("v_head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("max_q_tokens", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_position", ctypes.c_int32), ("max_seq_len", ctypes.c_int32)]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load(path=None):
+    """Load libmla.so (once).  Raises OSError if it is missing or does not load."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"libmla.so not found at {p}: build it with `python -m mla_latent_kv_paged_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.mla_absorb_weights.argtypes = [ctypes.POINTER(MLAConfig), vp, vp, vp, ctypes.POINTER(vp)]
+    lib.mla_absorb_weights.restype = i32
+    lib.mla_cache_write.argtypes = [vp, vp, i64, vp, i64, vp, vp, i32, vp, i32, vp]
+    lib.mla_cache_write.restype = i32
+    lib.mla_decode.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
+    lib.mla_decode.restype = i32
+    lib.mla_free.argtypes = [vp]
+    lib.mla_free.restype = None
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_set_split_blocks.argtypes = [vp, i32]
+    lib.mla_set_split_blocks.restype = i32
+    lib.mla_last_decode_shape.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.mla_last_decode_shape.restype = i32
+    lib.mla_profile_enable.argtypes = [vp, i32]
+    lib.mla_profile_enable.restype = i32
+    lib.mla_profile_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.mla_profile_read.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status):
+    try:
+        return load().mla_status_string(int(status)).decode()
+    except OSError:
+        return f"status {status}"
+
+
+def _check(status, where):
+    if status != MLA_OK:
+        raise MLAError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype=None, device=True, contiguous=True, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class MLAContext:
+    """Owns one mla_ctx (absorbed weights, RoPE table, decode workspace)."""
+
+    def __init__(self, kv_b_proj, gamma=None, *, num_heads, dtype="bf16", softmax_scale=0.0, rms_eps=1e-6,
+                 rope_theta=10000.0, max_q_tokens=1024, max_batch=1024, max_position=32768, max_seq_len=32768,
+                 stream=None):
+        torch = _torch()
+        self.lib = load()
+        self.storage = dtype
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.num_heads = num_heads
+        _need(kv_b_proj, "kv_b_proj", self.tdtype, shape=(num_heads * 256, 512))
+        if gamma is not None:
+            _need(gamma, "gamma", self.tdtype, shape=(512,))
+        cfg = MLAConfig(num_heads, 512, 128, 64, 128, 16, MLA_BF16 if dtype == "bf16" else MLA_F32,
+                        softmax_scale, rms_eps, rope_theta, max_q_tokens, max_batch, max_position, max_seq_len)
+        self.cfg = cfg
+        h = ctypes.c_void_p()
+        _check(self.lib.mla_absorb_weights(ctypes.byref(cfg), _ptr(kv_b_proj), _ptr(gamma), _stream_ptr(stream),
+                                           ctypes.byref(h)), "mla_absorb_weights")
+        self.handle = h
+
+    # -- lifetime
+    def free(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            self.lib.mla_free(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    # -- the two per-step calls
+    def cache_write(self, c_kv, k_pe, positions, slot_mapping, kv_cache, stream=None):
+        torch = _torch()
+        T = int(positions.shape[0]) if positions is not None else 0
+        _need(kv_cache, "kv_cache", self.tdtype)
+        if kv_cache.dim() != 4 or tuple(kv_cache.shape[1:]) != (16, 1, 576):
+            raise ValueError("kv_cache must be [n_blocks, 16, 1, 576]")
+        if T:
+            _need(c_kv, "c_kv", self.tdtype, contiguous=False)
+            _need(k_pe, "k_pe", self.tdtype, contiguous=False)
+            _need(positions, "positions", torch.int32, shape=(T,))
+            _need(slot_mapping, "slot_mapping", torch.int32, shape=(T,))
+            if c_kv.shape != (T, 512) or c_kv.stride(1) != 1 or k_pe.shape != (T, 64) or k_pe.stride(1) != 1:
+                raise ValueError("c_kv must be [T, 512] and k_pe [T, 64] with unit inner stride")
+        st = self.lib.mla_cache_write(self.handle, _ptr(c_kv), c_kv.stride(0) if T else 512, _ptr(k_pe),
+                                      k_pe.stride(0) if T else 64, _ptr(positions), _ptr(slot_mapping), T,
+                                      _ptr(kv_cache), int(kv_cache.shape[0]), _stream_ptr(stream))
+        _check(st, "mla_cache_write")
+
+    def decode(self, q, kv_cache, block_table, seq_lens, max_seq_len, q_len=1, out=None, stream=None):
+        torch = _torch()
+        H = self.num_heads
+        batch = int(seq_lens.shape[0])
+        _need(q, "q", self.tdtype, shape=(batch * q_len, H, 192))
+        _need(kv_cache, "kv_cache", self.tdtype)
+        _need(block_table, "block_table", torch.int32)
+        _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+        if block_table.dim() != 2 or block_table.shape[0] != batch:
+            raise ValueError("block_table must be [batch, stride]")
+        if out is None:
+            out = torch.empty((batch * q_len, H, 128), dtype=self.tdtype, device=q.device)
+        _need(out, "out", self.tdtype, shape=(batch * q_len, H, 128))
+        st = self.lib.mla_decode(self.handle, _ptr(q), batch, q_len, _ptr(kv_cache), int(kv_cache.shape[0]),
+                                 _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                                 _ptr(out), _stream_ptr(stream))
+        _check(st, "mla_decode")
+        return out
+
+    # -- helpers
+    def set_split_blocks(self, n):
+        _check(self.lib.mla_set_split_blocks(self.handle, int(n)), "mla_set_split_blocks")
+
+    def last_decode_shape(self):
+        a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self.lib.mla_last_decode_shape(self.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+               "mla_last_decode_shape")
+        return dict(split_blocks=a.value, n_split=b.value, waves=c.value)
+
+    def profile_enable(self, on=True):
+        _check(self.lib.mla_profile_enable(self.handle, 1 if on else 0), "mla_profile_enable")
+
+    def profile_read(self, kernel_id):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(self.lib.mla_profile_read(self.handle, int(kernel_id), ctypes.byref(ms), ctypes.byref(n)),
+               "mla_profile_read")
+        return ms.value, n.value
+
+
+def default_scale():
+    return 1.0 / math.sqrt(192.0)

@@ -1,0 +1,352 @@
+// Host side of libmla: argument validation, context ownership, workspace sizing, the split
+// heuristic and the launch sequence of one decode step.  Every entry point is extern "C" and
+// returns an mla_status; no exception crosses the boundary.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "mla_internal.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr int kMaxSplit = 32;      // upper bound of splits per sequence (sizes the workspace)
+constexpr int kProfRing = 1024;    // event pairs kept per kernel id while profiling
+
+struct Prof {
+  bool on = false;
+  hipEvent_t ev[MLA_K_COUNT][kProfRing][2] = {};
+  int64_t count[MLA_K_COUNT] = {};
+  double total_ms[MLA_K_COUNT] = {};
+  bool created = false;
+};
+
+}  // namespace
+
+struct mla_ctx {
+  mla_config cfg;
+  bool bf16 = false;
+  int device = 0;
+  int cu_count = 256;
+  float qscale = 0.f;
+  void* W_uk = nullptr;
+  void* W_uvT = nullptr;
+  double* gamma = nullptr;
+  double2* rope = nullptr;
+  void* qcat = nullptr;
+  float* part_acc = nullptr;
+  float2* part_ml = nullptr;
+  int32_t max_split = 1;
+  int32_t forced_split_blocks = 0;
+  int32_t last_split_blocks = 0, last_n_split = 0, last_waves = 0;
+  Prof prof;
+};
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+void ctx_release(mla_ctx* c) {
+  if (!c) return;
+  hipFree(c->W_uk);
+  hipFree(c->W_uvT);
+  hipFree(c->gamma);
+  hipFree(c->rope);
+  hipFree(c->qcat);
+  hipFree(c->part_acc);
+  hipFree(c->part_ml);
+  if (c->prof.created)
+    for (int k = 0; k < MLA_K_COUNT; ++k)
+      for (int i = 0; i < kProfRing; ++i) {
+        hipEventDestroy(c->prof.ev[k][i][0]);
+        hipEventDestroy(c->prof.ev[k][i][1]);
+      }
+  delete c;
+}
+
+// Accumulate the elapsed time of ring slot i of kernel k (waits for its events).
+void prof_harvest(mla_ctx* c, int k, int64_t slot_count) {
+  const int i = int(slot_count % kProfRing);
+  float ms = 0.f;
+  if (hipEventSynchronize(c->prof.ev[k][i][1]) == hipSuccess &&
+      hipEventElapsedTime(&ms, c->prof.ev[k][i][0], c->prof.ev[k][i][1]) == hipSuccess)
+    c->prof.total_ms[k] += ms;
+}
+
+struct ProfScope {
+  mla_ctx* c;
+  int k;
+  hipStream_t s;
+  bool on;
+  ProfScope(mla_ctx* c_, int k_, hipStream_t s_) : c(c_), k(k_), s(s_), on(c_->prof.on) {
+    if (!on) return;
+    const int64_t n = c->prof.count[k];
+    if (n >= kProfRing) prof_harvest(c, k, n - kProfRing);  // slot about to be reused
+    hipEventRecord(c->prof.ev[k][n % kProfRing][0], s);
+  }
+  ~ProfScope() {
+    if (!on) return;
+    const int64_t n = c->prof.count[k];
+    hipEventRecord(c->prof.ev[k][n % kProfRing][1], s);
+    c->prof.count[k] = n + 1;
+  }
+};
+
+mla_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  if (e == hipErrorOutOfMemory) return MLA_ENOMEM;
+  return MLA_EHIP;
+}
+
+// Split size (in 16-token blocks) for a decode of `units` independent (sequence, row-tile)
+// work items whose longest context spans max_blocks blocks.  Aim for about one 8-wave
+// workgroup per CU in flight, keep at least one block per wave, and cap the split length so
+// that a few long sequences in a ragged batch do not serialise the tail.
+int choose_split_blocks(const mla_ctx* c, int units, int max_blocks, int waves) {
+  const int target = c->cu_count;
+  int n_target = (target + units - 1) / units;
+  if (n_target < 1) n_target = 1;
+  int sb = (max_blocks + n_target - 1) / n_target;
+  if (sb > 128) sb = 128;
+  if (sb < waves) sb = waves;
+  return sb;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_EINVAL: return "MLA_EINVAL: invalid argument";
+    case MLA_EUNSUPPORTED: return "MLA_EUNSUPPORTED: unsupported dimensions or dtype";
+    case MLA_ENOMEM: return "MLA_ENOMEM: device allocation failed";
+    case MLA_EHIP: return "MLA_EHIP: HIP runtime or launch failure";
+    case MLA_ECAP: return "MLA_ECAP: size exceeds the context caps";
+    default: return "unknown mla_status";
+  }
+}
+
+mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, const void* kv_norm_gamma,
+                              void* stream, mla_ctx** out) {
+  if (out) *out = nullptr;
+  if (!cfg || !kv_b_proj_w || !out) return MLA_EINVAL;
+  if (cfg->dtype != MLA_F32 && cfg->dtype != MLA_BF16) return MLA_EUNSUPPORTED;
+  if (cfg->kv_lora_rank != DC || cfg->qk_rope_head_dim != DR || cfg->qk_nope_head_dim != DN ||
+      cfg->v_head_dim != DV || cfg->block_size != BLK)
+    return MLA_EUNSUPPORTED;
+  if (cfg->num_heads <= 0 || cfg->num_heads % 16 != 0) return MLA_EUNSUPPORTED;
+  if (cfg->max_q_tokens <= 0 || cfg->max_batch <= 0 || cfg->max_position < 0 || cfg->max_seq_len <= 0)
+    return MLA_EINVAL;
+  if (!(cfg->rms_eps >= 0.f) || !(cfg->rope_theta > 0.f)) return MLA_EINVAL;
+  if (int64_t(cfg->max_q_tokens) * cfg->num_heads > (int64_t(1) << 24)) return MLA_ECAP;
+
+  mla_ctx* c = new (std::nothrow) mla_ctx();
+  if (!c) return MLA_ENOMEM;
+  c->cfg = *cfg;
+  c->bf16 = cfg->dtype == MLA_BF16;
+  hipStream_t s = as_stream(stream);
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    ctx_release(c);
+    return MLA_EHIP;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) == hipSuccess && prop.multiProcessorCount > 0)
+    c->cu_count = prop.multiProcessorCount;
+  const double scale = cfg->softmax_scale > 0.f ? double(cfg->softmax_scale) : 1.0 / std::sqrt(double(DN + DR));
+  c->qscale = float(scale * 1.4426950408889634);  // log2(e): scores in log2 units for exp2
+
+  const int H = cfg->num_heads;
+  const size_t esz = c->bf16 ? 2 : 4;
+  const int max_blocks = (cfg->max_seq_len + BLK - 1) / BLK;
+  c->max_split = max_blocks < kMaxSplit ? max_blocks : kMaxSplit;
+  const size_t rows = size_t(cfg->max_q_tokens) * H;
+  hipError_t e = hipSuccess;
+  auto alloc = [&](void** p, size_t n) {
+    if (e == hipSuccess) e = hipMalloc(p, n);
+  };
+  alloc(&c->W_uk, size_t(H) * DN * DC * esz);
+  alloc(&c->W_uvT, size_t(H) * DC * DV * esz);
+  alloc(reinterpret_cast<void**>(&c->gamma), DC * sizeof(double));
+  alloc(reinterpret_cast<void**>(&c->rope), size_t(cfg->max_position + 1) * NPAIR * sizeof(double2));
+  alloc(&c->qcat, rows * ROW * esz);
+  alloc(reinterpret_cast<void**>(&c->part_acc), rows * c->max_split * DC * sizeof(float));
+  alloc(reinterpret_cast<void**>(&c->part_ml), rows * c->max_split * sizeof(float2));
+  if (e != hipSuccess) {
+    ctx_release(c);
+    return hip_status(e);
+  }
+
+  // gamma -> fp64 (exact upcast of the storage values)
+  std::vector<double> g(DC, 1.0);
+  if (kv_norm_gamma) {
+    std::vector<uint8_t> raw(DC * esz);
+    e = hipMemcpyAsync(raw.data(), kv_norm_gamma, DC * esz, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      ctx_release(c);
+      return hip_status(e);
+    }
+    for (int i = 0; i < DC; ++i) {
+      if (c->bf16) {
+        uint16_t bits;
+        std::memcpy(&bits, raw.data() + 2 * i, 2);
+        uint32_t u = uint32_t(bits) << 16;
+        float f;
+        std::memcpy(&f, &u, 4);
+        g[i] = f;
+      } else {
+        float f;
+        std::memcpy(&f, raw.data() + 4 * i, 4);
+        g[i] = f;
+      }
+    }
+  }
+  // RoPE table: pair i at position p rotates by p * theta^(-2i/64); cos and sin in fp64
+  std::vector<double2> rope(size_t(cfg->max_position + 1) * NPAIR);
+  for (int i = 0; i < NPAIR; ++i) {
+    const double inv_freq = std::pow(double(cfg->rope_theta), -2.0 * i / double(DR));
+    for (int p = 0; p <= cfg->max_position; ++p) {
+      const double ang = double(p) * inv_freq;
+      rope[size_t(p) * NPAIR + i] = make_double2(std::cos(ang), std::sin(ang));
+    }
+  }
+  e = hipMemcpyAsync(c->gamma, g.data(), DC * sizeof(double), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->rope, rope.data(), rope.size() * sizeof(double2), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) {
+    AbsorbArgs aa{kv_b_proj_w, c->W_uk, c->W_uvT, H};
+    e = launch_absorb(c->bf16, aa, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    ctx_release(c);
+    return hip_status(e);
+  }
+  *out = c;
+  return MLA_OK;
+}
+
+mla_status mla_cache_write(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
+                           int64_t k_pe_row_stride, const int32_t* positions, const int32_t* slot_mapping,
+                           int32_t num_tokens, void* kv_cache, int32_t num_blocks, void* stream) {
+  if (!ctx || num_tokens < 0) return MLA_EINVAL;
+  if (num_tokens == 0) return MLA_OK;
+  if (!c_kv || !k_pe || !positions || !slot_mapping || !kv_cache || num_blocks <= 0) return MLA_EINVAL;
+  if (c_kv_row_stride < DC || k_pe_row_stride < DR) return MLA_EINVAL;
+  hipStream_t s = as_stream(stream);
+  CacheWriteArgs a{c_kv, c_kv_row_stride, k_pe, k_pe_row_stride, positions, slot_mapping, num_tokens,
+                   kv_cache, int64_t(num_blocks) * BLK, ctx->gamma, ctx->rope, ctx->cfg.max_position,
+                   double(ctx->cfg.rms_eps)};
+  ProfScope ps(ctx, MLA_K_CACHE_WRITE, s);
+  return hip_status(launch_cache_write(ctx->bf16, a, s));
+}
+
+mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+                      int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                      const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream) {
+  if (!ctx || !q || !kv_cache || !block_table || !seq_lens || !out) return MLA_EINVAL;
+  if (batch < 1 || q_len < 1 || num_blocks <= 0 || max_seq_len < q_len) return MLA_EINVAL;
+  const mla_config& cf = ctx->cfg;
+  if (batch > cf.max_batch || int64_t(batch) * q_len > cf.max_q_tokens || max_seq_len > cf.max_seq_len ||
+      max_seq_len - 1 > cf.max_position)
+    return MLA_ECAP;
+  const int max_blocks = (max_seq_len + BLK - 1) / BLK;
+  if (block_table_stride < max_blocks) return MLA_EINVAL;
+  hipStream_t s = as_stream(stream);
+  const int H = cf.num_heads;
+  const int n_q = batch * q_len;
+
+  const int waves = ctx->bf16 ? 8 : 1;
+  int sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
+                                        : choose_split_blocks(ctx, batch * (H / 16) * q_len, max_blocks, waves);
+  const int min_sb = (max_blocks + ctx->max_split - 1) / ctx->max_split;  // workspace bound
+  if (sb < min_sb) sb = min_sb;
+  if (sb > max_blocks) sb = max_blocks;
+  const int n_split = (max_blocks + sb - 1) / sb;
+  ctx->last_split_blocks = sb;
+  ctx->last_n_split = n_split;
+  ctx->last_waves = waves;
+
+  hipError_t e;
+  {
+    QAbsorbArgs qa{q, ctx->W_uk, ctx->rope, seq_lens, q_len, n_q, H, max_seq_len, cf.max_position, ctx->qscale,
+                   ctx->qcat};
+    ProfScope ps(ctx, MLA_K_Q_ABSORB, s);
+    e = launch_q_absorb(ctx->bf16, qa, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  {
+    DecodeArgs da{batch, kv_cache, num_blocks, block_table, block_table_stride, seq_lens, max_seq_len, q_len, H,
+                  ctx->qcat, ctx->part_acc, ctx->part_ml, sb, n_split};
+    ProfScope ps(ctx, MLA_K_DECODE, s);
+    e = launch_decode(ctx->bf16, da, waves, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  {
+    CombineArgs ca{ctx->part_acc, ctx->part_ml, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split, ctx->W_uvT, out};
+    ProfScope ps(ctx, MLA_K_COMBINE, s);
+    e = launch_combine(ctx->bf16, ca, s);
+  }
+  return hip_status(e);
+}
+
+void mla_free(mla_ctx* ctx) {
+  if (!ctx) return;
+  hipDeviceSynchronize();
+  ctx_release(ctx);
+}
+
+mla_status mla_set_split_blocks(mla_ctx* ctx, int32_t split_blocks) {
+  if (!ctx || split_blocks < 0) return MLA_EINVAL;
+  ctx->forced_split_blocks = split_blocks;
+  return MLA_OK;
+}
+
+mla_status mla_last_decode_shape(const mla_ctx* ctx, int32_t* split_blocks, int32_t* n_split,
+                                 int32_t* waves_per_group) {
+  if (!ctx) return MLA_EINVAL;
+  if (split_blocks) *split_blocks = ctx->last_split_blocks;
+  if (n_split) *n_split = ctx->last_n_split;
+  if (waves_per_group) *waves_per_group = ctx->last_waves;
+  return MLA_OK;
+}
+
+mla_status mla_profile_enable(mla_ctx* ctx, int32_t enable) {
+  if (!ctx) return MLA_EINVAL;
+  if (enable && !ctx->prof.created) {
+    for (int k = 0; k < MLA_K_COUNT; ++k)
+      for (int i = 0; i < kProfRing; ++i)
+        for (int h = 0; h < 2; ++h)
+          if (hipEventCreate(&ctx->prof.ev[k][i][h]) != hipSuccess) return MLA_EHIP;
+    ctx->prof.created = true;
+  }
+  if (enable)
+    for (int k = 0; k < MLA_K_COUNT; ++k) {
+      ctx->prof.count[k] = 0;
+      ctx->prof.total_ms[k] = 0.0;
+    }
+  ctx->prof.on = enable != 0;
+  return MLA_OK;
+}
+
+mla_status mla_profile_read(mla_ctx* ctx, int32_t kernel_id, double* total_ms, int64_t* launches) {
+  if (!ctx || kernel_id < 0 || kernel_id >= MLA_K_COUNT) return MLA_EINVAL;
+  const int64_t n = ctx->prof.count[kernel_id];
+  const int64_t first = n > kProfRing ? n - kProfRing : 0;
+  double extra = 0.0;
+  const double before = ctx->prof.total_ms[kernel_id];
+  for (int64_t i = first; i < n; ++i) prof_harvest(ctx, kernel_id, i);
+  extra = ctx->prof.total_ms[kernel_id] - before;
+  // the harvested slots stay in the ring: undo so that a second read does not double count
+  ctx->prof.total_ms[kernel_id] = before;
+  if (total_ms) *total_ms = before + extra;
+  if (launches) *launches = n;
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Internal declarations shared by the host API and the kernels of libmla (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// Fixed MLA dimensions (DeepSeek-V2 / V2-Lite shapes).
+constexpr int DC = 512;        // kv_lora_rank: latent width
+constexpr int DR = 64;         // qk_rope_head_dim: decoupled-RoPE key width
+constexpr int DN = 128;        // qk_nope_head_dim
+constexpr int DV = 128;        // v_head_dim
+constexpr int ROW = DC + DR;   // 576 values per cache slot
+constexpr int QW = DN + DR;    // 192 values per head of q
+constexpr int BLK = 16;        // tokens per paged block
+constexpr int NPAIR = DR / 2;  // RoPE pairs
+
+// ------------------------------------------------------------------------------ kernel arguments
+
+struct AbsorbArgs {
+  const void* kv_b_proj;  // [H*(DN+DV), DC]
+  void* W_uk;             // [H, DN, DC]
+  void* W_uvT;            // [H, DC, DV]
+  int32_t H;
+};
+
+struct CacheWriteArgs {
+  const void* c_kv;
+  int64_t c_stride;  // elements
+  const void* k_pe;
+  int64_t k_stride;  // elements
+  const int32_t* positions;
+  const int32_t* slots;
+  int32_t T;
+  void* cache;
+  int64_t num_slots;     // num_blocks * BLK
+  const double* gamma;   // [DC]
+  const double2* rope;   // [(max_position+1) * NPAIR] (cos, sin)
+  int32_t max_position;
+  double eps;
+};
+
+struct QAbsorbArgs {
+  const void* q;          // [n_q, H, QW]
+  const void* W_uk;       // [H, DN, DC]
+  const double2* rope;
+  const int32_t* seq_lens;
+  int32_t q_len;
+  int32_t n_q;
+  int32_t H;
+  int32_t max_seq_len;
+  int32_t max_position;
+  float qscale;           // softmax_scale * log2(e): scores come out in log2 units
+  void* qcat;             // [n_q, H, ROW] (storage dtype): [q_lat | q_pe'] * qscale
+};
+
+struct DecodeArgs {
+  int32_t batch;
+  const void* cache;
+  int32_t num_blocks;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t q_len;
+  int32_t H;
+  const void* qcat;
+  float* part_acc;        // [n_q*H*n_split, DC]
+  float2* part_ml;        // [n_q*H*n_split] (running max in log2 units, sum)
+  int32_t split_blocks;
+  int32_t n_split;
+};
+
+struct CombineArgs {
+  const float* part_acc;
+  const float2* part_ml;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t q_len;
+  int32_t n_q;
+  int32_t H;
+  int32_t split_blocks;
+  int32_t n_split;
+  const void* W_uvT;      // [H, DC, DV]
+  void* out;              // [n_q, H, DV]
+};
+
+// ------------------------------------------------------------------------------ launchers
+
+hipError_t launch_absorb(bool bf16, const AbsorbArgs& a, hipStream_t s);
+hipError_t launch_cache_write(bool bf16, const CacheWriteArgs& a, hipStream_t s);
+hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s);
+// waves: waves per workgroup of the bf16 decode kernel (ignored in fp32 mode)
+hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// double -> bf16 with a single rounding (nearest even): round to odd at fp32 precision first
+// (truncate, then set the sticky bit if anything was lost), then round to nearest even.
+// 24 bits >= 8 + 2, so the two steps give the correctly rounded result.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  float f = __double2float_rz(x);
+  if (double(f) != x && !__builtin_isnan(x)) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f32_to_bf16(f);
+}
+
+// Context length of sequence b as the kernels use it: clamped to [q_len, max_seq_len].
+__device__ __forceinline__ int clamp_ctx(int v, int q_len, int max_seq_len) {
+  return v < q_len ? q_len : (v > max_seq_len ? max_seq_len : v);
+}
+
+}  // namespace mla

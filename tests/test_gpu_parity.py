@@ -1,0 +1,178 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on seeded inputs.
+
+Small cases compare every element; the full-size workloads compare sampled sequences (all
+their rows and heads) computed one by one by the oracle, in the launch configuration the
+benchmark uses.  Tolerances: fp32 storage -> cache bit-exact and decode max abs <= 1e-4;
+bf16 storage -> cache within 1 bf16 ulp, decode max abs <= 2e-2 and relative L2 <= 5e-3."""
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from workloads import mla_inputs as W
+
+from ._harness import (GpuRun, bf16_ulp_distance, compare, dev, dev_i32, oracle_full, oracle_sequence,
+                       oracle_weights)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mla_latent_kv_paged_amd import load
+    load()  # the HIP library must load: no fallback
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _check_cache(run, cache_ref, storage):
+    got = run.pool_f64()
+    live = np.isfinite(cache_ref)
+    assert np.array_equal(np.isnan(got), ~live), "slots outside the written set changed"
+    if storage == "f32":
+        assert np.array_equal(got[live], cache_ref[live]), "fp32 cache not bit-exact"
+    else:
+        d = bf16_ulp_distance(got[live], cache_ref[live])
+        assert np.max(d) <= 1.0
+        assert np.mean(d > 0) <= 1e-4
+
+
+# ------------------------------------------------------------------------------- small, elementwise
+
+SMALL = [
+    ("tiny_f32", lambda: W.tiny()),
+    ("lite_b1_s1", lambda: W.lite_b1(1)),
+    ("lite_b1_s256", lambda: W.lite_b1(256)),
+    ("lite_b1_s1024", lambda: W.lite_b1(1024)),
+    ("lite_b4_s300", lambda: W.lite_b64(batch=4, seq_len=300, n_blocks=200)),
+    ("wide_h128_b2", lambda: W.wide(batch=2, lo=100, hi=700)),
+    ("ragged_b8_q4", lambda: W.ragged(batch=8, median=200, hi=900)),
+    ("ragged_b6_q4_f32", lambda: W.custom("r_f32", "f32", 16, [4, 5, 21, 64, 300, 17], q_len=4, seed=5)),
+    ("wide_f32", lambda: W.custom("w_f32", "f32", 32, [33, 80], q_len=1, seed=6)),
+    ("gamma_bf16", lambda: W.custom("g_bf16", "bf16", 16, [70, 129], q_len=2, seed=7, gamma_noise=0.1)),
+    ("gamma_f32", lambda: W.custom("g_f32", "f32", 16, [70, 129], q_len=2, seed=8, gamma_noise=0.1)),
+    ("ctx_eq_qlen", lambda: W.custom("edge", "bf16", 16, [1, 2, 3, 4, 16, 17], q_len=1, seed=9)),
+    ("ctx_eq_qlen4", lambda: W.custom("edge4", "bf16", 16, [4, 16, 17, 20], q_len=4, seed=10)),
+]
+
+
+@pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(name, make):
+    w = make()
+    _say(name, w.storage, "H", w.num_heads, "B", w.batch, "q_len", w.q_len, "ctx", list(w.seq_lens[:8]))
+    cache_ref, out_ref = oracle_full(w)
+    run = GpuRun(w)
+    try:
+        _check_cache(run, cache_ref, w.storage)
+        out = run.decode()
+        compare(out, out_ref, w.storage, name)
+    finally:
+        run.free()
+
+
+def test_decode_only_from_generator_pool():
+    """Decode alone on a pool filled directly by the generator (isolates decode error)."""
+    w = W.ragged(batch=6, median=150, hi=600, seed=21)
+    _say("decode-only ragged", list(w.seq_lens))
+    pool = w.random_pool()
+    W_uk, W_uv = oracle_weights(w)
+    ref = O.decode_absorbed(w.queries(), pool.astype(np.float64), w.block_table, w.seq_lens, w.q_len, W_uk, W_uv,
+                            w.scale, w.theta)
+    run = GpuRun(w)
+    try:
+        out = run.decode(pool=dev(pool, w.storage))
+        compare(out, ref, w.storage, "decode-only")
+    finally:
+        run.free()
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+def test_split_sweep_and_determinism(storage):
+    w = W.custom("sweep", storage, 16, [2, 37, 200, 513], q_len=2, seed=31)
+    _say("split sweep", storage)
+    _, ref = oracle_full(w)
+    run = GpuRun(w)
+    try:
+        for sb in (1, 2, 3, 5, 8, 13, 33, 0):
+            out = run.decode(split_blocks=sb)
+            compare(out, ref, storage, f"split_blocks={sb}")
+            again = run.decode(split_blocks=sb)
+            assert torch.equal(out, again), f"non-deterministic at split_blocks={sb}"
+    finally:
+        run.free()
+
+
+def test_block_table_relabel_invariance():
+    w = W.custom("relabel", "bf16", 16, [45, 130], q_len=1, seed=41)
+    _say("relabel")
+    run = GpuRun(w)
+    try:
+        base = run.decode()
+        perm = np.random.default_rng(3).permutation(w.n_blocks)
+        pool2 = torch.empty_like(run.pool)
+        pool2[torch.from_numpy(perm).cuda()] = run.pool
+        bt2 = dev_i32(perm[w.block_table])
+        out = run.ctx.decode(run.q, pool2, bt2, run.sl, run.max_ctx, q_len=w.q_len)
+        torch.cuda.synchronize()
+        assert torch.equal(out, base)
+    finally:
+        run.free()
+
+
+# ------------------------------------------------------------------------------- full size, sampled
+
+FULL = [
+    ("lite_b64_s4096", lambda: W.lite_b64(), (0, 31, 63)),
+    ("wide_h128_b128", lambda: W.wide(), (0, 77)),
+    ("ragged_b256_q4", lambda: W.ragged(), None),
+]
+
+
+@pytest.mark.parametrize("name,make,samples", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, make, samples):
+    w = make()
+    if samples is None:   # the longest, the shortest and a median sequence
+        order = np.argsort(w.seq_lens)
+        samples = (int(order[-1]), int(order[0]), int(order[len(order) // 2]))
+    _say(name, "B", w.batch, "sum ctx", w.total_ctx, "samples", samples)
+    run = GpuRun(w, per_sequence_upload=True)
+    try:
+        out = run.decode()
+        assert torch.isfinite(out.float()).all()
+        W_uk, W_uv = oracle_weights(w)
+        for b in samples:
+            ref = oracle_sequence(w, b, W_uk, W_uv)
+            rows = slice(b * w.q_len, (b + 1) * w.q_len)
+            compare(out[rows], ref, w.storage, f"{name} seq {b} (ctx {w.seq_lens[b]})")
+    finally:
+        run.free()
+
+
+# ------------------------------------------------------------------------------- ABI on the GPU
+
+def test_abi_status_codes_on_device():
+    from mla_latent_kv_paged_amd import MLAContext, MLAError
+    w = W.custom("abi", "bf16", 16, [20, 40], seed=51)
+    run = GpuRun(w)
+    try:
+        with pytest.raises(MLAError) as e:      # batch above the cap
+            bt = dev_i32(np.zeros((3, 8)))
+            run.ctx.decode(dev(np.zeros((3, 16, 192), np.float32), "bf16"), run.pool, bt,
+                           dev_i32([5, 5, 5]), 40)
+        assert e.value.status == -5
+        with pytest.raises(MLAError) as e:      # max_seq_len above the cap
+            run.ctx.decode(run.q, run.pool, run.bt, run.sl, 10 ** 6)
+        assert e.value.status == -5
+        with pytest.raises(MLAError) as e:      # block table narrower than max_seq_len needs
+            run.ctx.decode(run.q, run.pool, run.bt[:, :1].contiguous(), run.sl, 40)
+        assert e.value.status == -1
+        with pytest.raises(MLAError) as e:      # unsupported head count
+            MLAContext(dev(np.zeros((24 * 256, 512), np.float32), "bf16"), num_heads=24, dtype="bf16")
+        assert e.value.status == -2
+    finally:
+        run.free()
