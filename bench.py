@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA decode step over the paged latent cache on one MI355X.
+
+A step is one pass of the whole per-token hot path on one batch: mla_cache_write of the
+batch's new tokens (RMSNorm + RoPE + scatter) followed by mla_decode (query absorption, split-KV
+attention over the latent cache, log-sum-exp combine fused with W_uv).  The weight split
+(mla_absorb_weights) runs once per layer at load time; its time is reported separately.
+
+Default workload: DeepSeek-V2-Lite shapes (16 heads, kv_lora_rank 512, rope 64), batch 64,
+4096 cached tokens + 1 new token per sequence, bf16 cache of 20,000 blocks x 16 slots, blocks
+shuffled over the pool.  Inputs are seeded synthetic data.  Three copies of the cache pool are
+rotated between steps so that consecutive steps never re-read the same 302 MB (the 256 MB
+Infinity Cache cannot serve a step from the previous one); each layer of a real model reads
+its own cache once per step in the same way.
+
+Prints ONE JSON line.  `value` = algorithmic latent-cache bytes per step / step time (GB/s).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode µs/step + achieved latent-cache GB/s, V2-Lite b=64 s=4096"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "decode_bf16_lite_b64_s4096_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_paged_amd", "csrc", "decode_bf16.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="lite_b64", choices=["lite_b64", "wide", "ragged", "lite_b1"])
+    ap.add_argument("--seq-len", type=int, default=1024, help="seq_len for lite_b1")
+    ap.add_argument("--rotate", type=int, default=3, help="cache pool copies rotated between steps")
+    ap.add_argument("--split-blocks", type=int, default=0, help="force the split size (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="sequences in the oracle's timed sample")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only"],
+                    help="copy-calibration: run a plain 256 MiB device copy (for counter scaling); "
+                         "decode-only: run just the decode loop (for profilers)")
+    return ap.parse_args()
+
+
+def make_workload(args):
+    from workloads import mla_inputs as W
+    if args.workload == "lite_b64":
+        return W.lite_b64()
+    if args.workload == "wide":
+        return W.wide()
+    if args.workload == "ragged":
+        return W.ragged()
+    return W.lite_b1(args.seq_len)
+
+
+def describe(w):
+    return {
+        "workload": f"{w.name}: MLA decode, {w.num_heads} heads, kv_lora_rank 512 + rope 64, batch {w.batch}, "
+                    f"q_len {w.q_len}, context {int(w.seq_lens.min())}..{int(w.seq_lens.max())} tokens "
+                    f"(sum {w.total_ctx}), {w.storage} paged cache [{w.n_blocks},16,1,576], shuffled block table",
+        "batch": w.batch, "q_len": w.q_len, "num_heads": w.num_heads,
+        "max_ctx": int(w.seq_lens.max()), "sum_ctx": w.total_ctx, "pool_blocks": w.n_blocks,
+    }
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy-calibration", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": 5}), flush=True)
+
+
+def traffic_entry():
+    """HBM traffic of the decode kernel from committed rocprofv3 --pmc summaries, if they were
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, n_seq):
+    """Time the fp64 oracle (absorbed form) on a bounded sample of the same workload: the step's
+    cache write of each sampled sequence's new tokens plus its full decode."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    ctxmgr = threadpool_limits(cores) if threadpool_limits else None
+    rng = np.random.default_rng(0)
+    seqs = sorted(rng.choice(w.batch, size=min(n_seq, w.batch), replace=False).tolist())
+    kvb = w.kv_b_proj().astype(np.float64)
+    W_uk, W_uv = O.absorb(kvb, w.num_heads, w.qk_nope_head_dim, w.v_head_dim)
+    gamma = w.gamma().astype(np.float64)
+    qall = w.queries()
+    prepared = []
+    for b in seqs:   # history (not timed): identity-paged local pool per sequence
+        ctx = int(w.seq_lens[b])
+        nb = (ctx + 15) // 16
+        c, k = w.history(b)
+        hist = ctx - w.q_len
+        pool = O.cache_write(np.full((nb, 16, 1, 576), np.nan), c[:hist], k[:hist], np.arange(hist),
+                             np.arange(hist), gamma, w.eps, w.theta, w.storage)
+        prepared.append((b, ctx, nb, c[hist:], k[hist:], pool))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for b, ctx, nb, cn, kn, pool in prepared:
+            cache = O.cache_write(pool, cn, kn, np.arange(ctx - w.q_len, ctx), np.arange(ctx - w.q_len, ctx),
+                                  gamma, w.eps, w.theta, w.storage)
+            O.decode_absorbed(qall[b * w.q_len:(b + 1) * w.q_len], cache, np.arange(nb)[None, :],
+                              np.array([ctx]), w.q_len, W_uk, W_uv, w.scale, w.theta)
+        times.append(time.perf_counter() - t0)
+        if times[-1] > 30:
+            break
+    t = float(np.median(times))
+    blas_threads = cores
+    if threadpool_limits:
+        try:
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [cores])
+        except Exception:
+            pass
+    if ctxmgr is not None:
+        ctxmgr.unregister() if hasattr(ctxmgr, "unregister") else None
+    bytes_sample = sum(int(w.seq_lens[b]) for b in seqs) * 576 * w.elem_bytes
+    return {"value": bytes_sample / t / 1e9, "unit": "GB/s", "cores": int(min(cores, blas_threads)),
+            "kind": "oracle",
+            "sample": f"{len(seqs)} of {w.batch} sequences (full context each); one step = cache write of the "
+                      f"new token(s) + absorbed fp64 decode; median of {len(times)} runs, {t:.3f} s per run; "
+                      f"host threads available {cores}",
+            "seconds_per_sample_step": t}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU sharding is a design "
+                                   "note only (the path has no cross-GPU step in this build)",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    if args.mode == "copy-calibration":
+        copy_calibration()
+        return
+    from mla_latent_kv_paged_amd import MLAContext, K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE
+
+    w = make_workload(args)
+    dt = torch.bfloat16 if w.storage == "bf16" else torch.float32
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda().to(dt)
+
+    def dev_i(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+    max_ctx = int(w.seq_lens.max())
+    t0 = time.perf_counter()
+    kvb = dev(w.kv_b_proj())
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    ctx = MLAContext(kvb, None, num_heads=w.num_heads, dtype=w.storage, rms_eps=w.eps, rope_theta=w.theta,
+                     max_q_tokens=w.n_q, max_batch=w.batch, max_position=max_ctx, max_seq_len=max_ctx)
+    absorb_ms = (time.perf_counter() - ta) * 1e3
+    if args.split_blocks:
+        ctx.set_split_blocks(args.split_blocks)
+    pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=dt, device="cuda")
+    new_c, new_k, new_pos, new_slot = [], [], [], []
+    for b in range(w.batch):       # history fill through the library, one sequence at a time
+        c, k = w.history(b)
+        ctxb = int(w.seq_lens[b])
+        hist = ctxb - w.q_len
+        if hist > 0:
+            ctx.cache_write(dev(c[:hist]), dev(k[:hist]), dev_i(np.arange(hist)), dev_i(w.slots(b, 0, hist)), pool)
+        new_c.append(c[hist:]); new_k.append(k[hist:])
+        new_pos.append(np.arange(hist, ctxb)); new_slot.append(w.slots(b, hist, ctxb))
+    nc, nk = dev(np.concatenate(new_c)), dev(np.concatenate(new_k))
+    npos, nslot = dev_i(np.concatenate(new_pos)), dev_i(np.concatenate(new_slot))
+    q = dev(w.queries())
+    bt = dev_i(w.block_table)
+    sl = dev_i(w.seq_lens)
+    pools = [pool] + [pool.clone() for _ in range(max(0, args.rotate - 1))]
+    out = torch.empty((w.n_q, w.num_heads, 128), dtype=dt, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+
+    def step(i):
+        p = pools[i % len(pools)]
+        ctx.cache_write(nc, nk, npos, nslot, p)
+        ctx.decode(q, p, bt, sl, max_ctx, q_len=w.q_len, out=out)
+
+    if args.mode == "decode-only":
+        for i in range(args.warmup + args.steps):
+            ctx.decode(q, pools[i % len(pools)], bt, sl, max_ctx, q_len=w.q_len, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "decode-only", "launches": args.warmup + args.steps, "workload": w.name}),
+              flush=True)
+        return
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # pass A: the step as a whole (no per-kernel events)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    # pass B: per-kernel HIP events recorded by the library on the launch stream
+    ctx.profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern = {}
+    for name, kid in (("cache_write", K_CACHE_WRITE), ("q_absorb", K_Q_ABSORB), ("decode", K_DECODE),
+                      ("combine", K_COMBINE)):
+        tot, n = ctx.profile_read(kid)
+        kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+    ctx.profile_enable(False)
+    shape = ctx.last_decode_shape()
+
+    latent_bytes = w.latent_bytes()
+    decode_us = kern["decode"]["avg_us"]
+    flops_attn = w.total_ctx * w.num_heads * w.q_len * 2 * (576 + 512)
+    achieved = latent_bytes / (decode_us * 1e-6) / 1e9
+    traffic = traffic_entry()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "decode_bf16_kernel" if w.storage == "bf16" else "decode_f32_kernel",
+                "algorithmic_bytes_per_launch": latent_bytes,
+                "mfma_tflops": round(flops_attn / (decode_us * 1e-6) / 1e12, 2)}
+    step_us = ms_per_step * 1e3
+    res = {
+        "metric": METRIC,
+        "value": round(latent_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(step_us, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.storage == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/512) kv_b_proj)",
+        "config": describe(w),
+        "decode_us": round(decode_us, 2),
+        "decode_latent_gbps": round(achieved, 1),
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+        "split": shape,
+        "absorb_weights_ms_once": round(absorb_ms, 2),
+        "rotated_pools": len(pools),
+        "setup_s": round(setup_s, 1),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    ctx.free()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
