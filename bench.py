@@ -43,9 +43,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lite_b64", choices=["lite_b64", "wide", "ragged", "lite_b1"])
-    ap.add_argument("--seq-len", type=int, default=1024, help="seq_len for lite_b1")
+    ap.add_argument("--seq-len", type=int, default=0, help="cached tokens per sequence (lite_b1: default 1024; "
+                    "lite_b64: default 4096)")
+    ap.add_argument("--batch", type=int, default=0, help="batch for lite_b64 (default 64)")
     ap.add_argument("--rotate", type=int, default=3, help="cache pool copies rotated between steps")
     ap.add_argument("--split-blocks", type=int, default=0, help="force the split size (0 = library choice)")
+    ap.add_argument("--waves", type=int, default=0, help="force waves per decode workgroup (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=32, help="sequences in the oracle's timed sample")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only"],
@@ -57,12 +60,16 @@ def parse():
 def make_workload(args):
     from workloads import mla_inputs as W
     if args.workload == "lite_b64":
+        if args.seq_len or args.batch:
+            S, B = args.seq_len or 4096, args.batch or 64
+            nb = B * ((S + 1 + 15) // 16)
+            return W.lite_b64(batch=B, seq_len=S, n_blocks=max(20000, int(nb * 1.25)))
         return W.lite_b64()
     if args.workload == "wide":
         return W.wide()
     if args.workload == "ragged":
         return W.ragged()
-    return W.lite_b1(args.seq_len)
+    return W.lite_b1(args.seq_len or 1024)
 
 
 def describe(w):
@@ -188,8 +195,8 @@ def main():
     ctx = MLAContext(kvb, None, num_heads=w.num_heads, dtype=w.storage, rms_eps=w.eps, rope_theta=w.theta,
                      max_q_tokens=w.n_q, max_batch=w.batch, max_position=max_ctx, max_seq_len=max_ctx)
     absorb_ms = (time.perf_counter() - ta) * 1e3
-    if args.split_blocks:
-        ctx.set_split_blocks(args.split_blocks)
+    if args.split_blocks or args.waves:
+        ctx.set_decode_tuning(args.split_blocks, args.waves)
     pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=dt, device="cuda")
     new_c, new_k, new_pos, new_slot = [], [], [], []
     for b in range(w.batch):       # history fill through the library, one sequence at a time

@@ -160,9 +160,11 @@ void mla_free(mla_ctx* ctx);
 /* Human-readable name of a status code (static string). */
 const char* mla_status_string(int32_t status);
 
-/* Force the split size in 16-token blocks for subsequent decodes (0 = automatic choice).
- * Returns MLA_EINVAL for a negative value. */
-mla_status mla_set_split_blocks(mla_ctx* ctx, int32_t split_blocks);
+/* Force the decode launch shape for subsequent decodes: split size in 16-token blocks and
+ * waves per workgroup of the bf16 kernel (2 or 4); 0 keeps the automatic choice for each.
+ * Any split size gives the same result up to fp32 summation order.  Returns MLA_EINVAL for a
+ * negative split size or an unsupported wave count. */
+mla_status mla_set_decode_tuning(mla_ctx* ctx, int32_t split_blocks, int32_t waves_per_group);
 
 /* Launch shape of the most recent decode: split size in blocks, number of splits launched
  * (grid x) and waves per workgroup.  Any pointer may be NULL. */

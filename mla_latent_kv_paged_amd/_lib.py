@@ -19,7 +19,7 @@ MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
 
 EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_free", "mla_status_string",
-           "mla_set_split_blocks", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read")
+           "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read")
 
 
 class MLAConfig(ctypes.Structure):
@@ -60,8 +60,8 @@ def load(path=None):
     lib.mla_free.restype = None
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
-    lib.mla_set_split_blocks.argtypes = [vp, i32]
-    lib.mla_set_split_blocks.restype = i32
+    lib.mla_set_decode_tuning.argtypes = [vp, i32, i32]
+    lib.mla_set_decode_tuning.restype = i32
     lib.mla_last_decode_shape.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.mla_last_decode_shape.restype = i32
     lib.mla_profile_enable.argtypes = [vp, i32]
@@ -186,8 +186,8 @@ class MLAContext:
         return out
 
     # -- helpers
-    def set_split_blocks(self, n):
-        _check(self.lib.mla_set_split_blocks(self.handle, int(n)), "mla_set_split_blocks")
+    def set_decode_tuning(self, split_blocks=0, waves=0):
+        _check(self.lib.mla_set_decode_tuning(self.handle, int(split_blocks), int(waves)), "mla_set_decode_tuning")
 
     def last_decode_shape(self):
         a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()

@@ -35,9 +35,15 @@ def _hipcc():
     return h
 
 
+# Per-source flags.  The decode kernel keeps its MFMA accumulators in VGPRs so that the online
+# softmax rescale runs on them in place (no AGPR<->VGPR copies); its block buffers then take the
+# AGPR half of the register file.
+PER_FILE = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src, extra, verbose):
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *PER_FILE.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

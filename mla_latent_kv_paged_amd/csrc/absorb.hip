@@ -1,8 +1,11 @@
 // S0 -- weight absorption split (mini-infer 17 "MLA Attention：从 KV Cache 压缩到矩阵吸收",
 // 版本 3 _build_absorbed): kv_b_proj viewed as (H, DN + DV, DC); per head the DN "nope" rows are
-// W_uk and the DV "value" rows are W_uv.  Pure data movement, no arithmetic:
-//   W_uk [H, DN, DC]  = rows h*(DN+DV) + n          (kept row-major: DC contiguous)
-//   W_uvT[H, DC, DV]  = transpose of rows h*(DN+DV) + DN + v  (DV contiguous for the output GEMM)
+// W_uk and the DV "value" rows are W_uv.  Pure data movement, no arithmetic; each factor is kept
+// in the two layouts its consumers read:
+//   W_uk [H, DN, DC]  rows h*(DN+DV) + n, DC contiguous        (fp32 query kernel)
+//   W_ukT[H, DC, DN]  its transpose, DN contiguous             (MFMA query kernel: K = DN)
+//   W_uv [H, DV, DC]  rows h*(DN+DV) + DN + v, DC contiguous   (MFMA output kernel: K = DC)
+//   W_uvT[H, DC, DV]  its transpose, DV contiguous             (fp32 output kernel)
 #include "mla_internal.h"
 
 namespace mla {
@@ -11,7 +14,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void absorb_kernel(AbsorbArgs a) {
   const T* src = static_cast<const T*>(a.kv_b_proj);
   T* wuk = static_cast<T*>(a.W_uk);
-  T* wuv = static_cast<T*>(a.W_uvT);
+  T* wukt = static_cast<T*>(a.W_ukT);
+  T* wuv = static_cast<T*>(a.W_uv);
+  T* wuvt = static_cast<T*>(a.W_uvT);
   const int64_t total = int64_t(a.H) * (DN + DV) * DC;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += int64_t(gridDim.x) * blockDim.x) {
     const int c = int(i % DC);
@@ -20,8 +25,10 @@ __global__ __launch_bounds__(256) void absorb_kernel(AbsorbArgs a) {
     const int r = int(rowi % (DN + DV));
     if (r < DN) {
       wuk[(int64_t(h) * DN + r) * DC + c] = src[i];
+      wukt[(int64_t(h) * DC + c) * DN + r] = src[i];
     } else {
-      wuv[(int64_t(h) * DC + c) * DV + (r - DN)] = src[i];
+      wuv[(int64_t(h) * DV + (r - DN)) * DC + c] = src[i];
+      wuvt[(int64_t(h) * DC + c) * DV + (r - DN)] = src[i];
     }
   }
 }

@@ -31,12 +31,7 @@
 
 namespace mla {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
@@ -47,25 +42,51 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // over distinct bank groups.
 __device__ __forceinline__ int ct_swz(int t) { return ((t & 7) << 1) | (t >> 3); }
 
-template <int NW>
+// Issue the loads of one paged block (16 tokens x 576 bf16) into registers: lane (t = lane%16,
+// g = lane/16) takes granules 4s + g of token t's row, s = 0..17.  The loads are unconditional
+// (no divergent branch, so the compiler can keep several blocks in flight): a lane whose token is
+// not visible, whose block id is outside the pool, or whose wave has no block left (!have)
+// reads the zero block instead.
+__device__ __forceinline__ void load_block(uint4 (&buf)[18], const char* cache, const char* zero, int phys,
+                                           bool have, int kb, int L, int num_blocks, int r16, int g) {
+  const bool ld_ok = have && unsigned(phys) < unsigned(num_blocks) && (kb * BLK + r16) < L;
+  const char* rowp = ld_ok ? cache + (int64_t(phys) * BLK + r16) * (ROW * 2) : zero + r16 * (ROW * 2);
+  const uint4* src = reinterpret_cast<const uint4*>(rowp);
+#pragma unroll
+  for (int s = 0; s < 18; ++s) buf[s] = src[4 * s + g];
+}
+
+// Running-max slack of the online softmax (log2 units): the max used for the exponentials is
+// only moved when a block's max exceeds it by more than this, so P <= 2^8 and the accumulator
+// rescale (a multiply of all 128 accumulator registers) is skipped for most blocks.  The result
+// is the same softmax; only the common factor carried in (acc, l) differs.
+constexpr float kMaxSlack = 8.f;
+
+template <int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
-  __shared__ uint4 q_lds[16 * 72];
   __shared__ uint4 c_lds[NW * 16 * 64];
   __shared__ float m_lds[NW][16];
   __shared__ float l_lds[NW][16];
 
+  // Work unit u = (sequence b, split j, row tile rt), rt fastest.  Workgroup i is dispatched to
+  // XCD i % 8; each XCD gets a contiguous range of units so that the row tiles and neighbouring
+  // splits of a sequence share one L2.
+  const int per_xcd = (a.units + 7) >> 3;
+  const int u = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
+  if (u >= a.units) return;
+  const int rt = u % a.n_rt;
+  const int j = (u / a.n_rt) % a.n_split;
+  const int b = u / (a.n_rt * a.n_split);
+
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  const int j = blockIdx.x;
-  const int b = blockIdx.y;
-  const int rt = blockIdx.z;
   const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
   const int nblk = (ctx + BLK - 1) / BLK;
   const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
-  if (j >= ns || j >= a.n_split) return;
+  if (j >= ns) return;
   const int tiles_per_q = a.H >> 4;
   const int iq = rt / tiles_per_q;
   const int h0 = (rt % tiles_per_q) << 4;
@@ -76,16 +97,15 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   if (kb1 > lblk) kb1 = lblk;
   const int row = b * a.q_len + iq;
 
-  // query tile -> LDS, granule (r, c) at r*72 + (c ^ (r & 7))
+  // query tile in registers, in the B-operand layout of the score MFMA: lane (r, g) holds
+  // granules 4e + g of query row r (head h0 + r), e = 0..17
+  uint4 qreg[18];
   {
     const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.qcat) +
-                                                       (int64_t(row) * a.H + h0) * ROW);
-    for (int idx = threadIdx.x; idx < 16 * 72; idx += NW * 64) {
-      const int r = idx / 72, c = idx - r * 72;
-      q_lds[r * 72 + (c ^ (r & 7))] = qsrc[idx];
-    }
+                                                       (int64_t(row) * a.H + h0 + r16) * ROW);
+#pragma unroll
+    for (int e = 0; e < 18; ++e) qreg[e] = qsrc[4 * e + g];
   }
-  __syncthreads();
 
   f32x4_t acc[32];
 #pragma unroll
@@ -94,65 +114,110 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 
   uint4* cbuf = c_lds + w * 16 * 64;
   const char* cache = static_cast<const char*>(a.cache);
+  const char* zero = static_cast<const char*>(a.zero_block);
+  // LDS addresses.  The swizzle only touches the low 4 bits of a granule index, so granule
+  // 16*q + x of a row maps to 16*q + (x ^ swz): a few per-lane base pointers plus immediate
+  // offsets cover every access.
   const int wr_swz = ct_swz(r16);
+  uint4* wr_base[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) wr_base[e2] = cbuf + r16 * 64 + ((4 * e2 + g) ^ wr_swz);
   const int tr_t = 4 * g + (r16 >> 2);
   const int tr_swz = ct_swz(tr_t);
   const int tr_cofs = (r16 & 3) >> 1;
   const int tr_half = r16 & 1;
+  const uint16_t* tr_base[8];
+#pragma unroll
+  for (int r8 = 0; r8 < 8; ++r8)
+    tr_base[r8] = reinterpret_cast<const uint16_t*>(cbuf + tr_t * 64 + ((2 * r8 + tr_cofs) ^ tr_swz)) + tr_half * 4;
   const int* bt = a.block_table + int64_t(b) * a.bt_stride;
 
-  for (int kb = kb0 + w; kb < kb1; kb += NW) {
-    const int phys = bt[kb];
-    const bool blk_ok = unsigned(phys) < unsigned(a.num_blocks);
-    const int tok = kb * BLK + r16;
-    const bool ld_ok = blk_ok && tok < L;
-    const uint4* src = reinterpret_cast<const uint4*>(cache + (int64_t(blk_ok ? phys : 0) * BLK + r16) * (ROW * 2));
-    uint4 creg[18];
-#pragma unroll
-    for (int s = 0; s < 18; ++s) creg[s] = ld_ok ? src[4 * s + g] : make_uint4(0u, 0u, 0u, 0u);
-    // c_kv part of the block -> per-wave LDS tile (row = token) for the transposed P.C operand
-#pragma unroll
-    for (int s = 0; s < 16; ++s) cbuf[r16 * 64 + ((4 * s + g) ^ wr_swz)] = creg[s];
+  // this wave's blocks: kb0 + w + NW*i, i < nwb (nwb <= 128).  Lane l holds the physical ids of
+  // the wave's blocks l and 64 + l, so each lookup is a register read (v_readlane), not a memory
+  // round trip in front of the next loads.
+  const int span = kb1 - kb0 - w;
+  const int nwb = span > 0 ? (span + NW - 1) / NW : 0;
+  const int phys_lo = lane < nwb ? bt[kb0 + w + NW * lane] : 0;
+  const int phys_hi = lane + 64 < nwb ? bt[kb0 + w + NW * (lane + 64)] : 0;
+  auto phys_of = [&](int i) {
+    return i < 64 ? __builtin_amdgcn_readlane(phys_lo, i & 63) : __builtin_amdgcn_readlane(phys_hi, i & 63);
+  };
 
-    // scores: S^T[t][r] = sum_k C[t][k] * Q[r][k]
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+  // NBUF (2 or 3) named register buffers processed in turn with no conditional in the loop body,
+  // so that the loads of the others stay in flight while one is consumed.  A short tail is padded
+  // with missing blocks (zero data, every token masked).
+  uint4 bufA[18], bufB[18], bufC[18];
+  load_block(bufA, cache, zero, phys_of(0), 0 < nwb, kb0 + w, L, a.num_blocks, r16, g);
+  load_block(bufB, cache, zero, phys_of(1), 1 < nwb, kb0 + w + NW, L, a.num_blocks,
+             r16, g);
+  if (NBUF == 3)
+    load_block(bufC, cache, zero, phys_of(2), 2 < nwb, kb0 + w + 2 * NW, L,
+               a.num_blocks, r16, g);
+
+  // One block: c_kv -> LDS tile, scores, refill of the buffer with block i + 2, online softmax,
+  // P.C on the matrix cores.
+  auto process = [&](uint4 (&buf)[18], int i) {
+    const int kb = kb0 + w + NW * i;
+    const bool have = i < nwb;
 #pragma unroll
-    for (int s = 0; s < 18; ++s) {
-      const int c = 4 * s + g;
-      const uint4 qv = q_lds[r16 * 72 + (c ^ (r16 & 7))];
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(creg[s]), as_bf16x8(qv), sc, 0, 0, 0);
+    for (int e = 0; e < 16; ++e) wr_base[e & 3][16 * (e >> 2)] = buf[e];
+
+    // scores: S^T[t][r] = sum_k C[t][k] * Q[r][k], two independent MFMA chains
+    f32x4_t sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 18; e += 2) {
+      sc0 = mfma32(buf[e], qreg[e], sc0);
+      sc1 = mfma32(buf[e + 1], qreg[e + 1], sc1);
     }
+    const f32x4_t sc = sc0 + sc1;
+    const int inext = i + NBUF;
+    load_block(buf, cache, zero, phys_of(inext & 127), inext < nwb, kb0 + w + NW * inext,
+               L, a.num_blocks, r16, g);
 
     // mask + online softmax (row r16; this lane holds tokens 4g..4g+3 of the block)
     float sv[4];
     float mb = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (kb * BLK + 4 * g + i < L) ? sc[i] : -INFINITY;
-      mb = fmaxf(mb, sv[i]);
+    for (int t = 0; t < 4; ++t) {
+      sv[t] = (have && kb * BLK + 4 * g + t < L) ? sc[t] : -INFINITY;
+      mb = fmaxf(mb, sv[t]);
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float mn = fmaxf(m, mb);
-    const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+    // lazy rescale: wave-uniform branch taken only when some row's max grew past the slack
+    if (__any(mb > m + kMaxSlack)) {
+      const float mn = fmaxf(m, mb);
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int jj = 0; jj < 32; ++jj) acc[jj] *= alpha;
+      m = mn;
+    }
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - mn);
-    lsum = lsum * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-    m = mn;
-#pragma unroll
-    for (int jj = 0; jj < 32; ++jj) acc[jj] *= alpha;
+    for (int t = 0; t < 4; ++t) p[t] = sv[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[t] - m);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
 
-    // transposed reads of the c_kv tile written above
+    // P.C: A = C^T tile jj (16 channels x 16 tokens) by transposed LDS read, B = P^T
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) {
-      const uint16_t* ap = reinterpret_cast<const uint16_t*>(cbuf + tr_t * 64 + ((2 * jj + tr_cofs) ^ tr_swz)) + tr_half * 4;
-      const s16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(ap));
-      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, acc[jj], 0, 0, 0);
+    for (int q8 = 0; q8 < 4; ++q8) {
+      s16x4_t av[8];
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8)  // tile 8*q8 + r8: + 16 granules per 8 tiles
+        av[r8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr_base[r8] + 16 * 8 * q8));
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8)
+        acc[8 * q8 + r8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[r8], pb, acc[8 * q8 + r8], 0, 0, 0);
     }
     asm volatile("" ::: "memory");
+  };
+
+  for (int i = 0; i < nwb; i += NBUF) {
+    process(bufA, i);
+    process(bufB, i + 1);
+    if (NBUF == 3) process(bufC, i + 2);
   }
 
   // merge the waves' states: row max, rescale, fixed-order tree sum through LDS
@@ -170,25 +235,27 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) {
     const float mw = m_lds[ww][r16];
-    if (mw != -INFINITY) Ltot += exp2f(mw - M) * l_lds[ww][r16];
+    if (mw != -INFINITY) Ltot += __builtin_amdgcn_exp2f(mw - M) * l_lds[ww][r16];
   }
-  const float sw = (m == -INFINITY) ? 0.f : exp2f(m - M);
+  const float sw = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) acc[jj] *= sw;
 
-  float* slots = reinterpret_cast<float*>(c_lds);  // NW/2 slots of 16 x 512 floats
+  // NW/2 slots of 32 x 64 lanes x 16 B; a lane's accumulator tile jj sits at [jj][lane], so
+  // that consecutive lanes touch consecutive 16-byte words (no bank conflicts)
+  f32x4_t* slots = reinterpret_cast<f32x4_t*>(c_lds);
 #pragma unroll
   for (int stride = NW / 2; stride >= 1; stride >>= 1) {
     if (w >= stride && w < 2 * stride) {
-      float* sl = slots + (w - stride) * (16 * DC);
+      f32x4_t* sl = slots + (w - stride) * (32 * 64);
 #pragma unroll
-      for (int jj = 0; jj < 32; ++jj) *reinterpret_cast<f32x4_t*>(sl + r16 * DC + 16 * jj + 4 * g) = acc[jj];
+      for (int jj = 0; jj < 32; ++jj) sl[jj * 64 + lane] = acc[jj];
     }
     __syncthreads();
     if (w < stride) {
-      const float* sl = slots + w * (16 * DC);
+      const f32x4_t* sl = slots + w * (32 * 64);
 #pragma unroll
-      for (int jj = 0; jj < 32; ++jj) acc[jj] += *reinterpret_cast<const f32x4_t*>(sl + r16 * DC + 16 * jj + 4 * g);
+      for (int jj = 0; jj < 32; ++jj) acc[jj] += sl[jj * 64 + lane];
     }
     __syncthreads();
   }
@@ -204,13 +271,13 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 
 hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t s) {
   if (!bf16) return launch_decode_f32(a, s);
-  dim3 grid(a.n_split, a.batch, (a.H / 16) * a.q_len);
+  const int grid = ((a.units + 7) >> 3) << 3;
   switch (waves) {
-    case 4:
-      decode_bf16_kernel<4><<<grid, 256, 0, s>>>(a);
+    case 2:
+      decode_bf16_kernel<2, 2><<<grid, 128, 0, s>>>(a);
       break;
-    case 8:
-      decode_bf16_kernel<8><<<grid, 512, 0, s>>>(a);
+    case 4:
+      decode_bf16_kernel<4, 2><<<grid, 256, 0, s>>>(a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -33,7 +33,10 @@ struct mla_ctx {
   int cu_count = 256;
   float qscale = 0.f;
   void* W_uk = nullptr;
+  void* W_ukT = nullptr;
+  void* W_uv = nullptr;
   void* W_uvT = nullptr;
+  void* zero_block = nullptr;
   double* gamma = nullptr;
   double2* rope = nullptr;
   void* qcat = nullptr;
@@ -41,6 +44,7 @@ struct mla_ctx {
   float2* part_ml = nullptr;
   int32_t max_split = 1;
   int32_t forced_split_blocks = 0;
+  int32_t forced_waves = 0;
   int32_t last_split_blocks = 0, last_n_split = 0, last_waves = 0;
   Prof prof;
 };
@@ -52,7 +56,10 @@ inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 void ctx_release(mla_ctx* c) {
   if (!c) return;
   hipFree(c->W_uk);
+  hipFree(c->W_ukT);
+  hipFree(c->W_uv);
   hipFree(c->W_uvT);
+  hipFree(c->zero_block);
   hipFree(c->gamma);
   hipFree(c->rope);
   hipFree(c->qcat);
@@ -101,16 +108,22 @@ mla_status hip_status(hipError_t e) {
   return MLA_EHIP;
 }
 
-// Split size (in 16-token blocks) for a decode of `units` independent (sequence, row-tile)
-// work items whose longest context spans max_blocks blocks.  Aim for about one 8-wave
-// workgroup per CU in flight, keep at least one block per wave, and cap the split length so
-// that a few long sequences in a ragged batch do not serialise the tail.
+// Split size (in 16-token blocks) for a decode of `units` independent (sequence, row-tile) work
+// items whose longest context spans max_blocks blocks.  The bf16 kernel holds one workgroup per
+// CU, so the grid is sized to a whole number of workgroups per CU where possible
+// (units * n_split ~ k * CUs); a split is capped so that a few long sequences in a ragged batch
+// do not serialise the tail, and holds at least one block per wave.
 int choose_split_blocks(const mla_ctx* c, int units, int max_blocks, int waves) {
-  const int target = c->cu_count;
-  int n_target = (target + units - 1) / units;
+  const int cus = c->cu_count;
+  int n_target;
+  if (units >= cus)
+    n_target = 1;
+  else
+    n_target = cus / units;  // floor: units * n_target <= CUs, one round
   if (n_target < 1) n_target = 1;
   int sb = (max_blocks + n_target - 1) / n_target;
-  if (sb > 128) sb = 128;
+  const int cap = 128 * waves;
+  if (sb > cap) sb = cap;
   if (sb < waves) sb = waves;
   return sb;
 }
@@ -163,14 +176,20 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
   const int H = cfg->num_heads;
   const size_t esz = c->bf16 ? 2 : 4;
   const int max_blocks = (cfg->max_seq_len + BLK - 1) / BLK;
+  // enough splits that a split never needs more than 128 blocks per wave at 2 waves per group
+  const int need_split = (max_blocks + 255) / 256;
   c->max_split = max_blocks < kMaxSplit ? max_blocks : kMaxSplit;
+  if (c->max_split < need_split) c->max_split = need_split;
   const size_t rows = size_t(cfg->max_q_tokens) * H;
   hipError_t e = hipSuccess;
   auto alloc = [&](void** p, size_t n) {
     if (e == hipSuccess) e = hipMalloc(p, n);
   };
   alloc(&c->W_uk, size_t(H) * DN * DC * esz);
+  alloc(&c->W_ukT, size_t(H) * DC * DN * esz);
+  alloc(&c->W_uv, size_t(H) * DV * DC * esz);
   alloc(&c->W_uvT, size_t(H) * DC * DV * esz);
+  alloc(&c->zero_block, size_t(BLK) * ROW * esz);
   alloc(reinterpret_cast<void**>(&c->gamma), DC * sizeof(double));
   alloc(reinterpret_cast<void**>(&c->rope), size_t(cfg->max_position + 1) * NPAIR * sizeof(double2));
   alloc(&c->qcat, rows * ROW * esz);
@@ -215,11 +234,12 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
       rope[size_t(p) * NPAIR + i] = make_double2(std::cos(ang), std::sin(ang));
     }
   }
-  e = hipMemcpyAsync(c->gamma, g.data(), DC * sizeof(double), hipMemcpyHostToDevice, s);
+  e = hipMemsetAsync(c->zero_block, 0, size_t(BLK) * ROW * esz, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(c->gamma, g.data(), DC * sizeof(double), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(c->rope, rope.data(), rope.size() * sizeof(double2), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) {
-    AbsorbArgs aa{kv_b_proj_w, c->W_uk, c->W_uvT, H};
+    AbsorbArgs aa{kv_b_proj_w, c->W_uk, c->W_ukT, c->W_uv, c->W_uvT, H};
     e = launch_absorb(c->bf16, aa, s);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -261,11 +281,13 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   const int H = cf.num_heads;
   const int n_q = batch * q_len;
 
-  const int waves = ctx->bf16 ? 8 : 1;
+  const int n_rt = (H / 16) * q_len;
+  const int waves = ctx->bf16 ? (ctx->forced_waves > 0 ? ctx->forced_waves : 2) : 1;
   int sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
-                                        : choose_split_blocks(ctx, batch * (H / 16) * q_len, max_blocks, waves);
+                                        : choose_split_blocks(ctx, batch * n_rt, max_blocks, waves);
   const int min_sb = (max_blocks + ctx->max_split - 1) / ctx->max_split;  // workspace bound
   if (sb < min_sb) sb = min_sb;
+  if (sb > 128 * waves) sb = 128 * waves;  // a wave tracks at most 128 block ids in two registers
   if (sb > max_blocks) sb = max_blocks;
   const int n_split = (max_blocks + sb - 1) / sb;
   ctx->last_split_blocks = sb;
@@ -274,21 +296,23 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
 
   hipError_t e;
   {
-    QAbsorbArgs qa{q, ctx->W_uk, ctx->rope, seq_lens, q_len, n_q, H, max_seq_len, cf.max_position, ctx->qscale,
+    QAbsorbArgs qa{q, ctx->W_uk, ctx->W_ukT, ctx->rope, seq_lens, q_len, n_q, H, max_seq_len, cf.max_position, ctx->qscale,
                    ctx->qcat};
     ProfScope ps(ctx, MLA_K_Q_ABSORB, s);
     e = launch_q_absorb(ctx->bf16, qa, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {
-    DecodeArgs da{batch, kv_cache, num_blocks, block_table, block_table_stride, seq_lens, max_seq_len, q_len, H,
-                  ctx->qcat, ctx->part_acc, ctx->part_ml, sb, n_split};
+    DecodeArgs da{batch,  kv_cache,       ctx->zero_block, num_blocks,    block_table, block_table_stride,
+                  seq_lens, max_seq_len,  q_len,           H,             ctx->qcat,   ctx->part_acc,
+                  ctx->part_ml, sb,       n_split,         n_rt,          batch * n_split * n_rt};
     ProfScope ps(ctx, MLA_K_DECODE, s);
     e = launch_decode(ctx->bf16, da, waves, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {
-    CombineArgs ca{ctx->part_acc, ctx->part_ml, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split, ctx->W_uvT, out};
+    CombineArgs ca{ctx->part_acc, ctx->part_ml, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split,
+                   ctx->W_uv, ctx->W_uvT, out};
     ProfScope ps(ctx, MLA_K_COMBINE, s);
     e = launch_combine(ctx->bf16, ca, s);
   }
@@ -301,9 +325,12 @@ void mla_free(mla_ctx* ctx) {
   ctx_release(ctx);
 }
 
-mla_status mla_set_split_blocks(mla_ctx* ctx, int32_t split_blocks) {
+mla_status mla_set_decode_tuning(mla_ctx* ctx, int32_t split_blocks, int32_t waves_per_group) {
   if (!ctx || split_blocks < 0) return MLA_EINVAL;
+  if (waves_per_group != 0 && waves_per_group != 2 && waves_per_group != 4)
+    return MLA_EINVAL;
   ctx->forced_split_blocks = split_blocks;
+  ctx->forced_waves = waves_per_group;
   return MLA_OK;
 }
 

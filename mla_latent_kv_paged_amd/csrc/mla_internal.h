@@ -22,8 +22,10 @@ constexpr int NPAIR = DR / 2;  // RoPE pairs
 
 struct AbsorbArgs {
   const void* kv_b_proj;  // [H*(DN+DV), DC]
-  void* W_uk;             // [H, DN, DC]
-  void* W_uvT;            // [H, DC, DV]
+  void* W_uk;             // [H, DN, DC]  (fp32 query kernel)
+  void* W_ukT;            // [H, DC, DN]  (MFMA query kernel: K = DN contiguous)
+  void* W_uv;             // [H, DV, DC]  (MFMA output kernel: K = DC contiguous)
+  void* W_uvT;            // [H, DC, DV]  (fp32 output kernel)
   int32_t H;
 };
 
@@ -46,6 +48,7 @@ struct CacheWriteArgs {
 struct QAbsorbArgs {
   const void* q;          // [n_q, H, QW]
   const void* W_uk;       // [H, DN, DC]
+  const void* W_ukT;      // [H, DC, DN]
   const double2* rope;
   const int32_t* seq_lens;
   int32_t q_len;
@@ -60,6 +63,7 @@ struct QAbsorbArgs {
 struct DecodeArgs {
   int32_t batch;
   const void* cache;
+  const void* zero_block;  // BLK * ROW zero values of the storage dtype (read by masked lanes)
   int32_t num_blocks;
   const int32_t* block_table;
   int32_t bt_stride;
@@ -72,6 +76,8 @@ struct DecodeArgs {
   float2* part_ml;        // [n_q*H*n_split] (running max in log2 units, sum)
   int32_t split_blocks;
   int32_t n_split;
+  int32_t n_rt;           // row tiles of 16 per sequence: (H/16) * q_len
+  int32_t units;          // batch * n_split * n_rt work items
 };
 
 struct CombineArgs {
@@ -84,6 +90,7 @@ struct CombineArgs {
   int32_t H;
   int32_t split_blocks;
   int32_t n_split;
+  const void* W_uv;       // [H, DV, DC]
   const void* W_uvT;      // [H, DC, DV]
   void* out;              // [n_q, H, DV]
 };
@@ -99,6 +106,18 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------------------ device helpers
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16].  Lane l holds A row l%16 and B column
+// l%16, with 8 consecutive K values per lane (K block l/16); D column l%16, rows 4(l/16)..+3.
+__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 

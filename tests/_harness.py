@@ -61,15 +61,15 @@ class GpuRun:
         self.bt = dev_i32(w.block_table)
         self.sl = dev_i32(w.seq_lens)
 
-    def decode(self, pool=None, split_blocks=None):
+    def decode(self, pool=None, split_blocks=None, waves=0):
         import torch
-        if split_blocks is not None:
-            self.ctx.set_split_blocks(split_blocks)
+        if split_blocks is not None or waves:
+            self.ctx.set_decode_tuning(split_blocks or 0, waves)
         out = self.ctx.decode(self.q, self.pool if pool is None else pool, self.bt, self.sl, self.max_ctx,
                               q_len=self.w.q_len)
         torch.cuda.synchronize()
-        if split_blocks is not None:
-            self.ctx.set_split_blocks(0)
+        if split_blocks is not None or waves:
+            self.ctx.set_decode_tuning(0, 0)
         return out
 
     def pool_f64(self):

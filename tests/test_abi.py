@@ -64,5 +64,5 @@ def test_invalid_host_arguments_rejected_without_device():
     # null context
     assert lib.mla_cache_write(None, None, 512, None, 64, None, None, 1, None, 1, None) == L.MLA_EINVAL
     assert lib.mla_decode(None, None, 1, 1, None, 1, None, 1, None, 1, None, None) == L.MLA_EINVAL
-    assert lib.mla_set_split_blocks(None, 1) == L.MLA_EINVAL
+    assert lib.mla_set_decode_tuning(None, 1, 0) == L.MLA_EINVAL
     lib.mla_free(None)
