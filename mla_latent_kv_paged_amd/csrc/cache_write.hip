@@ -21,39 +21,43 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (j >= a.T) return;
-  const int slot = a.slots[j];
-  if (slot < 0 || int64_t(slot) >= a.num_slots) return;  // padding or out-of-pool slot: skipped
+  // every load of the token is issued before any of them is inspected (one memory round trip)
   const T* c = static_cast<const T*>(a.c_kv) + int64_t(j) * a.c_stride;
   const T* k = static_cast<const T*>(a.k_pe) + int64_t(j) * a.k_stride;
-  T* dst = static_cast<T*>(a.cache) + int64_t(slot) * ROW;
+  const int slot = a.slots[j];
   const int pos = a.positions[j];
+  double x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = load_f64(c, lane * 8 + e);
+  const double kx0 = load_f64(k, 2 * (lane & (NPAIR - 1)));
+  const double kx1 = load_f64(k, 2 * (lane & (NPAIR - 1)) + 1);
+  double gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gm[e] = a.gamma[lane * 8 + e];
+  if (slot < 0 || int64_t(slot) >= a.num_slots) return;  // padding or out-of-pool slot: skipped
+  T* dst = static_cast<T*>(a.cache) + int64_t(slot) * ROW;
   const bool pos_ok = pos >= 0 && pos <= a.max_position;
+  const double2 cs = a.rope[int64_t(pos_ok ? pos : 0) * NPAIR + (lane & (NPAIR - 1))];
 
   // RMSNorm over the 512 latent channels (fp64): x / sqrt(mean(x^2) + eps) * gamma
-  double x[8];
   double ss = 0.0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    x[e] = load_f64(c, lane * 8 + e);
-    ss += x[e] * x[e];
-  }
+  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
   const double denom = sqrt(ss / double(DC) + a.eps);
   const double nan = __builtin_nan("");
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const double y = x[e] / denom * a.gamma[lane * 8 + e];
+    const double y = x[e] / denom * gm[e];
     store_round(dst, lane * 8 + e, pos_ok ? y : nan);
   }
 
   // RoPE on k_pe: pair i = (x[2i], x[2i+1]) rotated by pos * theta^(-2i/64)
   if (lane < NPAIR) {
-    const double x0 = load_f64(k, 2 * lane);
-    const double x1 = load_f64(k, 2 * lane + 1);
+    const double x0 = kx0, x1 = kx1;
     double y0 = nan, y1 = nan;
     if (pos_ok) {
-      const double2 cs = a.rope[int64_t(pos) * NPAIR + lane];
       y0 = x0 * cs.x - x1 * cs.y;
       y1 = x0 * cs.y + x1 * cs.x;
     }

@@ -10,7 +10,8 @@
 //   out^T[v, n] = sum_c W_uv[h][v, c] o_lat^T[c, n]   (K = 512, 16 steps of 16x16x32 bf16),
 // with o_lat carried as an unevaluated sum of two bf16 values (hi = bf16(o), lo = bf16(o - hi)),
 // i.e. about 16 significant bits, so the product loses nothing visible to the output rounding.
-// Each wave owns 32 of the 128 output channels; W_uv rows are read straight from global memory.
+// A workgroup owns 16 rows and a quarter (32) of the output channels; two waves compute 16
+// channels each, W_uv rows read straight from global memory.
 // fp32 storage: the same merge, then W_uv on the vector ALUs.  Both accumulate in fp32.
 #include "mla_internal.h"
 
@@ -80,41 +81,40 @@ __device__ __forceinline__ int o_swz(int r) { return ((r & 7) << 1) | (r >> 3); 
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   const int h = blockIdx.x;
   const int r0 = blockIdx.y * 16;
+  const int vq = blockIdx.z;  // quarter of the 128 output channels
   const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   __shared__ uint4 ohi[16 * 64];
   __shared__ uint4 olo[16 * 64];
 
-  // the W_uv fragments of this wave (32 output channels x 512) do not depend on the merge: issue
-  // their loads first so that they overlap it
-  const int lane0 = tid & 63, w0 = tid >> 6;
+  // W_uv fragments of this workgroup's 32 output channels (waves 0 and 1 take 16 each): their
+  // loads do not depend on the merge, so they are issued first
   const uint16_t* wuv_h = static_cast<const uint16_t*>(a.W_uv) + int64_t(h) * DV * DC;
-  const uint4* wrow0 = reinterpret_cast<const uint4*>(wuv_h + int64_t(w0 * 32 + (lane0 & 15)) * DC);
-  const uint4* wrow1 = reinterpret_cast<const uint4*>(wuv_h + int64_t(w0 * 32 + 16 + (lane0 & 15)) * DC);
-  uint4 wf0[16], wf1[16];
+  const uint4* wrow = reinterpret_cast<const uint4*>(wuv_h + int64_t(vq * 32 + (w & 1) * 16 + (lane & 15)) * DC);
+  uint4 wf[16];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    wf0[ks] = wrow0[4 * ks + (lane0 >> 4)];
-    wf1[ks] = wrow1[4 * ks + (lane0 >> 4)];
-  }
+  for (int ks = 0; ks < 16; ++ks) wf[ks] = wrow[4 * ks + (lane >> 4)];
 
   // merge the split partials: wave w owns rows 4w..4w+3, lane owns channels 8*lane..8*lane+7.
-  // Splits are consumed in chunks of 4 with unconditional loads (indices past the row's split
-  // count re-read split 0 and get weight 0), merged with a running max, so that the loads of
-  // the four rows and four splits are in flight together.
-  const int lane = tid & 63, w = tid >> 6;
-  int ns[4];
+  // Every one of the n_split slots is read unconditionally (slots past a row's split count hold
+  // stale values and are dropped by selection, never by multiplication), so the loads do not
+  // wait for the context length.  Chunks of 4 splits are merged with a running max.
+  // context lengths of the wave's 4 rows: four independent loads, issued together
+  int ns[4], sl[4];
   int64_t base[4];
-  int ns_max = 0;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int row = r0 + w * 4 + rr;
-    const int rowc = row < a.n_q ? row : 0;
-    const int ctx = clamp_ctx(a.seq_lens[rowc / a.q_len], a.q_len, a.max_seq_len);
+    const int rowc = row < a.n_q ? row : a.n_q - 1;
+    base[rr] = (int64_t(rowc) * a.H + h) * a.n_split;
+    sl[rr] = a.seq_lens[rowc / a.q_len];
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int ctx = clamp_ctx(sl[rr], a.q_len, a.max_seq_len);
     const int nblk = (ctx + BLK - 1) / BLK;
     const int n = (nblk + a.split_blocks - 1) / a.split_blocks;
-    ns[rr] = row < a.n_q ? (n < a.n_split ? n : a.n_split) : 0;
-    base[rr] = (int64_t(rowc) * a.H + h) * a.n_split;
-    ns_max = ns[rr] > ns_max ? ns[rr] : ns_max;
+    ns[rr] = (r0 + w * 4 + rr < a.n_q) ? (n < a.n_split ? n : a.n_split) : 0;
   }
   float M[4], den[4], o[4][8];
 #pragma unroll
@@ -124,14 +124,14 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[rr][e] = 0.f;
   }
-  for (int j0 = 0; j0 < ns_max; j0 += 4) {
+  for (int j0 = 0; j0 < a.n_split; j0 += 4) {
     float2 ml[4][4];
     float4 va[4][4], vb[4][4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int jc = (j0 + jj < ns[rr]) ? j0 + jj : 0;
+        const int jc = j0 + jj < a.n_split ? j0 + jj : 0;
         ml[rr][jj] = a.part_ml[base[rr] + jc];
         const float4* src = reinterpret_cast<const float4*>(a.part_acc + (base[rr] + jc) * DC + 8 * lane);
         va[rr][jj] = src[0];
@@ -139,19 +139,22 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
       }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
+      bool ok[4];
       float mc = M[rr];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (j0 + jj < ns[rr]) mc = fmaxf(mc, ml[rr][jj].x);
-      const float sc = (M[rr] == -INFINITY) ? 0.f : exp2f(M[rr] - mc);
+      for (int jj = 0; jj < 4; ++jj) {
+        ok[jj] = j0 + jj < ns[rr] && ml[rr][jj].x != -INFINITY;
+        mc = ok[jj] ? fmaxf(mc, ml[rr][jj].x) : mc;
+      }
+      const float sc = (M[rr] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[rr] - mc);
       den[rr] *= sc;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[rr][e] *= sc;
       M[rr] = mc;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float mj = ml[rr][jj].x;
-        const float wgt = (j0 + jj < ns[rr] && mj != -INFINITY) ? exp2f(mj - mc) : 0.f;
+        if (!ok[jj]) continue;
+        const float wgt = __builtin_amdgcn_exp2f(ml[rr][jj].x - mc);
         den[rr] = fmaf(wgt, ml[rr][jj].y, den[rr]);
         o[rr][0] = fmaf(wgt, va[rr][jj].x, o[rr][0]); o[rr][1] = fmaf(wgt, va[rr][jj].y, o[rr][1]);
         o[rr][2] = fmaf(wgt, va[rr][jj].z, o[rr][2]); o[rr][3] = fmaf(wgt, va[rr][jj].w, o[rr][3]);
@@ -168,49 +171,41 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float x0 = o[rr][2 * e] * inv, x1 = o[rr][2 * e + 1] * inv;
-      const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
-      const uint16_t l0 = f32_to_bf16(x0 - bf16_to_f32(h0)), l1 = f32_to_bf16(x1 - bf16_to_f32(h1));
-      hw[e] = uint32_t(h0) | (uint32_t(h1) << 16);
-      lw[e] = uint32_t(l0) | (uint32_t(l1) << 16);
+      hw[e] = cvt_pk_bf16(x0, x1);
+      lw[e] = cvt_pk_bf16(x0 - __uint_as_float(hw[e] << 16), x1 - __uint_as_float(hw[e] & 0xffff0000u));
     }
     const int gi = r * 64 + (lane ^ o_swz(r));
     ohi[gi] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     olo[gi] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   __syncthreads();
+  if (w >= 2) return;
 
+  // out^T[v, n] for 16 output channels v of this wave and the 16 rows n of this workgroup
   const int r16 = lane & 15, g = lane >> 4;
-  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     const int c = 4 * ks + g;
-    const uint4 bh = ohi[r16 * 64 + (c ^ o_swz(r16))];
-    const uint4 bl = olo[r16 * 64 + (c ^ o_swz(r16))];
-    const uint4 a0 = wf0[ks], a1 = wf1[ks];
-    acc[0] = mfma32(a0, bh, acc[0]);
-    acc[0] = mfma32(a0, bl, acc[0]);
-    acc[1] = mfma32(a1, bh, acc[1]);
-    acc[1] = mfma32(a1, bl, acc[1]);
+    acc = mfma32(wf[ks], ohi[r16 * 64 + (c ^ o_swz(r16))], acc);
+    acc = mfma32(wf[ks], olo[r16 * 64 + (c ^ o_swz(r16))], acc);
   }
-  // lane holds query row r0 + r16 (column), output channels w*32 + t*16 + 4g .. +3 (rows)
+  // lane holds query row r0 + r16 (column), output channels vq*32 + 16w + 4g .. +3 (rows)
   const int row = r0 + r16;
   if (row < a.n_q) {
-    uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.H + h) * DV;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t lo = uint32_t(f32_to_bf16(acc[t][0])) | (uint32_t(f32_to_bf16(acc[t][1])) << 16);
-      const uint32_t hi = uint32_t(f32_to_bf16(acc[t][2])) | (uint32_t(f32_to_bf16(acc[t][3])) << 16);
-      *reinterpret_cast<uint2*>(out + w * 32 + t * 16 + 4 * g) = make_uint2(lo, hi);
-    }
+    uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.H + h) * DV + vq * 32 + 16 * w + 4 * g;
+    *reinterpret_cast<uint2*>(out) = make_uint2(cvt_pk_bf16(acc[0], acc[1]), cvt_pk_bf16(acc[2], acc[3]));
   }
 }
 
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s) {
-  dim3 grid(a.H, (a.n_q + 15) / 16);
-  if (bf16)
+  if (bf16) {
+    dim3 grid(a.H, (a.n_q + 15) / 16, DV / 32);
     combine_bf16_kernel<<<grid, 256, 0, s>>>(a);
-  else
+  } else {
+    dim3 grid(a.H, (a.n_q + 15) / 16);
     combine_kernel<float><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

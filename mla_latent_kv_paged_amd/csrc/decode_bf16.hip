@@ -33,10 +33,6 @@ namespace mla {
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-}
-
 // swizzle of the per-wave C tile (16 rows of 64 granules): keeps both the granule writes
 // (16 rows, same granule) and the transposed reads (8 rows x 2 granules per half-wave) spread
 // over distinct bank groups.
@@ -197,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = sv[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[t] - m);
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])));
 
     // P.C: A = C^T tile jj (16 channels x 16 tokens) by transposed LDS read, B = P^T
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

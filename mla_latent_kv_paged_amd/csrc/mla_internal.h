@@ -128,6 +128,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Two floats -> packed bf16 pair (low half = lo) with the hardware converter
+// (v_cvt_pk_bf16_f32, round to nearest even in the default rounding mode).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
 // double -> bf16 with a single rounding (nearest even): round to odd at fp32 precision first
 // (truncate, then set the sticky bit if anything was lost), then round to nearest even.
 // 24 bits >= 8 + 2, so the two steps give the correctly rounded result.

@@ -126,9 +126,8 @@ __global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a) {
     // lane holds query row n (column), channels c0 + 4g .. +3 (rows)
     const int n = n_blk * 64 + tt * 16 + r16;
     if (n < a.n_q) {
-      const uint32_t lo = uint32_t(f32_to_bf16(acc[0] * a.qscale)) | (uint32_t(f32_to_bf16(acc[1] * a.qscale)) << 16);
-      const uint32_t hi = uint32_t(f32_to_bf16(acc[2] * a.qscale)) | (uint32_t(f32_to_bf16(acc[3] * a.qscale)) << 16);
-      *reinterpret_cast<uint2*>(qcat + (int64_t(n) * a.H + h) * ROW + c0 + 4 * g) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(qcat + (int64_t(n) * a.H + h) * ROW + c0 + 4 * g) =
+          make_uint2(cvt_pk_bf16(acc[0] * a.qscale, acc[1] * a.qscale), cvt_pk_bf16(acc[2] * a.qscale, acc[3] * a.qscale));
     }
   }
   // RoPE part: the 8 channel-block workgroups of this (head, 64 rows) each take 8 rows x 32 pairs,
@@ -142,7 +141,7 @@ __global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a) {
       float y0, y1;
       rope_q_pair(a, n, h, i, bf16_to_f32(src[2 * i]), bf16_to_f32(src[2 * i + 1]), &y0, &y1);
       uint16_t* o = qcat + (int64_t(n) * a.H + h) * ROW + DC;
-      *reinterpret_cast<uint32_t*>(o + 2 * i) = uint32_t(f32_to_bf16(y0)) | (uint32_t(f32_to_bf16(y1)) << 16);
+      *reinterpret_cast<uint32_t*>(o + 2 * i) = cvt_pk_bf16(y0, y1);
     }
   }
 }
