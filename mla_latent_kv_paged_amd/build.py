@@ -35,10 +35,12 @@ def _hipcc():
     return h
 
 
-# Per-source flags.  The decode kernel keeps its MFMA accumulators in VGPRs so that the online
-# softmax rescale runs on them in place (no AGPR<->VGPR copies); its block buffers then take the
-# AGPR half of the register file.
-PER_FILE = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags.  The decode kernels keep their MFMA accumulators in VGPRs so that the online
+# softmax rescale runs on them in place (no AGPR<->VGPR copies); their block buffers then take the
+# AGPR half of the register file.  The 32-row kernel uses the flag for its score MFMAs and pins its
+# P.C accumulator to the AGPRs itself.
+PER_FILE = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+            "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src, extra, verbose):

@@ -96,9 +96,9 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   for (int ks = 0; ks < 16; ++ks) wf[ks] = wrow[4 * ks + (lane >> 4)];
 
   // merge the split partials: wave w owns rows 4w..4w+3, lane owns channels 8*lane..8*lane+7.
-  // Every one of the n_split slots is read unconditionally (slots past a row's split count hold
-  // stale values and are dropped by selection, never by multiplication), so the loads do not
-  // wait for the context length.  Chunks of 4 splits are merged with a running max.
+  // Splits are taken in chunks of 4 up to the largest split count among the wave's rows; inside
+  // a chunk the loads are unconditional (slots past a row's own count hold stale values and are
+  // dropped by selection, never by multiplication).  Chunks are merged with a running max.
   // context lengths of the wave's 4 rows: four independent loads, issued together
   int ns[4], sl[4];
   int64_t base[4];
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
     const int n = (nblk + a.split_blocks - 1) / a.split_blocks;
     ns[rr] = (r0 + w * 4 + rr < a.n_q) ? (n < a.n_split ? n : a.n_split) : 0;
   }
+  const int ns_max = __builtin_amdgcn_readfirstlane(max(max(ns[0], ns[1]), max(ns[2], ns[3])));
   float M[4], den[4], o[4][8];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[rr][e] = 0.f;
   }
-  for (int j0 = 0; j0 < a.n_split; j0 += 4) {
+  for (int j0 = 0; j0 < ns_max; j0 += 4) {
     float2 ml[4][4];
     float4 va[4][4], vb[4][4];
 #pragma unroll

@@ -1,0 +1,320 @@
+// S3-S6 in bf16 storage for 32-row tiles (32 heads of one query, or 16 heads of two queries):
+// the same computation as decode_bf16.hip (mini-infer 17 "MLA Attention：从 KV Cache 压缩到矩阵吸收",
+// 版本 3 and 设计取舍; 踩坑记录 坑 2 causal mask; vLLM learning book ch. 07 §2.3 paged cache shape;
+// bxzpzcl.cn hybrid KV-cache page §2.1 block table), organised for many rows per sequence.
+//
+//  * A workgroup owns one (sequence, split) and T tiles of 32 rows; wave w owns tile w: its query
+//    tile (registers), its (m, l) per row and acc[32 rows x 512] (the AGPR file), and writes its
+//    own partial.
+//  * A step covers 32 tokens (two paged blocks).  The workgroup moves the step's 36 KB straight from
+//    HBM into one LDS stage with global_load_lds_dwordx4 (no register staging), NSTAGE - 1 steps
+//    ahead; masked lanes read the library's zero block.
+//  * Stage layout: chunk k (1 KB) holds granules 2k and 2k+1 (16 B = 8 channels each) of all 32
+//    tokens; token t of granule 2k+h sits at position 32h + (t ^ 4h) of the chunk.  Lane l of a
+//    DMA instruction writes position l, so the layout costs nothing to build; the score reads of a
+//    chunk are a permutation of it (conflict-free), and the transposed reads below hit 8 distinct
+//    16-byte bank groups per 16 lanes.
+//  * Scores S^T[32 tok x 32 rows] = C Q^T on v_mfma_f32_32x32x16_bf16: A = chunk k as read, B = the
+//    query tile's granules 2k, 2k+1.  Lane l then holds row l%32 at tokens 8(r/4) + 4(l/32) + r%4.
+//  * Causal mask per row; softmax against a per-row reference max that moves only by more than 64
+//    (log2 units), exp2; P is at most 2^64, well inside bf16 and fp32.
+//  * P.C: acc^T[32 ch x 32 rows] += C^T[32 ch x 16 tok] P^T[16 tok x 32 rows], two K steps of 16
+//    tokens per step.  The K order inside a step is {4h..4h+3, 8+4h..8+4h+3} for lane half h, which
+//    is exactly the order in which the score registers hold P, so B is the score registers rounded
+//    to bf16; A is two ds_read_b64_tr_b16 per MFMA.
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+
+constexpr float kReset = 64.f;    // reference-max headroom (log2 units): P <= 2^64
+constexpr int kChunks = 36;       // 1 KB chunks per stage (72 granules x 32 tokens)
+constexpr int kStageBytes = kChunks * 1024;
+
+__device__ __forceinline__ f32x16_t mfma32x32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// P.C step on one accumulator tile kept in AGPRs (acc is the whole AGPR file; the builtin would
+// let the allocator shuttle it through VGPRs).  The compiler does not see this as an MFMA, so the
+// wait states it would add are provided by the callers: an accumulator tile is next touched 16
+// MFMAs later at the earliest, its VALU readers run after a drain (mfma_drain), and the P operand
+// written by VALU is followed by s_nop before the first of these.
+__device__ __forceinline__ void mfma32x32_acc(f32x16_t& acc, u32x4_t a, u32x4_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// wait states after the last asm MFMA before VALU reads its accumulator (> 18 for 16 passes)
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// One 16-byte global -> LDS transfer per lane: lane l's data lands at lds + 16 l.  Issued from asm
+// so that the compiler does not track it (it would wait for every transfer in flight before the
+// next LDS read); the kernel orders it itself with wait_vmcnt and the barrier.  Loads complete in
+// issue order, so the compiler's own vmcnt waits for older loads stay correct.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt for vector memory only: vmcnt(n), lgkmcnt and expcnt left at their maxima
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (15 << 8) | (7 << 4) | (N & 15));
+}
+
+// Workgroup barrier ordering LDS only (the wave's own LDS accesses are complete when it arrives).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+}  // namespace
+
+template <int T, int NSTAGE>
+__global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) {
+  constexpr int CPW = kChunks / T;  // DMA chunks per wave per step
+  static_assert(kChunks % T == 0, "chunks split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) char stage_mem[NSTAGE * kStageBytes];
+
+  // work unit u = (sequence b, split j, tile group grp), grp fastest; XCD-aware order: the
+  // dispatcher deals consecutive workgroup ids round-robin over the 8 XCDs, so id x runs on XCD
+  // x % 8 and takes unit (x % 8) * per_xcd + x / 8 (neighbouring units share an L2)
+  const int n_grp = a.n_rt / T;  // n_rt = tiles of 32 rows per sequence here
+  const int per_xcd = (a.units + 7) >> 3;
+  const int u = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
+  if (u >= a.units) return;
+  const int grp = u % n_grp;
+  const int j = (u / n_grp) % a.n_split;
+  const int b = u / (n_grp * a.n_split);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;    // lane half: K block of the MFMA operands
+  const int r32 = lane & 31;  // row of the tile (N index) / token of a score operand (M index)
+
+  const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
+  const int nblk = (ctx + BLK - 1) / BLK;
+  const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
+  if (j >= ns) return;
+  const int kb0 = j * a.split_blocks;
+  const int nb = min(kb0 + a.split_blocks, nblk) - kb0;  // blocks of this split
+  const int steps = (nb + 1) >> 1;
+
+  // this lane's row: rr = tile row within the sequence, rows ordered (query, head)
+  const int rr = (grp * T + w) * 32 + r32;
+  const int iq = rr / a.H;
+  // tokens visible to the row in this split: causal limit, and the split's end (a step spans two
+  // blocks, so with an odd split size its last step reaches one block past the split)
+  const int Lw = min(ctx - a.q_len + iq + 1, (kb0 + nb) * BLK);
+  const int64_t R = int64_t(b) * a.q_len * a.H + rr;
+
+  // query tile: B operand of the score MFMA k is granule 2k + h of the row
+  u32x4_t qreg[kChunks];
+  {
+    const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.qcat) + R * ROW);
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) qreg[k] = qsrc[2 * k + h];
+  }
+
+  // block ids of the split in registers: lane l holds entries l and 64 + l (<= 128 blocks)
+  const int* bt = a.block_table + int64_t(b) * a.bt_stride;
+  const int phys_lo = lane < nb ? bt[kb0 + lane] : 0;
+  const int phys_hi = lane + 64 < nb ? bt[kb0 + 64 + lane] : 0;
+  auto phys_of = [&](int i) {
+    return i < 64 ? __builtin_amdgcn_readlane(phys_lo, i & 63) : __builtin_amdgcn_readlane(phys_hi, i & 63);
+  };
+
+  // DMA geometry: lane l of chunk k fetches token t = (l & 31) ^ 4h, granule 2k + h
+  const int dt = r32 ^ (4 * h);
+  const int dsel = dt >> 4;  // 0: first block of the step, 1: second
+  const int drow = dt & 15;
+  const char* cache = static_cast<const char*>(a.cache);
+  const char* zero_row = static_cast<const char*>(a.zero_block) + drow * (ROW * 2) + 16 * h;
+  lds_char_t* const stages = (lds_char_t*)stage_mem;
+
+  auto issue = [&](int i) {  // DMA of step i into stage i % NSTAGE (this wave's chunks)
+    const int bi = 2 * i + dsel;  // block index within the split
+    const int pa = phys_of((2 * i) & 127), pb = phys_of((2 * i + 1) & 127);
+    const int phys = dsel ? pb : pa;
+    const bool ok = bi < nb && unsigned(phys) < unsigned(a.num_blocks) && (kb0 + bi) * BLK + drow < ctx;
+    const char* src = ok ? cache + (int64_t(phys) * BLK + drow) * (ROW * 2) + 16 * h : zero_row;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes + w * CPW * 1024)));
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) dma16(src + 32 * (w * CPW + m), dst + 1024 * m);
+  };
+
+  f32x16_t acc[16];
+#pragma unroll
+  for (int jt = 0; jt < 16; ++jt) {
+    acc[jt] = f32x16_t{};
+    asm volatile("" : "+a"(acc[jt]));
+  }
+  float m = -INFINITY, lsum = 0.f;
+
+  // per-lane LDS offsets: score operand (position r32 ^ 4h of half h) and transposed reads
+  const int sc_off = 16 * (32 * h + (r32 ^ (4 * h)));
+  const int G = lane >> 4, li = lane & 15;
+  const int c1 = (li >> 1) & 1;
+  const int tr_off = 1024 * (G & 1) + 16 * (32 * c1 + 4 * ((G >> 1) ^ c1) + (li >> 2)) + 8 * (li & 1);
+
+  // the query tile and block ids are in registers before the first transfer: from here on every
+  // outstanding vector load is a transfer of this loop (the compiler's own waits in the loop would
+  // otherwise count the query loads and drain the transfers in flight)
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < steps) issue(i);
+
+  for (int i = 0; i < steps; ++i) {
+    // step i's chunks have landed for this wave (the newer steps' DMAs may stay in flight), then
+    // for every wave; the barrier also retires the stage read at step i - 1
+    if (i + NSTAGE - 2 < steps)
+      wait_vmcnt<(NSTAGE - 2) * CPW>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (i + NSTAGE - 1 < steps) issue(i + NSTAGE - 1);
+
+    // LDS byte address of the stage (32-bit)
+    const uint32_t st = uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes));
+    const int tok0 = (kb0 + 2 * i) * BLK;
+
+    // scores
+    f32x16_t sc = f32x16_t{};
+    {
+      uint32_t spa = st + uint32_t(sc_off);
+      asm volatile("" : "+v"(spa));
+      lds_u32x4_t* sp = (lds_u32x4_t*)uintptr_t(spa);
+      constexpr int D = 6;
+      u32x4_t ring[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k) ring[k] = sp[64 * k];
+#pragma unroll
+      for (int k = 0; k < kChunks; ++k) {
+        const u32x4_t x = ring[k % D];
+        if (k + D < kChunks) ring[k % D] = sp[64 * (k + D)];
+        sc = mfma32x32(x, qreg[k], sc);
+      }
+      // keep the reads D ahead: D reads, then (MFMA, read) pairs, then the last D MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+#pragma unroll
+      for (int k = 0; k < kChunks - D; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+    }
+
+    // mask, running max, lazy rescale
+    float sv[16];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = tok0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      sv[r] = t < Lw ? sc[r] : -INFINITY;
+      mb = fmaxf(mb, sv[r]);
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    // The reference max m of a row moves only when a score exceeds it by more than kReset; the
+    // row's earlier terms then weigh at most 2^-kReset each against the new maximum (at most 2^15
+    // tokens: <= 2^-49 in total, far below fp32 rounding), so the row restarts from zero instead
+    // of being rescaled: a masked AGPR write, no pass of the accumulator through VGPRs.
+    const bool upd = mb > m + kReset;
+    if (__any(upd)) {
+      if (upd) {
+        if (m != -INFINITY) {  // nothing was accumulated while m was -inf
+          mfma_drain();
+#pragma unroll
+          for (int jt = 0; jt < 16; ++jt) {
+            acc[jt] = f32x16_t{};
+            asm volatile("" : "+a"(acc[jt]));
+          }
+        }
+        lsum = 0.f;
+        m = mb;
+      }
+    }
+    uint32_t pw[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = sv[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m);
+      const float p1 = sv[r + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r + 1] - m);
+      lsum += p0 + p1;
+      pw[r >> 1] = cvt_pk_bf16(p0, p1);
+    }
+
+    // P.C: K step s covers tokens 16s..16s+15 of the step; B = P registers 8s..8s+7
+    {
+      // one base per step, opaque to the compiler so that the 64 constant offsets below fold into
+      // the instructions' immediate offsets (instead of 64 hoisted loop-invariant registers)
+      uint32_t tpa = st + uint32_t(tr_off);
+      asm volatile("" : "+v"(tpa));
+      lds_char_t* tp = (lds_char_t*)uintptr_t(tpa);
+      auto tr = [&](int s, int r, int jt) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tp + 2048 * jt + 256 * s + 128 * r));
+      };
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x4_t pb = u32x4_t{pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]};
+        asm volatile("s_nop 4" ::"v"(pb));  // VALU-written B operand -> MFMA read
+        constexpr int D = 4;
+        s16x4_t ra[D], rb[D];
+#pragma unroll
+        for (int jt = 0; jt < D; ++jt) {
+          ra[jt] = tr(s, 0, jt);
+          rb[jt] = tr(s, 1, jt);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 16; ++jt) {
+          const u32x4_t av = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(ra[jt % D], rb[jt % D], 0, 1, 2, 3, 4, 5, 6, 7));
+          if (jt + D < 16) {
+            ra[jt % D] = tr(s, 0, jt + D);
+            rb[jt % D] = tr(s, 1, jt + D);
+          }
+          mfma32x32_acc(acc[jt], av, pb);
+        }
+      }
+    }
+  }
+
+  // partial of this wave's rows: channel 32jt + 8q + 4h + e sits in acc[jt][4q + e]
+  mfma_drain();
+  lsum += __shfl_xor(lsum, 32, 64);
+  const int64_t pidx = R * a.n_split + j;
+  float* dst = a.part_acc + pidx * DC;
+#pragma unroll
+  for (int jt = 0; jt < 16; ++jt) {
+    f32x16_t v = acc[jt];
+    asm volatile("" : "+v"(v));  // one tile at a time out of the AGPRs
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4_t*>(dst + 32 * jt + 8 * q + 4 * h) = f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  }
+  if (h == 0) a.part_ml[pidx] = make_float2(m, lsum);
+}
+
+hipError_t launch_decode_mt32(const DecodeArgs& a, int T, hipStream_t s) {
+  const int grid = ((a.units + 7) >> 3) << 3;
+  switch (T) {
+    case 1:
+      decode_bf16_mt32_kernel<1, 2><<<grid, 64, 0, s>>>(a);
+      break;
+    case 2:
+      decode_bf16_mt32_kernel<2, 2><<<grid, 128, 0, s>>>(a);
+      break;
+    case 4:
+      decode_bf16_mt32_kernel<4, 3><<<grid, 256, 0, s>>>(a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

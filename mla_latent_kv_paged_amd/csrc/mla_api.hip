@@ -281,13 +281,20 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   const int H = cf.num_heads;
   const int n_q = batch * q_len;
 
-  const int n_rt = (H / 16) * q_len;
-  const int waves = ctx->bf16 ? (ctx->forced_waves > 0 ? ctx->forced_waves : 2) : 1;
+  const int n_rt16 = (H / 16) * q_len;  // row tiles of 16 per sequence (rows ordered query, head)
+  // bf16 kernels by rows per sequence: a multiple of 32 -> 32-row tiles, T of them per workgroup
+  // (each block read once per workgroup); otherwise the one-tile kernel, 16-row tiles in the grid
+  const int n_rt32 = (H * q_len) % 32 == 0 ? H * q_len / 32 : 0;
+  const int t32 = (ctx->bf16 && n_rt32 > 0) ? ((n_rt32 % 4 == 0) ? 4 : (n_rt32 % 2 == 0) ? 2 : 1) : 0;
+  const int n_rt = t32 ? n_rt32 : n_rt16;
+  const int waves = ctx->bf16 ? (t32 ? t32 : (ctx->forced_waves > 0 ? ctx->forced_waves : 2)) : 1;
+  const int groups = t32 ? n_rt / t32 : n_rt;  // workgroups per (sequence, split)
+  const int blocks_per_wave_cap = t32 ? 128 : 128 * waves;  // block ids held in two registers
   int sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
-                                        : choose_split_blocks(ctx, batch * n_rt, max_blocks, waves);
+                                        : choose_split_blocks(ctx, batch * groups, max_blocks, t32 ? 1 : waves);
   const int min_sb = (max_blocks + ctx->max_split - 1) / ctx->max_split;  // workspace bound
   if (sb < min_sb) sb = min_sb;
-  if (sb > 128 * waves) sb = 128 * waves;  // a wave tracks at most 128 block ids in two registers
+  if (sb > blocks_per_wave_cap) sb = blocks_per_wave_cap;
   if (sb > max_blocks) sb = max_blocks;
   const int n_split = (max_blocks + sb - 1) / sb;
   ctx->last_split_blocks = sb;
@@ -305,9 +312,9 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   {
     DecodeArgs da{batch,  kv_cache,       ctx->zero_block, num_blocks,    block_table, block_table_stride,
                   seq_lens, max_seq_len,  q_len,           H,             ctx->qcat,   ctx->part_acc,
-                  ctx->part_ml, sb,       n_split,         n_rt,          batch * n_split * n_rt};
+                  ctx->part_ml, sb,       n_split,         n_rt,          batch * n_split * groups};
     ProfScope ps(ctx, MLA_K_DECODE, s);
-    e = launch_decode(ctx->bf16, da, waves, s);
+    e = t32 ? launch_decode_mt32(da, t32, s) : launch_decode(ctx->bf16, da, waves, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {

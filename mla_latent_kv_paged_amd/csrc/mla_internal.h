@@ -76,7 +76,7 @@ struct DecodeArgs {
   float2* part_ml;        // [n_q*H*n_split] (running max in log2 units, sum)
   int32_t split_blocks;
   int32_t n_split;
-  int32_t n_rt;           // row tiles of 16 per sequence: (H/16) * q_len
+  int32_t n_rt;           // row tiles per sequence: of 16 rows ((H/16) * q_len), or of 32 for the 32-row kernel
   int32_t units;          // batch * n_split * n_rt work items
 };
 
@@ -103,6 +103,9 @@ hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s);
 // waves: waves per workgroup of the bf16 decode kernel (ignored in fp32 mode)
 hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+// bf16, 32-row tiles (H*q_len a multiple of 32), T in {1, 2, 4} tiles per workgroup; n_rt = tiles of
+// 32 rows per sequence (a multiple of T); units = batch*n_split*(n_rt/T)
+hipError_t launch_decode_mt32(const DecodeArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------------------ device helpers

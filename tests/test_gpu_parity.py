@@ -58,6 +58,8 @@ SMALL = [
     ("gamma_f32", lambda: W.custom("g_f32", "f32", 16, [70, 129], q_len=2, seed=8, gamma_noise=0.1)),
     ("ctx_eq_qlen", lambda: W.custom("edge", "bf16", 16, [1, 2, 3, 4, 16, 17], q_len=1, seed=9)),
     ("ctx_eq_qlen4", lambda: W.custom("edge4", "bf16", 16, [4, 16, 17, 20], q_len=4, seed=10)),
+    ("h48_q2_bf16", lambda: W.custom("h48", "bf16", 48, [40, 300, 77], q_len=2, seed=11)),
+    ("h32_q1_bf16", lambda: W.custom("h32", "bf16", 32, [33, 200, 517], q_len=1, seed=12)),
 ]
 
 
@@ -91,10 +93,64 @@ def test_decode_only_from_generator_pool():
         run.free()
 
 
-@pytest.mark.parametrize("storage", ["bf16", "f32"])
-def test_split_sweep_and_determinism(storage):
-    w = W.custom("sweep", storage, 16, [2, 37, 200, 513], q_len=2, seed=31)
-    _say("split sweep", storage)
+@pytest.mark.parametrize("heads,q_len", [(16, 1), (16, 2), (128, 1)])
+def test_large_score_jump(heads, q_len):
+    """A score far above everything before it: the rope part of the token at position 200 is scaled
+    by 2^8 (exact in bf16), which puts its score near +-300 (log2 units) for most rows, so the
+    running max jumps by far more than any softmax headroom in the middle of a split.
+
+    Such a key magnifies the bf16 rounding of q into its score (about 0.4 log2 units), so rows where
+    the spike competes with the other tokens are ill-conditioned for any bf16 kernel; the test
+    compares the rows where the fp64 oracle puts the spike at least 40 log2 units above (it
+    dominates) or below (it vanishes) every other visible score, and requires both kinds, with
+    jumps of more than 64 over the split's first steps, to be present."""
+    w = W.custom("jump", "bf16", heads, [40, 260, 700], q_len=q_len, seed=61)
+    _say("score jump", "H", heads, "q_len", q_len)
+    spike = 200
+    pool = w.random_pool()
+    for b in range(w.batch):
+        if int(w.seq_lens[b]) > spike:
+            pool[w.block_table[b, spike // 16], spike % 16, 0, 512:] *= 256.0
+    pool64 = pool.astype(np.float64)
+    W_uk, W_uv = oracle_weights(w)
+    ref = O.decode_absorbed(w.queries(), pool64, w.block_table, w.seq_lens, w.q_len, W_uk, W_uv, w.scale, w.theta)
+
+    log2e = 1.0 / np.log(2.0)
+    q = w.queries().astype(np.float64)
+    keep = np.ones(ref.shape[:2], dtype=bool)
+    n_dom = n_van = 0
+    for b in range(w.batch):
+        ctx = int(w.seq_lens[b])
+        if ctx <= spike:
+            continue
+        C, R = O.gather_sequence(pool64, w.block_table[b], ctx, 512)
+        for i in range(w.q_len):
+            pos, row = ctx - w.q_len + i, b * w.q_len + i
+            for h in range(heads):
+                s2 = O._absorbed_scores(q[row, h], C, R, W_uk[h], pos, w.scale, w.theta)[:pos + 1] * log2e
+                d = s2[spike] - np.max(np.delete(s2, spike))
+                keep[row, h] = abs(d) >= 40.0
+                if d >= 40.0 and s2[spike] - np.max(s2[:32]) > 64.0:
+                    n_dom += 1
+                n_van += d <= -40.0
+    assert n_dom > 0 and n_van > 0 and keep.mean() > 0.75, (n_dom, n_van, keep.mean())
+
+    run = GpuRun(w)
+    try:
+        for sb in (64, 5):
+            out = run.decode(pool=dev(pool, w.storage), split_blocks=sb)
+            got = out.float().cpu().numpy().astype(np.float64)
+            compare(got[keep], ref[keep], w.storage, f"score jump split_blocks={sb}")
+    finally:
+        run.free()
+
+
+@pytest.mark.parametrize("storage,heads,q_len", [("bf16", 16, 2), ("f32", 16, 2), ("bf16", 128, 1), ("bf16", 16, 4)])
+def test_split_sweep_and_determinism(storage, heads, q_len):
+    """Every split size from one block to the whole context (odd sizes end a two-block step past
+    the split), run twice each: results within tolerance and bit-identical between runs."""
+    w = W.custom("sweep", storage, heads, [4, 37, 200, 513], q_len=q_len, seed=31)
+    _say("split sweep", storage, "H", heads, "q_len", q_len)
     _, ref = oracle_full(w)
     run = GpuRun(w)
     try:
