@@ -9,11 +9,11 @@
 //  * A step covers 32 tokens (two paged blocks).  The workgroup moves the step's 36 KB straight from
 //    HBM into one LDS stage with global_load_lds_dwordx4 (no register staging), NSTAGE - 1 steps
 //    ahead; masked lanes read the library's zero block.
-//  * Stage layout: chunk k (1 KB) holds granules 2k and 2k+1 (16 B = 8 channels each) of all 32
-//    tokens; token t of granule 2k+h sits at position 32h + (t ^ 4h) of the chunk.  Lane l of a
-//    DMA instruction writes position l, so the layout costs nothing to build; the score reads of a
-//    chunk are a permutation of it (conflict-free), and the transposed reads below hit 8 distinct
-//    16-byte bank groups per 16 lanes.
+//  * Stage layout: 8 x 8 tiles of 16-byte granules (8 channels).  Chunk K = 9 tg + gq (1 KB) holds
+//    tokens 8tg..8tg+7 x granules 8gq..8gq+7, granule c of token t at slot 8 (c % 8) + t % 8.  Lane
+//    l of a DMA instruction writes slot l and reads token 8tg + l % 8, granule 8gq + l / 8: eight
+//    rows x 128 contiguous bytes, i.e. whole cache lines.  Both operand reads below are a per-lane
+//    base plus immediate offsets (score operand k at + 256 k) and run at the LDS's full rate.
 //  * Scores S^T[32 tok x 32 rows] = C Q^T on v_mfma_f32_32x32x16_bf16: A = chunk k as read, B = the
 //    query tile's granules 2k, 2k+1.  Lane l then holds row l%32 at tokens 8(r/4) + 4(l/32) + r%4.
 //  * Causal mask per row; softmax against a per-row reference max that moves only by more than 64
@@ -23,6 +23,7 @@
 //    is exactly the order in which the score registers hold P, so B is the score registers rounded
 //    to bf16; A is two ds_read_b64_tr_b16 per MFMA.
 #include "mla_internal.h"
+
 
 namespace mla {
 
@@ -79,6 +80,7 @@ template <int T, int NSTAGE>
 __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) {
   constexpr int CPW = kChunks / T;  // DMA chunks per wave per step
   static_assert(kChunks % T == 0, "chunks split evenly over the waves");
+  static_assert(NSTAGE >= 2, "a step is read while a later one is loaded");
   __shared__ __attribute__((aligned(16))) char stage_mem[NSTAGE * kStageBytes];
 
   // work unit u = (sequence b, split j, tile group grp), grp fastest; XCD-aware order: the
@@ -129,25 +131,31 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
     return i < 64 ? __builtin_amdgcn_readlane(phys_lo, i & 63) : __builtin_amdgcn_readlane(phys_hi, i & 63);
   };
 
-  // DMA geometry: lane l of chunk k fetches token t = (l & 31) ^ 4h, granule 2k + h
-  const int dt = r32 ^ (4 * h);
-  const int dsel = dt >> 4;  // 0: first block of the step, 1: second
-  const int drow = dt & 15;
+  // DMA geometry: wave w takes chunks K = w CPW .. w CPW + CPW - 1 (token groups tg = K / 9); lane l
+  // of chunk K reads token 8 tg + l % 8, granule 8 (K % 9) + l / 8
   const char* cache = static_cast<const char*>(a.cache);
-  const char* zero_row = static_cast<const char*>(a.zero_block) + drow * (ROW * 2) + 16 * h;
+  const char* zero = static_cast<const char*>(a.zero_block);
   lds_char_t* const stages = (lds_char_t*)stage_mem;
+  const int lrow = lane & 7, lgr = lane >> 3;
 
   auto issue = [&](int i) {  // DMA of step i into stage i % NSTAGE (this wave's chunks)
-    const int bi = 2 * i + dsel;  // block index within the split
     const int pa = phys_of((2 * i) & 127), pb = phys_of((2 * i + 1) & 127);
-    const int phys = dsel ? pb : pa;
-    const bool ok = bi < nb && unsigned(phys) < unsigned(a.num_blocks) && (kb0 + bi) * BLK + drow < ctx;
-    const char* src = ok ? cache + (int64_t(phys) * BLK + drow) * (ROW * 2) + 16 * h : zero_row;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
         uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes + w * CPW * 1024)));
+    constexpr int NTG = (CPW + 8) / 9;  // token groups this wave touches (CPW is 9, 18 or 36)
 #pragma unroll
-    for (int m = 0; m < CPW; ++m) dma16(src + 32 * (w * CPW + m), dst + 1024 * m);
+    for (int g = 0; g < NTG; ++g) {
+      const int tg = (w * CPW) / 9 + g;                 // token group of the step (uniform)
+      const int bi = 2 * i + (tg >> 1);                  // block index within the split
+      const int trow = 8 * (tg & 1) + lrow;              // token row within the block
+      const int phys = (tg >> 1) ? pb : pa;
+      const bool ok = bi < nb && unsigned(phys) < unsigned(a.num_blocks) && (kb0 + bi) * BLK + trow < ctx;
+      const char* src = (ok ? cache + (int64_t(phys) * BLK + trow) * (ROW * 2) : zero + trow * (ROW * 2)) + 16 * lgr;
+#pragma unroll
+      for (int gq = 0; gq < 9; ++gq) dma16(src + 128 * gq, dst + 1024 * (9 * g + gq));
+    }
   };
+  auto stage_addr = [&](int i) { return uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes)); };
 
   f32x16_t acc[16];
 #pragma unroll
@@ -157,11 +165,136 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   }
   float m = -INFINITY, lsum = 0.f;
 
-  // per-lane LDS offsets: score operand (position r32 ^ 4h of half h) and transposed reads
-  const int sc_off = 16 * (32 * h + (r32 ^ (4 * h)));
+  // per-lane LDS offsets.  Score operand k (token r32, granule 2k + h): 9216 (r32 / 8) + 128 h +
+  // 16 (r32 % 8) + 256 k.  Transposed read of K step s, half r, channel tile jt (tokens 16s + 8r +
+  // 4 hh + li / 4, channels 32 jt + 16 cb + 4 (li % 4)): the base below + 18432 s + 9216 r + 512 jt.
+  const int sc_off = 9216 * (r32 >> 3) + 128 * h + 16 * (r32 & 7);
   const int G = lane >> 4, li = lane & 15;
-  const int c1 = (li >> 1) & 1;
-  const int tr_off = 1024 * (G & 1) + 16 * (32 * c1 + 4 * ((G >> 1) ^ c1) + (li >> 2)) + 8 * (li & 1);
+  const int tr_off = 128 * (2 * (G & 1) + ((li >> 1) & 1)) + 64 * (G >> 1) + 16 * (li >> 2) + 8 * (li & 1);
+  // smallest visible-token count over the wave's rows (its first row has the smallest query index)
+  const int Lw_min = min(ctx - a.q_len + ((grp * T + w) * 32) / a.H + 1, (kb0 + nb) * BLK);
+
+  // scores of step i: S^T on v_mfma_f32_32x32x16_bf16, operand reads kept D ahead of the MFMAs;
+  // masked only when the step reaches a row's limit (a uniform test)
+  auto scores = [&](int i, float (&sv)[16]) {
+    uint32_t spa = stage_addr(i) + uint32_t(sc_off);
+    asm volatile("" : "+v"(spa));  // one base per step: the 36 offsets fold into the reads
+    lds_u32x4_t* sp = (lds_u32x4_t*)uintptr_t(spa);
+    constexpr int D = 4;
+    u32x4_t ring[D];
+    f32x16_t sc = f32x16_t{};
+#pragma unroll
+    for (int k = 0; k < D; ++k) ring[k] = sp[16 * k];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const u32x4_t x = ring[k % D];
+      if (k + D < kChunks) ring[k % D] = sp[16 * (k + D)];
+      sc = mfma32x32(x, qreg[k], sc);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+#pragma unroll
+    for (int k = 0; k < kChunks - D; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = sc[r];
+    const int tok0 = (kb0 + 2 * i) * BLK;
+    if (tok0 + 32 > Lw_min) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = tok0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        sv[r] = t < Lw ? sv[r] : -INFINITY;
+      }
+    }
+  };
+
+  // row maximum over both lane halves (lanes l and l ^ 32 hold the same row)
+  auto row_max = [&](float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+  // reference-max update for a step with row max mb: returns whether the row restarts with
+  // accumulated terms (its accumulator must then be cleared); sets m, lsum and the exponent base
+  auto ref_update = [&](float mb, float& msub) {
+    const bool upd = mb > m + kReset;
+    const bool rst = upd && m != -INFINITY;
+    m = upd ? mb : m;
+    lsum = upd ? 0.f : lsum;
+    msub = m == -INFINITY ? 0.f : m;  // a row with nothing visible yet: every p is exp2(-inf) = 0
+    return rst;
+  };
+
+  // P.C of step i, with the step's softmax folded in.  Before the MFMAs: the row max, the reference
+  // update and P for the step's first 16 tokens (the first K step's B operand).  Then 32 slots of
+  // one MFMA each (two K steps of 16 tokens x 16 channel tiles); slots 0-11 also compute P for the
+  // second 16 tokens (needed from slot 16 on), pinned slot by slot so that the VALU work runs under
+  // the MFMAs.  Returns the lanes whose row restarts.
+  auto step = [&](int i, float (&sv)[16]) {
+    float t0 = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    float t1 = fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]));
+    float t2 = fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11]));
+    float t3 = fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]));
+    float msub;
+    const bool rst = ref_update(row_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3))), msub);
+    if (__any(rst)) {  // the row restarts: everything accumulated so far is dropped
+      mfma_drain();
+      if (rst) {
+#pragma unroll
+        for (int jt = 0; jt < 16; ++jt) {
+          acc[jt] = f32x16_t{};
+          asm volatile("" : "+a"(acc[jt]));
+        }
+      }
+    }
+    uint32_t pw[8];
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(sv[r] - msub), p1 = __builtin_amdgcn_exp2f(sv[r + 1] - msub);
+      lsum += p0 + p1;
+      pw[r >> 1] = cvt_pk_bf16(p0, p1);
+    }
+    asm volatile("" : "+v"(sv[8]));
+
+    uint32_t tpa = stage_addr(i) + uint32_t(tr_off);
+    asm volatile("" : "+v"(tpa));  // one base per step: the 64 offsets fold into the reads
+    lds_char_t* tp = (lds_char_t*)uintptr_t(tpa);
+    auto tr = [&](int k, int r) {  // slot k = 16 s + jt, read r: tokens 16s + 8r + 4(l/32) + 0..3
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tp + 512 * (k & 15) + 18432 * (k >> 4) + 9216 * r));
+    };
+    constexpr int D = 3;
+    s16x4_t ra[D], rb[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      ra[k] = tr(k, 0);
+      rb[k] = tr(k, 1);
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int s = k >> 4;
+      const u32x4_t pb = u32x4_t{pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]};
+      if ((k & 15) == 0) asm volatile("s_nop 4" ::"v"(pb));  // VALU-written B operand -> MFMA read
+      const u32x4_t av = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(ra[k % D], rb[k % D], 0, 1, 2, 3, 4, 5, 6, 7));
+      mfma32x32_acc(acc[k & 15], av, pb);
+      if (k + D < 32) {
+        ra[k % D] = tr(k + D, 0);
+        rb[k % D] = tr(k + D, 1);
+      }
+      if (k < 8) {  // p_r for r = 8 + k, in place
+        sv[8 + k] = __builtin_amdgcn_exp2f(sv[8 + k] - msub);
+        asm volatile("" : "+v"(sv[8 + k]));
+        if (k < 7) asm volatile("" : "+v"(sv[9 + k]));
+      } else if (k < 12) {  // pack and sum pairs of the second half
+        const int q = k - 4;
+        lsum += sv[2 * q] + sv[2 * q + 1];
+        pw[q] = cvt_pk_bf16(sv[2 * q], sv[2 * q + 1]);
+        asm volatile("" : "+v"(pw[q]), "+v"(lsum));
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
   // the query tile and block ids are in registers before the first transfer: from here on every
   // outstanding vector load is a transfer of this loop (the compiler's own waits in the loop would
@@ -171,116 +304,19 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   for (int i = 0; i < NSTAGE - 1; ++i)
     if (i < steps) issue(i);
 
+  float sv[16];
   for (int i = 0; i < steps; ++i) {
-    // step i's chunks have landed for this wave (the newer steps' DMAs may stay in flight), then
-    // for every wave; the barrier also retires the stage read at step i - 1
+    // step i's chunks have landed for this wave (the newer steps' transfers may stay in flight),
+    // then for every wave; the barrier also retires the stage read at step i - 1, which then takes
+    // step i + NSTAGE - 1
     if (i + NSTAGE - 2 < steps)
       wait_vmcnt<(NSTAGE - 2) * CPW>();
     else
       wait_vmcnt<0>();
     lds_barrier();
     if (i + NSTAGE - 1 < steps) issue(i + NSTAGE - 1);
-
-    // LDS byte address of the stage (32-bit)
-    const uint32_t st = uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes));
-    const int tok0 = (kb0 + 2 * i) * BLK;
-
-    // scores
-    f32x16_t sc = f32x16_t{};
-    {
-      uint32_t spa = st + uint32_t(sc_off);
-      asm volatile("" : "+v"(spa));
-      lds_u32x4_t* sp = (lds_u32x4_t*)uintptr_t(spa);
-      constexpr int D = 6;
-      u32x4_t ring[D];
-#pragma unroll
-      for (int k = 0; k < D; ++k) ring[k] = sp[64 * k];
-#pragma unroll
-      for (int k = 0; k < kChunks; ++k) {
-        const u32x4_t x = ring[k % D];
-        if (k + D < kChunks) ring[k % D] = sp[64 * (k + D)];
-        sc = mfma32x32(x, qreg[k], sc);
-      }
-      // keep the reads D ahead: D reads, then (MFMA, read) pairs, then the last D MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
-#pragma unroll
-      for (int k = 0; k < kChunks - D; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
-    }
-
-    // mask, running max, lazy rescale
-    float sv[16];
-    float mb = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = tok0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      sv[r] = t < Lw ? sc[r] : -INFINITY;
-      mb = fmaxf(mb, sv[r]);
-    }
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    // The reference max m of a row moves only when a score exceeds it by more than kReset; the
-    // row's earlier terms then weigh at most 2^-kReset each against the new maximum (at most 2^15
-    // tokens: <= 2^-49 in total, far below fp32 rounding), so the row restarts from zero instead
-    // of being rescaled: a masked AGPR write, no pass of the accumulator through VGPRs.
-    const bool upd = mb > m + kReset;
-    if (__any(upd)) {
-      if (upd) {
-        if (m != -INFINITY) {  // nothing was accumulated while m was -inf
-          mfma_drain();
-#pragma unroll
-          for (int jt = 0; jt < 16; ++jt) {
-            acc[jt] = f32x16_t{};
-            asm volatile("" : "+a"(acc[jt]));
-          }
-        }
-        lsum = 0.f;
-        m = mb;
-      }
-    }
-    uint32_t pw[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = sv[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m);
-      const float p1 = sv[r + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r + 1] - m);
-      lsum += p0 + p1;
-      pw[r >> 1] = cvt_pk_bf16(p0, p1);
-    }
-
-    // P.C: K step s covers tokens 16s..16s+15 of the step; B = P registers 8s..8s+7
-    {
-      // one base per step, opaque to the compiler so that the 64 constant offsets below fold into
-      // the instructions' immediate offsets (instead of 64 hoisted loop-invariant registers)
-      uint32_t tpa = st + uint32_t(tr_off);
-      asm volatile("" : "+v"(tpa));
-      lds_char_t* tp = (lds_char_t*)uintptr_t(tpa);
-      auto tr = [&](int s, int r, int jt) {
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tp + 2048 * jt + 256 * s + 128 * r));
-      };
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4_t pb = u32x4_t{pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]};
-        asm volatile("s_nop 4" ::"v"(pb));  // VALU-written B operand -> MFMA read
-        constexpr int D = 4;
-        s16x4_t ra[D], rb[D];
-#pragma unroll
-        for (int jt = 0; jt < D; ++jt) {
-          ra[jt] = tr(s, 0, jt);
-          rb[jt] = tr(s, 1, jt);
-        }
-#pragma unroll
-        for (int jt = 0; jt < 16; ++jt) {
-          const u32x4_t av = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(ra[jt % D], rb[jt % D], 0, 1, 2, 3, 4, 5, 6, 7));
-          if (jt + D < 16) {
-            ra[jt % D] = tr(s, 0, jt + D);
-            rb[jt % D] = tr(s, 1, jt + D);
-          }
-          mfma32x32_acc(acc[jt], av, pb);
-        }
-      }
-    }
+    scores(i, sv);
+    step(i, sv);
   }
 
   // partial of this wave's rows: channel 32jt + 8q + 4h + e sits in acc[jt][4q + e]
@@ -309,7 +345,7 @@ hipError_t launch_decode_mt32(const DecodeArgs& a, int T, hipStream_t s) {
       decode_bf16_mt32_kernel<2, 2><<<grid, 128, 0, s>>>(a);
       break;
     case 4:
-      decode_bf16_mt32_kernel<4, 3><<<grid, 256, 0, s>>>(a);
+      decode_bf16_mt32_kernel<4, 4><<<grid, 256, 0, s>>>(a);
       break;
     default:
       return hipErrorInvalidValue;
