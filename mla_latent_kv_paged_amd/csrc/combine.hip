@@ -10,8 +10,9 @@
 //   out^T[v, n] = sum_c W_uv[h][v, c] o_lat^T[c, n]   (K = 512, 16 steps of 16x16x32 bf16),
 // with o_lat carried as an unevaluated sum of two bf16 values (hi = bf16(o), lo = bf16(o - hi)),
 // i.e. about 16 significant bits, so the product loses nothing visible to the output rounding.
-// A workgroup owns 16 rows and a quarter (32) of the output channels; two waves compute 16
-// channels each, W_uv rows read straight from global memory.
+// A workgroup owns 16 rows and either all 128 output channels (four waves, 32 each) or, when the
+// (head, 16 rows) grid alone would leave CUs idle, a quarter of them (two waves, 16 each); W_uv
+// rows are read straight from global memory.
 // fp32 storage: the same merge, then W_uv on the vector ALUs.  Both accumulate in fp32.
 #include "mla_internal.h"
 
@@ -81,40 +82,64 @@ __device__ __forceinline__ int o_swz(int r) { return ((r & 7) << 1) | (r >> 3); 
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   const int h = blockIdx.x;
   const int r0 = blockIdx.y * 16;
-  const int vq = blockIdx.z;  // quarter of the 128 output channels
+  const int vq = blockIdx.z;  // part of the 128 output channels (one of v_parts)
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   __shared__ uint4 ohi[16 * 64];
   __shared__ uint4 olo[16 * 64];
 
-  // W_uv fragments of this workgroup's 32 output channels (waves 0 and 1 take 16 each): their
-  // loads do not depend on the merge, so they are issued first
+  // output channel tiles of 16: with 4 parts, waves 0 and 1 take one tile each of this
+  // workgroup's 32 channels; with 1 part, every wave takes two tiles of its 32.  The first tile's
+  // W_uv fragments do not depend on the merge, so their loads are issued first.
+  const int ntile = a.v_parts == 1 ? 2 : 1;
+  const int vbase = a.v_parts == 1 ? 32 * w : vq * 32 + (w & 1) * 16;
   const uint16_t* wuv_h = static_cast<const uint16_t*>(a.W_uv) + int64_t(h) * DV * DC;
-  const uint4* wrow = reinterpret_cast<const uint4*>(wuv_h + int64_t(vq * 32 + (w & 1) * 16 + (lane & 15)) * DC);
+  const uint4* wrow = reinterpret_cast<const uint4*>(wuv_h + int64_t(vbase + (lane & 15)) * DC);
   uint4 wf[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) wf[ks] = wrow[4 * ks + (lane >> 4)];
 
-  // merge the split partials: wave w owns rows 4w..4w+3, lane owns channels 8*lane..8*lane+7.
-  // Splits are taken in chunks of 4 up to the largest split count among the wave's rows; inside
-  // a chunk the loads are unconditional (slots past a row's own count hold stale values and are
-  // dropped by selection, never by multiplication).  Chunks are merged with a running max.
-  // context lengths of the wave's 4 rows: four independent loads, issued together
-  int ns[4], sl[4];
+  // merge the partials: wave w owns rows 4w..4w+3, lane owns channels 8*lane..8*lane+7.  Row rr's
+  // partials are base[rr] + j * stride[rr], j < ns[rr] (by split: consecutive slots; by piece:
+  // consecutive pieces of its stream).  They are taken in chunks of 4 up to the largest count
+  // among the wave's rows; inside a chunk the loads are unconditional (a row's index is clamped to
+  // its last partial and the surplus dropped by selection, never by multiplication).  Chunks are
+  // merged with a running max.
+  int ns[4], stride[4];
   int64_t base[4];
+  if (a.piece_tbl) {
+    int2 pt[4];
+    int rq[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = r0 + w * 4 + rr;
-    const int rowc = row < a.n_q ? row : a.n_q - 1;
-    base[rr] = (int64_t(rowc) * a.H + h) * a.n_split;
-    sl[rr] = a.seq_lens[rowc / a.q_len];
-  }
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = r0 + w * 4 + rr;
+      const int rowc = row < a.n_q ? row : a.n_q - 1;
+      rq[rr] = (rowc % a.q_len) * a.H + h;  // row within the sequence
+      pt[rr] = a.piece_tbl[(rowc / a.q_len) * a.n_grp + rq[rr] / a.rows_per_piece];
+    }
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int ctx = clamp_ctx(sl[rr], a.q_len, a.max_seq_len);
-    const int nblk = (ctx + BLK - 1) / BLK;
-    const int n = (nblk + a.split_blocks - 1) / a.split_blocks;
-    ns[rr] = (r0 + w * 4 + rr < a.n_q) ? (n < a.n_split ? n : a.n_split) : 0;
+    for (int rr = 0; rr < 4; ++rr) {
+      base[rr] = int64_t(pt[rr].x) * a.rows_per_piece + rq[rr] % a.rows_per_piece;
+      stride[rr] = a.rows_per_piece;
+      ns[rr] = (r0 + w * 4 + rr < a.n_q) ? pt[rr].y : 0;
+    }
+  } else {
+    int sl[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = r0 + w * 4 + rr;
+      const int rowc = row < a.n_q ? row : a.n_q - 1;
+      base[rr] = (int64_t(rowc) * a.H + h) * a.n_split;
+      sl[rr] = a.seq_lens[rowc / a.q_len];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int ctx = clamp_ctx(sl[rr], a.q_len, a.max_seq_len);
+      const int nblk = (ctx + BLK - 1) / BLK;
+      const int n = (nblk + a.split_blocks - 1) / a.split_blocks;
+      stride[rr] = 1;
+      ns[rr] = (r0 + w * 4 + rr < a.n_q) ? (n < a.n_split ? n : a.n_split) : 0;
+    }
   }
   const int ns_max = __builtin_amdgcn_readfirstlane(max(max(ns[0], ns[1]), max(ns[2], ns[3])));
   float M[4], den[4], o[4][8];
@@ -132,9 +157,10 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int jc = j0 + jj < a.n_split ? j0 + jj : 0;
-        ml[rr][jj] = a.part_ml[base[rr] + jc];
-        const float4* src = reinterpret_cast<const float4*>(a.part_acc + (base[rr] + jc) * DC + 8 * lane);
+        const int jc = min(j0 + jj, max(ns[rr] - 1, 0));
+        const int64_t pi = base[rr] + int64_t(jc) * stride[rr];
+        ml[rr][jj] = a.part_ml[pi];
+        const float4* src = reinterpret_cast<const float4*>(a.part_acc + pi * DC + 8 * lane);
         va[rr][jj] = src[0];
         vb[rr][jj] = src[1];
       }
@@ -180,28 +206,35 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
     olo[gi] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   __syncthreads();
-  if (w >= 2) return;
+  if (a.v_parts != 1 && w >= 2) return;
 
-  // out^T[v, n] for 16 output channels v of this wave and the 16 rows n of this workgroup
+  // out^T[v, n] for 16 output channels v per tile and the 16 rows n of this workgroup
   const int r16 = lane & 15, g = lane >> 4;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    const int c = 4 * ks + g;
-    acc = mfma32(wf[ks], ohi[r16 * 64 + (c ^ o_swz(r16))], acc);
-    acc = mfma32(wf[ks], olo[r16 * 64 + (c ^ o_swz(r16))], acc);
-  }
-  // lane holds query row r0 + r16 (column), output channels vq*32 + 16w + 4g .. +3 (rows)
   const int row = r0 + r16;
-  if (row < a.n_q) {
-    uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.H + h) * DV + vq * 32 + 16 * w + 4 * g;
-    *reinterpret_cast<uint2*>(out) = make_uint2(cvt_pk_bf16(acc[0], acc[1]), cvt_pk_bf16(acc[2], acc[3]));
+  for (int t = 0; t < ntile; ++t) {
+    if (t > 0) {
+      const uint4* wr = reinterpret_cast<const uint4*>(wuv_h + int64_t(vbase + 16 * t + (lane & 15)) * DC);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) wf[ks] = wr[4 * ks + (lane >> 4)];
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const int c = 4 * ks + g;
+      acc = mfma32(wf[ks], ohi[r16 * 64 + (c ^ o_swz(r16))], acc);
+      acc = mfma32(wf[ks], olo[r16 * 64 + (c ^ o_swz(r16))], acc);
+    }
+    // lane holds query row r0 + r16 (column), output channels vbase + 16t + 4g .. +3 (rows)
+    if (row < a.n_q) {
+      uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.H + h) * DV + vbase + 16 * t + 4 * g;
+      *reinterpret_cast<uint2*>(out) = make_uint2(cvt_pk_bf16(acc[0], acc[1]), cvt_pk_bf16(acc[2], acc[3]));
+    }
   }
 }
 
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s) {
   if (bf16) {
-    dim3 grid(a.H, (a.n_q + 15) / 16, DV / 32);
+    dim3 grid(a.H, (a.n_q + 15) / 16, a.v_parts);
     combine_bf16_kernel<<<grid, 256, 0, s>>>(a);
   } else {
     dim3 grid(a.H, (a.n_q + 15) / 16);

@@ -79,264 +79,339 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 template <int T, int NSTAGE>
 __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) {
   constexpr int CPW = kChunks / T;  // DMA chunks per wave per step
+  constexpr int RP = 32 * T;        // rows of a piece (one tile group)
   static_assert(kChunks % T == 0, "chunks split evenly over the waves");
   static_assert(NSTAGE >= 2, "a step is read while a later one is loaded");
   __shared__ __attribute__((aligned(16))) char stage_mem[NSTAGE * kStageBytes];
-
-  // work unit u = (sequence b, split j, tile group grp), grp fastest; XCD-aware order: the
-  // dispatcher deals consecutive workgroup ids round-robin over the 8 XCDs, so id x runs on XCD
-  // x % 8 and takes unit (x % 8) * per_xcd + x / 8 (neighbouring units share an L2)
-  const int n_grp = a.n_rt / T;  // n_rt = tiles of 32 rows per sequence here
-  const int per_xcd = (a.units + 7) >> 3;
-  const int u = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
-  if (u >= a.units) return;
-  const int grp = u % n_grp;
-  const int j = (u / n_grp) % a.n_split;
-  const int b = u / (n_grp * a.n_split);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;    // lane half: K block of the MFMA operands
   const int r32 = lane & 31;  // row of the tile (N index) / token of a score operand (M index)
+  const int n_grp = a.n_rt / T;  // tile groups per sequence (n_rt = tiles of 32 rows)
+  const int n_wg = a.units;
 
-  const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
-  const int nblk = (ctx + BLK - 1) / BLK;
-  const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
-  if (j >= ns) return;
-  const int kb0 = j * a.split_blocks;
-  const int nb = min(kb0 + a.split_blocks, nblk) - kb0;  // blocks of this split
-  const int steps = (nb + 1) >> 1;
-
-  // this lane's row: rr = tile row within the sequence, rows ordered (query, head)
-  const int rr = (grp * T + w) * 32 + r32;
-  const int iq = rr / a.H;
-  // tokens visible to the row in this split: causal limit, and the split's end (a step spans two
-  // blocks, so with an odd split size its last step reaches one block past the split)
-  const int Lw = min(ctx - a.q_len + iq + 1, (kb0 + nb) * BLK);
-  const int64_t R = int64_t(b) * a.q_len * a.H + rr;
-
-  // query tile: B operand of the score MFMA k is granule 2k + h of the row
-  u32x4_t qreg[kChunks];
-  {
-    const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.qcat) + R * ROW);
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) qreg[k] = qsrc[2 * k + h];
-  }
-
-  // block ids of the split in registers: lane l holds entries l and 64 + l (<= 128 blocks)
-  const int* bt = a.block_table + int64_t(b) * a.bt_stride;
-  const int phys_lo = lane < nb ? bt[kb0 + lane] : 0;
-  const int phys_hi = lane + 64 < nb ? bt[kb0 + 64 + lane] : 0;
-  auto phys_of = [&](int i) {
-    return i < 64 ? __builtin_amdgcn_readlane(phys_lo, i & 63) : __builtin_amdgcn_readlane(phys_hi, i & 63);
+  // ---- balanced partition.  Stream (b, grp) = tile group grp of sequence b, L_b steps of two
+  // blocks; streams are ordered (b, grp) and the workgroups take equal contiguous ranges of the
+  // concatenated steps.  A range cuts streams into pieces; the piece of stream s done by workgroup
+  // g keeps its partial under id g + s (unique: between consecutive pieces g or s grows), so the
+  // pieces of a stream have consecutive ids.
+  auto steps_of = [&](int b) {
+    const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
+    return (((ctx + BLK - 1) / BLK) + 1) >> 1;
   };
+  int S = 0;  // total steps (uniform)
+  for (int c0 = 0; c0 < a.batch; c0 += 64) {
+    int v = c0 + lane < a.batch ? steps_of(c0 + lane) : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    S += __builtin_amdgcn_readfirstlane(v);
+  }
+  S *= n_grp;
+  const int W = (S + n_wg - 1) / n_wg;
+  const int lo = int(blockIdx.x) * W;
+  const int hi = min(lo + W, S);
+  // the sequence holding step lo: the last b whose streams start at or before lo; workgroup 0
+  // also records each stream's first piece id and piece count for the combine
+  int bstar = 0, Cstar = 0, Lstar = 0;
+  {
+    int C = 0;  // steps of the sequences before this chunk, per tile group
+    for (int c0 = 0; c0 < a.batch; c0 += 64) {
+      const int b = c0 + lane;
+      const int L = b < a.batch ? steps_of(b) : 0;
+      int incl = L;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int pre = C + incl - L;  // steps before sequence b, per tile group
+      const uint64_t before = __ballot(b < a.batch && n_grp * pre <= lo);
+      if (before) {
+        const int k = 63 - __builtin_clzll(before);  // the last such lane (prefixes grow with b)
+        bstar = c0 + k;
+        Cstar = __builtin_amdgcn_readlane(pre, k);
+        Lstar = __builtin_amdgcn_readlane(L, k);
+      }
+      if (blockIdx.x == 0 && w == 0 && b < a.batch) {
+        for (int grp = 0; grp < n_grp; ++grp) {
+          const int st = n_grp * pre + grp * L, s = b * n_grp + grp;
+          const int gf = st / W, gl = (st + L - 1) / W;
+          a.piece_tbl[s] = make_int2(gf + s, gl - gf + 1);
+        }
+      }
+      C += __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+    }
+  }
+  if (lo >= hi) return;
 
-  // DMA geometry: wave w takes chunks K = w CPW .. w CPW + CPW - 1 (token groups tg = K / 9); lane l
-  // of chunk K reads token 8 tg + l % 8, granule 8 (K % 9) + l / 8
+  lds_char_t* const stages = (lds_char_t*)stage_mem;
   const char* cache = static_cast<const char*>(a.cache);
   const char* zero = static_cast<const char*>(a.zero_block);
-  lds_char_t* const stages = (lds_char_t*)stage_mem;
   const int lrow = lane & 7, lgr = lane >> 3;
-
-  auto issue = [&](int i) {  // DMA of step i into stage i % NSTAGE (this wave's chunks)
-    const int pa = phys_of((2 * i) & 127), pb = phys_of((2 * i + 1) & 127);
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes + w * CPW * 1024)));
-    constexpr int NTG = (CPW + 8) / 9;  // token groups this wave touches (CPW is 9, 18 or 36)
-#pragma unroll
-    for (int g = 0; g < NTG; ++g) {
-      const int tg = (w * CPW) / 9 + g;                 // token group of the step (uniform)
-      const int bi = 2 * i + (tg >> 1);                  // block index within the split
-      const int trow = 8 * (tg & 1) + lrow;              // token row within the block
-      const int phys = (tg >> 1) ? pb : pa;
-      const bool ok = bi < nb && unsigned(phys) < unsigned(a.num_blocks) && (kb0 + bi) * BLK + trow < ctx;
-      const char* src = (ok ? cache + (int64_t(phys) * BLK + trow) * (ROW * 2) : zero + trow * (ROW * 2)) + 16 * lgr;
-#pragma unroll
-      for (int gq = 0; gq < 9; ++gq) dma16(src + 128 * gq, dst + 1024 * (9 * g + gq));
-    }
-  };
-  auto stage_addr = [&](int i) { return uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes)); };
-
-  f32x16_t acc[16];
-#pragma unroll
-  for (int jt = 0; jt < 16; ++jt) {
-    acc[jt] = f32x16_t{};
-    asm volatile("" : "+a"(acc[jt]));
-  }
-  float m = -INFINITY, lsum = 0.f;
-
   // per-lane LDS offsets.  Score operand k (token r32, granule 2k + h): 9216 (r32 / 8) + 128 h +
   // 16 (r32 % 8) + 256 k.  Transposed read of K step s, half r, channel tile jt (tokens 16s + 8r +
   // 4 hh + li / 4, channels 32 jt + 16 cb + 4 (li % 4)): the base below + 18432 s + 9216 r + 512 jt.
   const int sc_off = 9216 * (r32 >> 3) + 128 * h + 16 * (r32 & 7);
   const int G = lane >> 4, li = lane & 15;
   const int tr_off = 128 * (2 * (G & 1) + ((li >> 1) & 1)) + 64 * (G >> 1) + 16 * (li >> 2) + 8 * (li & 1);
-  // smallest visible-token count over the wave's rows (its first row has the smallest query index)
-  const int Lw_min = min(ctx - a.q_len + ((grp * T + w) * 32) / a.H + 1, (kb0 + nb) * BLK);
-
-  // scores of step i: S^T on v_mfma_f32_32x32x16_bf16, operand reads kept D ahead of the MFMAs;
-  // masked only when the step reaches a row's limit (a uniform test)
-  auto scores = [&](int i, float (&sv)[16]) {
-    uint32_t spa = stage_addr(i) + uint32_t(sc_off);
-    asm volatile("" : "+v"(spa));  // one base per step: the 36 offsets fold into the reads
-    lds_u32x4_t* sp = (lds_u32x4_t*)uintptr_t(spa);
-    constexpr int D = 4;
-    u32x4_t ring[D];
-    f32x16_t sc = f32x16_t{};
-#pragma unroll
-    for (int k = 0; k < D; ++k) ring[k] = sp[16 * k];
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const u32x4_t x = ring[k % D];
-      if (k + D < kChunks) ring[k % D] = sp[16 * (k + D)];
-      sc = mfma32x32(x, qreg[k], sc);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
-#pragma unroll
-    for (int k = 0; k < kChunks - D; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = sc[r];
-    const int tok0 = (kb0 + 2 * i) * BLK;
-    if (tok0 + 32 > Lw_min) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = tok0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        sv[r] = t < Lw ? sv[r] : -INFINITY;
-      }
-    }
-  };
+  auto stage_addr = [&](int i) { return uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes)); };
 
   // row maximum over both lane halves (lanes l and l ^ 32 hold the same row)
   auto row_max = [&](float x) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
-  // reference-max update for a step with row max mb: returns whether the row restarts with
-  // accumulated terms (its accumulator must then be cleared); sets m, lsum and the exponent base
-  auto ref_update = [&](float mb, float& msub) {
-    const bool upd = mb > m + kReset;
-    const bool rst = upd && m != -INFINITY;
-    m = upd ? mb : m;
-    lsum = upd ? 0.f : lsum;
-    msub = m == -INFINITY ? 0.f : m;  // a row with nothing visible yet: every p is exp2(-inf) = 0
-    return rst;
-  };
 
-  // P.C of step i, with the step's softmax folded in.  Before the MFMAs: the row max, the reference
-  // update and P for the step's first 16 tokens (the first K step's B operand).  Then 32 slots of
-  // one MFMA each (two K steps of 16 tokens x 16 channel tiles); slots 0-11 also compute P for the
-  // second 16 tokens (needed from slot 16 on), pinned slot by slot so that the VALU work runs under
-  // the MFMAs.  Returns the lanes whose row restarts.
-  auto step = [&](int i, float (&sv)[16]) {
-    float t0 = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    float t1 = fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]));
-    float t2 = fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11]));
-    float t3 = fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]));
-    float msub;
-    const bool rst = ref_update(row_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3))), msub);
-    if (__any(rst)) {  // the row restarts: everything accumulated so far is dropped
-      mfma_drain();
-      if (rst) {
+  // ---- one piece: steps k0..k1-1 of stream (b, grp), partial under id pid
+  auto piece = [&](const int b, const int grp, const int k0, const int k1, const int pid) {
+    const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
+    const int nblk = (ctx + BLK - 1) / BLK;
+    const int kb0 = 2 * k0;
+    const int nb = min(2 * k1, nblk) - kb0;  // blocks of the piece
+    const int steps = k1 - k0;
+
+    // this lane's row: rr = tile row within the sequence, rows ordered (query, head)
+    const int rr = (grp * T + w) * 32 + r32;
+    const int iq = rr / a.H;
+    // tokens visible to the row in this piece: causal limit and the piece's end (a step spans two
+    // blocks, so an odd block count ends the last step one block past the piece)
+    const int Lw = min(ctx - a.q_len + iq + 1, (kb0 + nb) * BLK);
+    const int Lw_min = min(ctx - a.q_len + ((grp * T + w) * 32) / a.H + 1, (kb0 + nb) * BLK);
+    const int64_t R = int64_t(b) * a.q_len * a.H + rr;
+
+    // query tile: B operand of the score MFMA k is granule 2k + h of the row
+    u32x4_t qreg[kChunks];
+    {
+      const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.qcat) + R * ROW);
 #pragma unroll
-        for (int jt = 0; jt < 16; ++jt) {
-          acc[jt] = f32x16_t{};
-          asm volatile("" : "+a"(acc[jt]));
+      for (int k = 0; k < kChunks; ++k) qreg[k] = qsrc[2 * k + h];
+    }
+    const int* bt_row = a.block_table + int64_t(b) * a.bt_stride + kb0;
+
+    // block ids of step i through the scalar cache (read only); the second id is clamped into the
+    // piece (its lanes are masked when the step has one block)
+    auto ids = [&](int i, int& pa, int& pb) {
+      const uint32_t oa = 4u * uint32_t(2 * i), ob = 4u * uint32_t(min(2 * i + 1, nb - 1));
+      asm volatile("s_load_dword %0, %2, %3\n\ts_load_dword %1, %2, %4"
+                   : "=&s"(pa), "=&s"(pb) : "s"(bt_row), "s"(oa), "s"(ob));
+    };
+    auto ids_ready = [&](int& pa, int& pb) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(pa), "+s"(pb)); };
+
+    // DMA of step i into stage i % NSTAGE: wave w takes chunks K = w CPW .. w CPW + CPW - 1 (token
+    // groups tg = K / 9); lane l of chunk K reads token 8 tg + l % 8, granule 8 (K % 9) + l / 8
+    auto issue = [&](int i, int pa, int pb) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes + w * CPW * 1024)));
+      constexpr int NTG = (CPW + 8) / 9;  // token groups this wave touches (CPW is 9, 18 or 36)
+#pragma unroll
+      for (int gi = 0; gi < NTG; ++gi) {
+        const int tg = (w * CPW) / 9 + gi;     // token group of the step (uniform)
+        const int bi = 2 * i + (tg >> 1);       // block index within the piece
+        const int trow = 8 * (tg & 1) + lrow;   // token row within the block
+        const int phys = (tg >> 1) ? pb : pa;
+        const bool ok = bi < nb && unsigned(phys) < unsigned(a.num_blocks) && (kb0 + bi) * BLK + trow < ctx;
+        const char* src = (ok ? cache + (int64_t(phys) * BLK + trow) * (ROW * 2) : zero + trow * (ROW * 2)) + 16 * lgr;
+#pragma unroll
+        for (int gq = 0; gq < 9; ++gq) dma16(src + 128 * gq, dst + 1024 * (9 * gi + gq));
+      }
+    };
+
+    f32x16_t acc[16];
+#pragma unroll
+    for (int jt = 0; jt < 16; ++jt) {
+      acc[jt] = f32x16_t{};
+      asm volatile("" : "+a"(acc[jt]));
+    }
+    float m = -INFINITY, lsum = 0.f;
+
+    // reference-max update for a step with row max mb: returns whether the row restarts with
+    // accumulated terms (its accumulator must then be cleared); sets m, lsum and the exponent base
+    auto ref_update = [&](float mb, float& msub) {
+      const bool upd = mb > m + kReset;
+      const bool rst = upd && m != -INFINITY;
+      m = upd ? mb : m;
+      lsum = upd ? 0.f : lsum;
+      msub = m == -INFINITY ? 0.f : m;  // a row with nothing visible yet: every p is exp2(-inf) = 0
+      return rst;
+    };
+
+    // scores of step i: S^T on v_mfma_f32_32x32x16_bf16, operand reads kept D ahead of the MFMAs;
+    // masked only when the step reaches a row's limit (a uniform test)
+    auto scores = [&](int i, float (&sv)[16]) {
+      uint32_t spa = stage_addr(i) + uint32_t(sc_off);
+      asm volatile("" : "+v"(spa));  // one base per step: the 36 offsets fold into the reads
+      lds_u32x4_t* sp = (lds_u32x4_t*)uintptr_t(spa);
+      constexpr int D = 4;
+      u32x4_t ring[D];
+      f32x16_t sc = f32x16_t{};
+#pragma unroll
+      for (int k = 0; k < D; ++k) ring[k] = sp[16 * k];
+#pragma unroll
+      for (int k = 0; k < kChunks; ++k) {
+        const u32x4_t x = ring[k % D];
+        if (k + D < kChunks) ring[k % D] = sp[16 * (k + D)];
+        sc = mfma32x32(x, qreg[k], sc);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+#pragma unroll
+      for (int k = 0; k < kChunks - D; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = sc[r];
+      const int tok0 = (kb0 + 2 * i) * BLK;
+      if (tok0 + 32 > Lw_min) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = tok0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          sv[r] = t < Lw ? sv[r] : -INFINITY;
         }
       }
-    }
-    uint32_t pw[8];
-#pragma unroll
-    for (int r = 0; r < 8; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(sv[r] - msub), p1 = __builtin_amdgcn_exp2f(sv[r + 1] - msub);
-      lsum += p0 + p1;
-      pw[r >> 1] = cvt_pk_bf16(p0, p1);
-    }
-    asm volatile("" : "+v"(sv[8]));
-
-    uint32_t tpa = stage_addr(i) + uint32_t(tr_off);
-    asm volatile("" : "+v"(tpa));  // one base per step: the 64 offsets fold into the reads
-    lds_char_t* tp = (lds_char_t*)uintptr_t(tpa);
-    auto tr = [&](int k, int r) {  // slot k = 16 s + jt, read r: tokens 16s + 8r + 4(l/32) + 0..3
-      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tp + 512 * (k & 15) + 18432 * (k >> 4) + 9216 * r));
     };
-    constexpr int D = 3;
-    s16x4_t ra[D], rb[D];
+
+    // P.C of step i, with the step's softmax folded in.  Before the MFMAs: the row max, the
+    // reference update and P for the step's first 16 tokens (the first K step's B operand).  Then
+    // 32 slots of one MFMA each (two K steps of 16 tokens x 16 channel tiles); slots 0-11 also
+    // compute P for the second 16 tokens (needed from slot 16 on), pinned slot by slot so that the
+    // VALU work runs under the MFMAs.
+    auto step = [&](int i, float (&sv)[16]) {
+      float t0 = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      float t1 = fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]));
+      float t2 = fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11]));
+      float t3 = fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]));
+      float msub;
+      const bool rst = ref_update(row_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3))), msub);
+      if (__any(rst)) {  // the row restarts: everything accumulated so far is dropped
+        mfma_drain();
+        if (rst) {
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-      ra[k] = tr(k, 0);
-      rb[k] = tr(k, 1);
-    }
+          for (int jt = 0; jt < 16; ++jt) {
+            acc[jt] = f32x16_t{};
+            asm volatile("" : "+a"(acc[jt]));
+          }
+        }
+      }
+      uint32_t pw[8];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const int s = k >> 4;
-      const u32x4_t pb = u32x4_t{pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]};
-      if ((k & 15) == 0) asm volatile("s_nop 4" ::"v"(pb));  // VALU-written B operand -> MFMA read
-      const u32x4_t av = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(ra[k % D], rb[k % D], 0, 1, 2, 3, 4, 5, 6, 7));
-      mfma32x32_acc(acc[k & 15], av, pb);
-      if (k + D < 32) {
-        ra[k % D] = tr(k + D, 0);
-        rb[k % D] = tr(k + D, 1);
+      for (int r = 0; r < 8; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[r] - msub), p1 = __builtin_amdgcn_exp2f(sv[r + 1] - msub);
+        lsum += p0 + p1;
+        pw[r >> 1] = cvt_pk_bf16(p0, p1);
       }
-      if (k < 8) {  // p_r for r = 8 + k, in place
-        sv[8 + k] = __builtin_amdgcn_exp2f(sv[8 + k] - msub);
-        asm volatile("" : "+v"(sv[8 + k]));
-        if (k < 7) asm volatile("" : "+v"(sv[9 + k]));
-      } else if (k < 12) {  // pack and sum pairs of the second half
-        const int q = k - 4;
-        lsum += sv[2 * q] + sv[2 * q + 1];
-        pw[q] = cvt_pk_bf16(sv[2 * q], sv[2 * q + 1]);
-        asm volatile("" : "+v"(pw[q]), "+v"(lsum));
+      asm volatile("" : "+v"(sv[8]));
+
+      uint32_t tpa = stage_addr(i) + uint32_t(tr_off);
+      asm volatile("" : "+v"(tpa));  // one base per step: the 64 offsets fold into the reads
+      lds_char_t* tp = (lds_char_t*)uintptr_t(tpa);
+      auto tr = [&](int k, int r) {  // slot k = 16 s + jt, read r: tokens 16s + 8r + 4(l/32) + 0..3
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tp + 512 * (k & 15) + 18432 * (k >> 4) + 9216 * r));
+      };
+      constexpr int D = 3;
+      s16x4_t ra[D], rb[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        ra[k] = tr(k, 0);
+        rb[k] = tr(k, 1);
       }
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int s = k >> 4;
+        const u32x4_t pb = u32x4_t{pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]};
+        if ((k & 15) == 0) asm volatile("s_nop 4" ::"v"(pb));  // VALU-written B operand -> MFMA read
+        const u32x4_t av = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(ra[k % D], rb[k % D], 0, 1, 2, 3, 4, 5, 6, 7));
+        mfma32x32_acc(acc[k & 15], av, pb);
+        if (k + D < 32) {
+          ra[k % D] = tr(k + D, 0);
+          rb[k % D] = tr(k + D, 1);
+        }
+        if (k < 8) {  // p_r for r = 8 + k, in place
+          sv[8 + k] = __builtin_amdgcn_exp2f(sv[8 + k] - msub);
+          asm volatile("" : "+v"(sv[8 + k]));
+          if (k < 7) asm volatile("" : "+v"(sv[9 + k]));
+        } else if (k < 12) {  // pack and sum pairs of the second half
+          const int q = k - 4;
+          lsum += sv[2 * q] + sv[2 * q + 1];
+          pw[q] = cvt_pk_bf16(sv[2 * q], sv[2 * q + 1]);
+          asm volatile("" : "+v"(pw[q]), "+v"(lsum));
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // the query tile is in registers (and the previous piece's stores are out) before the first
+    // transfer: from here on every outstanding vector memory operation is a transfer of this piece
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i) {
+      if (i < steps) {
+        int pa, pb;
+        ids(i, pa, pb);
+        ids_ready(pa, pb);
+        issue(i, pa, pb);
+      }
     }
+    float sv[16];
+    for (int i = 0; i < steps; ++i) {
+      // ids of the step to load next, fetched under the wait below
+      const int inext = i + NSTAGE - 1;
+      int pa = 0, pb = 0;
+      if (inext < steps) ids(inext, pa, pb);
+      // step i's chunks have landed for this wave (newer steps' transfers may stay in flight),
+      // then for every wave; the barrier also retires the stage read at step i - 1, which then
+      // takes step i + NSTAGE - 1
+      if (i + NSTAGE - 2 < steps)
+        wait_vmcnt<(NSTAGE - 2) * CPW>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (inext < steps) {
+        ids_ready(pa, pb);
+        issue(inext, pa, pb);
+      }
+      scores(i, sv);
+      step(i, sv);
+    }
+
+    // partial of this wave's rows: channel 32jt + 8q + 4h + e sits in acc[jt][4q + e]
+    mfma_drain();
+    lsum += __shfl_xor(lsum, 32, 64);
+    const int64_t pidx = int64_t(pid) * RP + w * 32 + r32;
+    float* dst = a.part_acc + pidx * DC;
+#pragma unroll
+    for (int jt = 0; jt < 16; ++jt) {
+      f32x16_t v = acc[jt];
+      asm volatile("" : "+v"(v));  // one tile at a time out of the AGPRs
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t*>(dst + 32 * jt + 8 * q + 4 * h) = f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    }
+    if (h == 0) a.part_ml[pidx] = make_float2(m, lsum);
+    lds_barrier();  // every wave is done with the stages before the next piece refills them
   };
 
-  // the query tile and block ids are in registers before the first transfer: from here on every
-  // outstanding vector load is a transfer of this loop (the compiler's own waits in the loop would
-  // otherwise count the query loads and drain the transfers in flight)
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int i = 0; i < NSTAGE - 1; ++i)
-    if (i < steps) issue(i);
-
-  float sv[16];
-  for (int i = 0; i < steps; ++i) {
-    // step i's chunks have landed for this wave (the newer steps' transfers may stay in flight),
-    // then for every wave; the barrier also retires the stage read at step i - 1, which then takes
-    // step i + NSTAGE - 1
-    if (i + NSTAGE - 2 < steps)
-      wait_vmcnt<(NSTAGE - 2) * CPW>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    if (i + NSTAGE - 1 < steps) issue(i + NSTAGE - 1);
-    scores(i, sv);
-    step(i, sv);
+  // ---- walk this workgroup's range piece by piece
+  int b = bstar, Lb = Lstar;
+  int off = lo - n_grp * Cstar;  // position within sequence b's streams
+  int grp = off / Lb, k0 = off % Lb;
+  for (int q = lo; q < hi;) {
+    const int k1 = min(Lb, k0 + (hi - q));
+    piece(b, grp, k0, k1, int(blockIdx.x) + b * n_grp + grp);
+    q += k1 - k0;
+    k0 = 0;
+    if (++grp == n_grp) {
+      grp = 0;
+      ++b;
+      if (q < hi) Lb = steps_of(b);
+    }
   }
-
-  // partial of this wave's rows: channel 32jt + 8q + 4h + e sits in acc[jt][4q + e]
-  mfma_drain();
-  lsum += __shfl_xor(lsum, 32, 64);
-  const int64_t pidx = R * a.n_split + j;
-  float* dst = a.part_acc + pidx * DC;
-#pragma unroll
-  for (int jt = 0; jt < 16; ++jt) {
-    f32x16_t v = acc[jt];
-    asm volatile("" : "+v"(v));  // one tile at a time out of the AGPRs
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4_t*>(dst + 32 * jt + 8 * q + 4 * h) = f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-  }
-  if (h == 0) a.part_ml[pidx] = make_float2(m, lsum);
 }
 
 hipError_t launch_decode_mt32(const DecodeArgs& a, int T, hipStream_t s) {
-  const int grid = ((a.units + 7) >> 3) << 3;
+  const int grid = a.units;  // one workgroup per resident slot, each with an equal share
   switch (T) {
     case 1:
       decode_bf16_mt32_kernel<1, 2><<<grid, 64, 0, s>>>(a);

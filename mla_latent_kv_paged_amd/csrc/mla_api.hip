@@ -1,6 +1,7 @@
 // Host side of libmla: argument validation, context ownership, workspace sizing, the split
 // heuristic and the launch sequence of one decode step.  Every entry point is extern "C" and
 // returns an mla_status; no exception crosses the boundary.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -42,6 +43,8 @@ struct mla_ctx {
   void* qcat = nullptr;
   float* part_acc = nullptr;
   float2* part_ml = nullptr;
+  int2* piece_tbl = nullptr;  // 32-row kernel: per stream (first piece id, piece count)
+  int32_t max_wg32 = 0;       // 32-row kernel: most workgroups the partial buffer holds pieces for
   int32_t max_split = 1;
   int32_t forced_split_blocks = 0;
   int32_t forced_waves = 0;
@@ -65,6 +68,7 @@ void ctx_release(mla_ctx* c) {
   hipFree(c->qcat);
   hipFree(c->part_acc);
   hipFree(c->part_ml);
+  hipFree(c->piece_tbl);
   if (c->prof.created)
     for (int k = 0; k < MLA_K_COUNT; ++k)
       for (int i = 0; i < kProfRing; ++i) {
@@ -193,8 +197,14 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
   alloc(reinterpret_cast<void**>(&c->gamma), DC * sizeof(double));
   alloc(reinterpret_cast<void**>(&c->rope), size_t(cfg->max_position + 1) * NPAIR * sizeof(double2));
   alloc(&c->qcat, rows * ROW * esz);
-  alloc(reinterpret_cast<void**>(&c->part_acc), rows * c->max_split * DC * sizeof(float));
-  alloc(reinterpret_cast<void**>(&c->part_ml), rows * c->max_split * sizeof(float2));
+  // partials: by split (rows x max_split) for the one-tile and fp32 kernels; by piece for the
+  // 32-row kernel, at most (workgroups + streams) pieces of 32 T rows, i.e. at most
+  // 128 * max_wg32 + rows rows (streams of a decode hold rows / (32 T) pieces' worth of rows)
+  c->max_wg32 = 2 * c->cu_count;
+  const size_t part_rows = std::max(rows * c->max_split, size_t(128) * c->max_wg32 + rows);
+  alloc(reinterpret_cast<void**>(&c->part_acc), part_rows * DC * sizeof(float));
+  alloc(reinterpret_cast<void**>(&c->part_ml), part_rows * sizeof(float2));
+  alloc(reinterpret_cast<void**>(&c->piece_tbl), (rows / 32 + 1) * sizeof(int2));
   if (e != hipSuccess) {
     ctx_release(c);
     return hip_status(e);
@@ -289,16 +299,24 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   const int n_rt = t32 ? n_rt32 : n_rt16;
   const int waves = ctx->bf16 ? (t32 ? t32 : (ctx->forced_waves > 0 ? ctx->forced_waves : 2)) : 1;
   const int groups = t32 ? n_rt / t32 : n_rt;  // workgroups per (sequence, split)
-  const int blocks_per_wave_cap = t32 ? 128 : 128 * waves;  // block ids held in two registers
-  int sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
-                                        : choose_split_blocks(ctx, batch * groups, max_blocks, t32 ? 1 : waves);
-  const int min_sb = (max_blocks + ctx->max_split - 1) / ctx->max_split;  // workspace bound
-  if (sb < min_sb) sb = min_sb;
-  if (sb > blocks_per_wave_cap) sb = blocks_per_wave_cap;
-  if (sb > max_blocks) sb = max_blocks;
-  const int n_split = (max_blocks + sb - 1) / sb;
-  ctx->last_split_blocks = sb;
-  ctx->last_n_split = n_split;
+  int sb = 0, n_split = 0, n_wg = 0;
+  if (t32) {
+    // balanced partition over one workgroup per resident slot (T = 4 fills a CU; T <= 2, two)
+    n_wg = ctx->cu_count * (t32 == 4 ? 1 : 2);
+    if (ctx->forced_split_blocks > 0) n_wg = ctx->forced_split_blocks;  // tuning: workgroup count
+    if (n_wg > ctx->max_wg32) n_wg = ctx->max_wg32;
+  } else {
+    const int blocks_per_wave_cap = 128 * waves;  // block ids held in two registers
+    sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
+                                      : choose_split_blocks(ctx, batch * groups, max_blocks, waves);
+    const int min_sb = (max_blocks + ctx->max_split - 1) / ctx->max_split;  // workspace bound
+    if (sb < min_sb) sb = min_sb;
+    if (sb > blocks_per_wave_cap) sb = blocks_per_wave_cap;
+    if (sb > max_blocks) sb = max_blocks;
+    n_split = (max_blocks + sb - 1) / sb;
+  }
+  ctx->last_split_blocks = t32 ? 0 : sb;
+  ctx->last_n_split = t32 ? n_wg : n_split;
   ctx->last_waves = waves;
 
   hipError_t e;
@@ -312,14 +330,18 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   {
     DecodeArgs da{batch,  kv_cache,       ctx->zero_block, num_blocks,    block_table, block_table_stride,
                   seq_lens, max_seq_len,  q_len,           H,             ctx->qcat,   ctx->part_acc,
-                  ctx->part_ml, sb,       n_split,         n_rt,          batch * n_split * groups};
+                  ctx->part_ml, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
+                  ctx->piece_tbl};
     ProfScope ps(ctx, MLA_K_DECODE, s);
     e = t32 ? launch_decode_mt32(da, t32, s) : launch_decode(ctx->bf16, da, waves, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {
+    // output channels split over 4 workgroups only when the (head, 16 rows) grid is small
+    const int v_parts = int64_t(H) * ((n_q + 15) / 16) >= 2 * ctx->cu_count ? 1 : 4;
     CombineArgs ca{ctx->part_acc, ctx->part_ml, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split,
-                   ctx->W_uv, ctx->W_uvT, out};
+                   ctx->W_uv, ctx->W_uvT, out, t32 ? ctx->piece_tbl : nullptr, 32 * t32,
+                   t32 ? n_rt / t32 : 0, v_parts};
     ProfScope ps(ctx, MLA_K_COMBINE, s);
     e = launch_combine(ctx->bf16, ca, s);
   }

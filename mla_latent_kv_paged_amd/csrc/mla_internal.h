@@ -77,7 +77,8 @@ struct DecodeArgs {
   int32_t split_blocks;
   int32_t n_split;
   int32_t n_rt;           // row tiles per sequence: of 16 rows ((H/16) * q_len), or of 32 for the 32-row kernel
-  int32_t units;          // batch * n_split * n_rt work items
+  int32_t units;          // batch * n_split * n_rt work items; the 32-row kernel: its workgroup count
+  int2* piece_tbl;        // 32-row kernel: per stream (first piece id, piece count), written by workgroup 0
 };
 
 struct CombineArgs {
@@ -93,6 +94,13 @@ struct CombineArgs {
   const void* W_uv;       // [H, DV, DC]
   const void* W_uvT;      // [H, DC, DV]
   void* out;              // [n_q, H, DV]
+  // partials by piece (32-row kernel) instead of by split: row (n, h) of sequence b = n / q_len has
+  // rr = (n % q_len) H + h, stream s = b n_grp + rr / rows_per_piece; piece k of s is partial
+  // (piece_tbl[s].x + k) rows_per_piece + rr % rows_per_piece, k < piece_tbl[s].y
+  const int2* piece_tbl;  // null: by split
+  int32_t rows_per_piece;
+  int32_t n_grp;
+  int32_t v_parts;        // bf16: output channels split over this many workgroups (1 or 4)
 };
 
 // ------------------------------------------------------------------------------ launchers
