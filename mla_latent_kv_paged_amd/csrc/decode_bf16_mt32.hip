@@ -8,7 +8,7 @@
 //    own partial.
 //  * A step covers 32 tokens (two paged blocks).  The workgroup moves the step's 36 KB straight from
 //    HBM into one LDS stage with global_load_lds_dwordx4 (no register staging), NSTAGE - 1 steps
-//    ahead; masked lanes read the library's zero block.
+//    ahead; masked lanes read the library's zero block.  The block ids of a piece are staged in LDS.
 //  * Stage layout: 8 x 8 tiles of 16-byte granules (8 channels).  Chunk K = 9 tg + gq (1 KB) holds
 //    tokens 8tg..8tg+7 x granules 8gq..8gq+7, granule c of token t at slot 8 (c % 8) + t % 8.  Lane
 //    l of a DMA instruction writes slot l and reads token 8tg + l % 8, granule 8gq + l / 8: eight
@@ -39,6 +39,7 @@ typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
 constexpr float kReset = 64.f;    // reference-max headroom (log2 units): P <= 2^64
 constexpr int kChunks = 36;       // 1 KB chunks per stage (72 granules x 32 tokens)
 constexpr int kStageBytes = kChunks * 1024;
+constexpr int kIdCap = 2048;      // block ids of one piece held in LDS (a range is <= kIdCap / 2 steps)
 
 __device__ __forceinline__ f32x16_t mfma32x32(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -82,7 +83,9 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   constexpr int RP = 32 * T;        // rows of a piece (one tile group)
   static_assert(kChunks % T == 0, "chunks split evenly over the waves");
   static_assert(NSTAGE >= 2, "a step is read while a later one is loaded");
+  static_assert(kIdCap >= 2 * kMt32MaxSteps, "a workgroup's block ids fit the LDS table");
   __shared__ __attribute__((aligned(16))) char stage_mem[NSTAGE * kStageBytes];
+  __shared__ int ids_lds[kIdCap];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -187,16 +190,20 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
 #pragma unroll
       for (int k = 0; k < kChunks; ++k) qreg[k] = qsrc[2 * k + h];
     }
-    const int* bt_row = a.block_table + int64_t(b) * a.bt_stride + kb0;
-
-    // block ids of step i through the scalar cache (read only); the second id is clamped into the
-    // piece (its lanes are masked when the step has one block)
+    // the piece's block ids, staged in LDS once (a miss in the table per step would otherwise
+    // stall the barrier that precedes each transfer); nb <= kIdCap by the launch
+    {
+      const int* bt_row = a.block_table + int64_t(b) * a.bt_stride + kb0;
+      for (int e = int(threadIdx.x); e < nb; e += T * 64) ids_lds[e] = bt_row[e];
+    }
+    lds_barrier();
+    // block ids of step i; the second is clamped into the piece (its lanes are masked when the
+    // step has one block)
     auto ids = [&](int i, int& pa, int& pb) {
-      const uint32_t oa = 4u * uint32_t(2 * i), ob = 4u * uint32_t(min(2 * i + 1, nb - 1));
-      asm volatile("s_load_dword %0, %2, %3\n\ts_load_dword %1, %2, %4"
-                   : "=&s"(pa), "=&s"(pb) : "s"(bt_row), "s"(oa), "s"(ob));
+      pa = __builtin_amdgcn_readfirstlane(ids_lds[2 * i]);
+      pb = __builtin_amdgcn_readfirstlane(ids_lds[min(2 * i + 1, nb - 1)]);
     };
-    auto ids_ready = [&](int& pa, int& pb) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(pa), "+s"(pb)); };
+    auto ids_ready = [&](int& pa, int& pb) { (void)pa; (void)pb; };
 
     // DMA of step i into stage i % NSTAGE: wave w takes chunks K = w CPW .. w CPW + CPW - 1 (token
     // groups tg = K / 9); lane l of chunk K reads token 8 tg + l % 8, granule 8 (K % 9) + l / 8

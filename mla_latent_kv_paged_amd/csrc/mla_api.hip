@@ -200,7 +200,13 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
   // partials: by split (rows x max_split) for the one-tile and fp32 kernels; by piece for the
   // 32-row kernel, at most (workgroups + streams) pieces of 32 T rows, i.e. at most
   // 128 * max_wg32 + rows rows (streams of a decode hold rows / (32 T) pieces' worth of rows)
-  c->max_wg32 = 2 * c->cu_count;
+  {
+    // workgroups the 32-row kernel may need: a resident slot each, or enough that no range
+    // exceeds kMt32MaxSteps steps at the caps (every stream at max_seq_len)
+    const int64_t streams = std::max<int64_t>(1, int64_t(cfg->max_q_tokens) * H / 32);
+    const int64_t steps_max = streams * ((max_blocks + 1) / 2);
+    c->max_wg32 = int(std::max<int64_t>(2 * c->cu_count, (steps_max + kMt32MaxSteps - 1) / kMt32MaxSteps));
+  }
   const size_t part_rows = std::max(rows * c->max_split, size_t(128) * c->max_wg32 + rows);
   alloc(reinterpret_cast<void**>(&c->part_acc), part_rows * DC * sizeof(float));
   alloc(reinterpret_cast<void**>(&c->part_ml), part_rows * sizeof(float2));
@@ -301,10 +307,13 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   const int groups = t32 ? n_rt / t32 : n_rt;  // workgroups per (sequence, split)
   int sb = 0, n_split = 0, n_wg = 0;
   if (t32) {
-    // balanced partition over one workgroup per resident slot (T = 4 fills a CU; T <= 2, two)
+    // balanced partition over one workgroup per resident slot (T = 4 fills a CU; T <= 2, two),
+    // and enough workgroups that no range exceeds the block ids one workgroup stages in LDS
     n_wg = ctx->cu_count * (t32 == 4 ? 1 : 2);
     if (ctx->forced_split_blocks > 0) n_wg = ctx->forced_split_blocks;  // tuning: workgroup count
-    if (n_wg > ctx->max_wg32) n_wg = ctx->max_wg32;
+    const int64_t steps_max = int64_t(batch) * groups * ((max_blocks + 1) / 2);
+    n_wg = int(std::max<int64_t>(n_wg, (steps_max + kMt32MaxSteps - 1) / kMt32MaxSteps));
+    if (n_wg > ctx->max_wg32) return MLA_ECAP;
   } else {
     const int blocks_per_wave_cap = 128 * waves;  // block ids held in two registers
     sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
