@@ -126,10 +126,18 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// 16-byte granule as a native vector.  Register arrays of HIP's uint4 struct are copied with memcpy
+// and can be left in private memory; arrays of this type stay in registers.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16].  Lane l holds A row l%16 and B column
 // l%16, with 8 consecutive K values per lane (K block l/16); D column l%16, rows 4(l/16)..+3.
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma32v(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

@@ -7,8 +7,9 @@
 //
 // bf16 storage: a batched MFMA GEMM per head, computed transposed so that each lane stores four
 // consecutive channels: q_lat^T[c, n] = sum_k W_uk^T[c, k] q_nope^T[k, n], K = 128 (4 steps of
-// v_mfma_f32_16x16x32_bf16).  A workgroup owns 64 channels x 64 query rows of one head (each wave
-// 16 channels); operands are read straight from global memory (16 B per lane per step).
+// v_mfma_f32_16x16x32_bf16).  A workgroup owns 64 query rows of one head (each wave 16 rows, their
+// q_nope loaded once) and half of the 512 channels, or less when the grid would otherwise be too
+// small to fill the chip; its W_uk^T slice is staged in LDS with one batch of loads.
 // fp32 storage: one workgroup per (head, 16 query rows) on the vector ALUs, W_uk[h] streamed once
 // per workgroup, each thread owning two latent columns.  Both accumulate in fp32.
 #include "mla_internal.h"
@@ -93,63 +94,126 @@ __global__ __launch_bounds__(256) void q_absorb_kernel(QAbsorbArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a) {
+__global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a, int c_split) {
+  __shared__ u32x4_t wlds[256 * 16];  // up to 256 channels of W_uk^T (64 KiB)
   const int h = blockIdx.x;
-  const int c_blk = blockIdx.y;  // 64 channels
-  const int n_blk = blockIdx.z;  // 64 query rows
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rb = blockIdx.y;  // 64 query rows
+  const int cp = blockIdx.z;  // part of the 512 channels (one of c_split)
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   uint16_t* qcat = static_cast<uint16_t*>(a.qcat);
-  const int c0 = c_blk * 64 + w * 16;
-  // A = W_uk^T rows c0..c0+15 (granule 4*ks + g of the 128-wide row)
-  const uint4* wrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.W_ukT) +
-                                                     (int64_t(h) * DC + c0 + r16) * DN);
-  uint4 af[4];
+  // B operand: q_nope of this wave's 16 rows (granule 4 ks + g of the 128-wide row), loaded once;
+  // rows past n_q read row 0 and are not stored
+  const int n = rb * 64 + 16 * w + r16;
+  const bool nv = n < a.n_q;
+  const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(q + (int64_t(nv ? n : 0) * a.H + h) * QW);
+  u32x4_t bq[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) af[ks] = wrow[4 * ks + g];
-  // all B-operand loads are issued up front and unconditionally (rows past n_q read row 0 and
-  // are not stored), so that the 16 loads of a lane are in flight together
-  uint4 bq[4][4];
+  for (int ks = 0; ks < 4; ++ks) bq[ks] = qrow[4 * ks + g];
+  // RoPE inputs, loaded before the GEMM so that their two dependent round trips overlap it: the
+  // c_split workgroups of this (head, 64 rows) share the rows, each thread taking ppt consecutive
+  // pairs of one row (one context-length load, then contiguous q_pe values and table entries)
+  const int ppt = 8 / c_split;  // pairs per thread (4, 2 or 1)
+  const int tpr = NPAIR / ppt;  // threads per row
+  const int nr = rb * 64 + cp * (64 / c_split) + int(threadIdx.x) / tpr;
+  const int i0 = (int(threadIdx.x) % tpr) * ppt;
+  const bool rv = nr < a.n_q;
+  uint32_t rq[4] = {0u, 0u, 0u, 0u};
+  double2 rc[4] = {};
+  bool rok = false;
+  uint16_t* ro = qcat + (int64_t(rv ? nr : 0) * a.H + h) * ROW + DC + 2 * i0;
+  if (rv) {
+    const int ctx = clamp_ctx(a.seq_lens[nr / a.q_len], a.q_len, a.max_seq_len);
+    const int pos = ctx - a.q_len + nr % a.q_len;
+    rok = pos >= 0 && pos <= a.max_position;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(q + (int64_t(nr) * a.H + h) * QW + DN + 2 * i0);
+    const double2* cs = a.rope + int64_t(rok ? pos : 0) * NPAIR + i0;
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int n = n_blk * 64 + tt * 16 + r16;
-    const uint4* qrow = reinterpret_cast<const uint4*>(q + (int64_t(n < a.n_q ? n : 0) * a.H + h) * QW);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bq[tt][ks] = qrow[4 * ks + g];
-  }
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma32(af[ks], bq[tt][ks], acc);
-    // lane holds query row n (column), channels c0 + 4g .. +3 (rows)
-    const int n = n_blk * 64 + tt * 16 + r16;
-    if (n < a.n_q) {
-      *reinterpret_cast<uint2*>(qcat + (int64_t(n) * a.H + h) * ROW + c0 + 4 * g) =
-          make_uint2(cvt_pk_bf16(acc[0] * a.qscale, acc[1] * a.qscale), cvt_pk_bf16(acc[2] * a.qscale, acc[3] * a.qscale));
+    for (int e = 0; e < 4; ++e) {
+      if (e < ppt) {
+        rq[e] = src[e];
+        rc[e] = cs[e];
+      }
     }
   }
-  // RoPE part: the 8 channel-block workgroups of this (head, 64 rows) each take 8 rows x 32 pairs,
-  // one pair per thread, so that the two dependent loads (context length, rotation table) are paid
-  // once per thread.
-  {
-    const int r = c_blk * 8 + (threadIdx.x >> 5), i = threadIdx.x & 31;
-    const int n = n_blk * 64 + r;
-    if (n < a.n_q) {
-      const uint16_t* src = q + (int64_t(n) * a.H + h) * QW + DN;
-      float y0, y1;
-      rope_q_pair(a, n, h, i, bf16_to_f32(src[2 * i]), bf16_to_f32(src[2 * i + 1]), &y0, &y1);
-      uint16_t* o = qcat + (int64_t(n) * a.H + h) * ROW + DC;
-      *reinterpret_cast<uint32_t*>(o + 2 * i) = cvt_pk_bf16(y0, y1);
+  // A operand: this workgroup's W_uk^T rows (NC channels x 16 granules).  64 channels go straight
+  // into registers; more are staged in LDS with one batch of loads, granule gi of row r at
+  // r*16 + (gi ^ (r % 16)), so that the 16 rows of a tile read at one granule column hit distinct
+  // bank groups
+  const int NC = DC / c_split;  // <= 256
+  const int ntile = NC / 16;
+  const int c_first = cp * NC;
+  uint16_t* orow = qcat + (int64_t(nv ? n : 0) * a.H + h) * ROW + c_first + 4 * g;
+  if (c_split == 8) {
+    // 64 channels: each wave's four tiles straight from global memory, all loads in flight together
+    // (a small grid is latency-bound; staging through LDS would add a round trip)
+    const u32x4_t* wt = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.W_ukT) +
+                                                       (int64_t(h) * DC + c_first + r16) * DN);
+    u32x4_t af[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) af[t][ks] = wt[t * 16 * (DN / 8) + 4 * ks + g];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma32v(af[t][ks], bq[ks], acc);
+      if (nv)
+        *reinterpret_cast<uint2*>(orow + 16 * t) =
+            make_uint2(cvt_pk_bf16(acc[0] * a.qscale, acc[1] * a.qscale), cvt_pk_bf16(acc[2] * a.qscale, acc[3] * a.qscale));
+    }
+  } else {
+    {
+      const u32x4_t* wsrc = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.W_ukT) +
+                                                           (int64_t(h) * DC + c_first) * DN);
+      const int cnt = NC * 16 / 256;  // granules per thread (16 or 8)
+      u32x4_t tmp[16];  // native vectors: plain loads and stores, the array stays in registers
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < cnt) tmp[k] = wsrc[threadIdx.x + 256 * k];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < cnt) {
+          const int e = threadIdx.x + 256 * k, r = e >> 4, gi = e & 15;
+          wlds[r * 16 + (gi ^ (r & 15))] = tmp[k];
+        }
+    }
+    __syncthreads();
+    for (int t = 0; t < ntile; ++t) {
+      const int r = 16 * t + r16;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma32v(wlds[r * 16 + ((4 * ks + g) ^ r16)], bq[ks], acc);
+      // lane holds query row n (column), channels c_first + 16 t + 4g .. +3 (rows)
+      if (nv)
+        *reinterpret_cast<uint2*>(orow + 16 * t) =
+            make_uint2(cvt_pk_bf16(acc[0] * a.qscale, acc[1] * a.qscale), cvt_pk_bf16(acc[2] * a.qscale, acc[3] * a.qscale));
+    }
+  }
+  // RoPE part: results computed and stored after the GEMM from the values loaded above
+  if (rv) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (e < ppt) {
+        const double x0 = bf16_to_f32(rq[e] & 0xffffu), x1 = bf16_to_f32(rq[e] >> 16);
+        const float y0 = rok ? float((x0 * rc[e].x - x1 * rc[e].y) * double(a.qscale)) : __builtin_nanf("");
+        const float y1 = rok ? float((x0 * rc[e].y + x1 * rc[e].x) * double(a.qscale)) : __builtin_nanf("");
+        *reinterpret_cast<uint32_t*>(ro + 2 * e) = cvt_pk_bf16(y0, y1);
+      }
     }
   }
 }
 
 hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s) {
   if (bf16) {
-    dim3 grid(a.H, DC / 64, (a.n_q + 63) / 64);
-    q_absorb_bf16_kernel<<<grid, 256, 0, s>>>(a);
+    // channels split over c_split workgroups only as far as needed for about 512 workgroups
+    const int rbs = (a.n_q + 63) / 64;
+    int c_split = 2;  // at most 256 channels per workgroup (its W_uk^T slice fits 64 KiB of LDS)
+    while (c_split < 8 && int64_t(a.H) * rbs * c_split < 512) c_split *= 2;
+    dim3 grid(a.H, rbs, c_split);
+    q_absorb_bf16_kernel<<<grid, 256, 0, s>>>(a, c_split);
   } else {
     dim3 grid(a.H, (a.n_q + 15) / 16);
     q_absorb_kernel<float><<<grid, 256, 0, s>>>(a);
