@@ -33,8 +33,11 @@ METRIC = "MLA decode µs/step + achieved latent-cache GB/s, V2-Lite b=64 s=4096"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "decode_bf16_lite_b64_s4096_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_paged_amd", "csrc", "decode_bf16.hip")
+CSRC = os.path.join(ROOT, "mla_latent_kv_paged_amd", "csrc")
+# committed rocprofv3 FETCH/WRITE summaries per default workload, and the kernel source they were taken on
+TRAFFIC = {"lite_b64": ("decode_bf16_lite_b64_s4096_traffic.json", "decode_bf16.hip"),
+           "wide": ("decode_bf16_mt32_wide_h128_b128_traffic.json", "decode_bf16_mt32.hip"),
+           "ragged": ("decode_bf16_mt32_ragged_b256_q4_traffic.json", "decode_bf16_mt32.hip")}
 
 
 def parse():
@@ -50,7 +53,8 @@ def parse():
     ap.add_argument("--split-blocks", type=int, default=0, help="force the split size (0 = library choice)")
     ap.add_argument("--waves", type=int, default=0, help="force waves per decode workgroup (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=32, help="sequences in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="sequences in the oracle's timed sample (capped at "
+                    "the batch)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only"],
                     help="copy-calibration: run a plain 256 MiB device copy (for counter scaling); "
                          "decode-only: run just the decode loop (for profilers)")
@@ -94,14 +98,18 @@ def copy_calibration():
                       "copies": 5}), flush=True)
 
 
-def traffic_entry():
-    """HBM traffic of the decode kernel from committed rocprofv3 --pmc summaries, if they were
-    taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_entry(args):
+    """HBM traffic of the decode kernel from the committed rocprofv3 --pmc summary of this workload
+    (default sizes only), if it was taken on the current kernel source; else None."""
+    if args.workload not in TRAFFIC or args.seq_len or args.batch:
+        return None
+    fname, src = TRAFFIC[args.workload]
+    path = os.path.join(PROFILES, fname)
+    if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-        sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
         if rec.get("kernel_source_sha256") != sha:
             return None
         return rec.get("traffic_bytes_per_launch")
@@ -135,8 +143,10 @@ def cpu_baseline(w, n_seq):
         pool = O.cache_write(np.full((nb, 16, 1, 576), np.nan), c[:hist], k[:hist], np.arange(hist),
                              np.arange(hist), gamma, w.eps, w.theta, w.storage)
         prepared.append((b, ctx, nb, c[hist:], k[hist:], pool))
+    # repeat the sampled step until about 10 s of CPU work has been timed (at least 3 runs, at most
+    # 30 s), and report the median run
     times = []
-    for _ in range(3):
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 200):
         t0 = time.perf_counter()
         for b, ctx, nb, cn, kn, pool in prepared:
             cache = O.cache_write(pool, cn, kn, np.arange(ctx - w.q_len, ctx), np.arange(ctx - w.q_len, ctx),
@@ -144,7 +154,7 @@ def cpu_baseline(w, n_seq):
             O.decode_absorbed(qall[b * w.q_len:(b + 1) * w.q_len], cache, np.arange(nb)[None, :],
                               np.array([ctx]), w.q_len, W_uk, W_uv, w.scale, w.theta)
         times.append(time.perf_counter() - t0)
-        if times[-1] > 30:
+        if sum(times) > 30:
             break
     t = float(np.median(times))
     blas_threads = cores
@@ -159,8 +169,8 @@ def cpu_baseline(w, n_seq):
     return {"value": bytes_sample / t / 1e9, "unit": "GB/s", "cores": int(min(cores, blas_threads)),
             "kind": "oracle",
             "sample": f"{len(seqs)} of {w.batch} sequences (full context each); one step = cache write of the "
-                      f"new token(s) + absorbed fp64 decode; median of {len(times)} runs, {t:.3f} s per run; "
-                      f"host threads available {cores}",
+                      f"new token(s) + absorbed fp64 decode; median of {len(times)} runs ({sum(times):.1f} s of "
+                      f"CPU work), {t:.3f} s per run; host threads available {cores}",
             "seconds_per_sample_step": t}
 
 
@@ -259,10 +269,12 @@ def main():
     decode_us = kern["decode"]["avg_us"]
     flops_attn = w.total_ctx * w.num_heads * w.q_len * 2 * (576 + 512)
     achieved = latent_bytes / (decode_us * 1e-6) / 1e9
-    traffic = traffic_entry()
+    traffic = traffic_entry(args)
+    rows32 = (w.num_heads * w.q_len) % 32 == 0
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "decode_bf16_kernel" if w.storage == "bf16" else "decode_f32_kernel",
+                "kernel": ("decode_bf16_mt32_kernel" if rows32 else "decode_bf16_kernel") if w.storage == "bf16"
+                else "decode_f32_kernel",
                 "algorithmic_bytes_per_launch": latent_bytes,
                 "mfma_tflops": round(flops_attn / (decode_us * 1e-6) / 1e12, 2)}
     step_us = ms_per_step * 1e3
