@@ -30,10 +30,7 @@ namespace mla {
 namespace {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) char lds_char_t;
-typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
 
 constexpr float kReset = 64.f;    // reference-max headroom (log2 units): P <= 2^64
 constexpr int kChunks = 36;       // 1 KB chunks per stage (72 granules x 32 tokens)
@@ -55,24 +52,6 @@ __device__ __forceinline__ void mfma32x32_acc(f32x16_t& acc, u32x4_t a, u32x4_t 
 }
 // wait states after the last asm MFMA before VALU reads its accumulator (> 18 for 16 passes)
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
-// One 16-byte global -> LDS transfer per lane: lane l's data lands at lds + 16 l.  Issued from asm
-// so that the compiler does not track it (it would wait for every transfer in flight before the
-// next LDS read); the kernel orders it itself with wait_vmcnt and the barrier.  Loads complete in
-// issue order, so the compiler's own vmcnt waits for older loads stay correct.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-
-// s_waitcnt for vector memory only: vmcnt(n), lgkmcnt and expcnt left at their maxima
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (15 << 8) | (7 << 4) | (N & 15));
-}
-
-// Workgroup barrier ordering LDS only (the wave's own LDS accesses are complete when it arrives).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace
 

@@ -365,7 +365,7 @@ void mla_free(mla_ctx* ctx) {
 
 mla_status mla_set_decode_tuning(mla_ctx* ctx, int32_t split_blocks, int32_t waves_per_group) {
   if (!ctx || split_blocks < 0) return MLA_EINVAL;
-  if (waves_per_group != 0 && waves_per_group != 2 && waves_per_group != 4)
+  if (waves_per_group != 0 && waves_per_group != 2)
     return MLA_EINVAL;
   ctx->forced_split_blocks = split_blocks;
   ctx->forced_waves = waves_per_group;

@@ -171,4 +171,29 @@ __device__ __forceinline__ int clamp_ctx(int v, int q_len, int max_seq_len) {
   return v < q_len ? q_len : (v > max_seq_len ? max_seq_len : v);
 }
 
+// ------------------------------------------------------------------------------ HBM -> LDS transfers
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4): lane l's data lands at
+// lds + 16 l.  Issued from asm so that the compiler does not track it (it would wait for every
+// transfer in flight before the next LDS read); the kernels order it themselves with wait_vmcnt
+// (and a barrier when another wave reads the data).  Vector-memory loads complete in issue order,
+// so the compiler's own vmcnt waits for older loads stay correct.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt for vector memory only: vmcnt(n), lgkmcnt and expcnt left at their maxima
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (15 << 8) | (7 << 4) | (N & 15));
+}
+
+// Workgroup barrier ordering LDS only (the wave's own LDS accesses are complete when it arrives).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace mla
