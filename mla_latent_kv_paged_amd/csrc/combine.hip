@@ -4,6 +4,8 @@
 // result is the log-sum-exp merge
 //   o_lat = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,   M = max_j m_j,
 // and then out[n, h, :] = o_lat . W_uv[h]^T.  Splits are merged in index order: deterministic.
+// The fp32 path keeps acc_j; the bf16 kernels store o_j = acc_j / l_j in fp16, merged with the
+// weights 2^(m_j - M) l_j.  A split with m_j = -inf saw no token and weighs nothing.
 //
 // One workgroup per (head, 16 query rows); merged o_lat rows are staged in LDS.
 // bf16 storage: the projection is a batched MFMA GEMM computed transposed,
@@ -12,7 +14,7 @@
 // i.e. about 16 significant bits, so the product loses nothing visible to the output rounding.
 // A workgroup owns 16 rows and either all 128 output channels (four waves, 32 each) or, when the
 // (head, 16 rows) grid alone would leave CUs idle, a quarter of them (two waves, 16 each); W_uv
-// rows are read straight from global memory.
+// rows are read straight from global memory, issued before the partials (they depend on nothing).
 // fp32 storage: the same merge, then W_uv on the vector ALUs.  Both accumulate in fp32.
 #include "mla_internal.h"
 
@@ -95,9 +97,12 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   const int vbase = a.v_parts == 1 ? 32 * w : vq * 32 + (w & 1) * 16;
   const uint16_t* wuv_h = static_cast<const uint16_t*>(a.W_uv) + int64_t(h) * DV * DC;
   const uint4* wrow = reinterpret_cast<const uint4*>(wuv_h + int64_t(vbase + (lane & 15)) * DC);
+  const bool gemm_wave = a.v_parts == 1 || w < 2;
   uint4 wf[16];
+  if (gemm_wave) {
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) wf[ks] = wrow[4 * ks + (lane >> 4)];
+    for (int ks = 0; ks < 16; ++ks) wf[ks] = wrow[4 * ks + (lane >> 4)];
+  }
 
   // merge the partials: wave w owns rows 4w..4w+3, lane owns channels 8*lane..8*lane+7.  Row rr's
   // partials are base[rr] + j * stride[rr], j < ns[rr] (by split: consecutive slots; by piece:
@@ -124,21 +129,15 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
       ns[rr] = (r0 + w * 4 + rr < a.n_q) ? pt[rr].y : 0;
     }
   } else {
-    int sl[4];
+    // every split is read (an empty one carries m = -inf and is skipped by selection), so the
+    // loads do not wait for the context length
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int row = r0 + w * 4 + rr;
       const int rowc = row < a.n_q ? row : a.n_q - 1;
       base[rr] = (int64_t(rowc) * a.H + h) * a.n_split;
-      sl[rr] = a.seq_lens[rowc / a.q_len];
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int ctx = clamp_ctx(sl[rr], a.q_len, a.max_seq_len);
-      const int nblk = (ctx + BLK - 1) / BLK;
-      const int n = (nblk + a.split_blocks - 1) / a.split_blocks;
       stride[rr] = 1;
-      ns[rr] = (r0 + w * 4 + rr < a.n_q) ? (n < a.n_split ? n : a.n_split) : 0;
+      ns[rr] = row < a.n_q ? a.n_split : 0;
     }
   }
   const int ns_max = __builtin_amdgcn_readfirstlane(max(max(ns[0], ns[1]), max(ns[2], ns[3])));
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   }
   for (int j0 = 0; j0 < ns_max; j0 += 4) {
     float2 ml[4][4];
-    float4 va[4][4], vb[4][4];
+    u32x4_t vo[4][4];  // fp16 o of channels 8 lane .. 8 lane + 7
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
@@ -160,9 +159,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
         const int jc = min(j0 + jj, max(ns[rr] - 1, 0));
         const int64_t pi = base[rr] + int64_t(jc) * stride[rr];
         ml[rr][jj] = a.part_ml[pi];
-        const float4* src = reinterpret_cast<const float4*>(a.part_acc + pi * DC + 8 * lane);
-        va[rr][jj] = src[0];
-        vb[rr][jj] = src[1];
+        vo[rr][jj] = *reinterpret_cast<const u32x4_t*>(a.part_o16 + pi * DC + 8 * lane);
       }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -181,19 +178,22 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         if (!ok[jj]) continue;
-        const float wgt = __builtin_amdgcn_exp2f(ml[rr][jj].x - mc);
-        den[rr] = fmaf(wgt, ml[rr][jj].y, den[rr]);
-        o[rr][0] = fmaf(wgt, va[rr][jj].x, o[rr][0]); o[rr][1] = fmaf(wgt, va[rr][jj].y, o[rr][1]);
-        o[rr][2] = fmaf(wgt, va[rr][jj].z, o[rr][2]); o[rr][3] = fmaf(wgt, va[rr][jj].w, o[rr][3]);
-        o[rr][4] = fmaf(wgt, vb[rr][jj].x, o[rr][4]); o[rr][5] = fmaf(wgt, vb[rr][jj].y, o[rr][5]);
-        o[rr][6] = fmaf(wgt, vb[rr][jj].z, o[rr][6]); o[rr][7] = fmaf(wgt, vb[rr][jj].w, o[rr][7]);
+        // weight of split j: 2^(m_j - M) l_j (its o is already divided by l_j)
+        const float wgt = __builtin_amdgcn_exp2f(ml[rr][jj].x - mc) * ml[rr][jj].y;
+        den[rr] += wgt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2_t x = f16x2_to_f32(vo[rr][jj][e]);
+          o[rr][2 * e] = fmaf(wgt, x[0], o[rr][2 * e]);
+          o[rr][2 * e + 1] = fmaf(wgt, x[1], o[rr][2 * e + 1]);
+        }
       }
     }
   }
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int r = w * 4 + rr;
-    const float inv = ns[rr] > 0 ? 1.f / den[rr] : 0.f;
+    const float inv = den[rr] > 0.f ? 1.f / den[rr] : 0.f;
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

@@ -8,7 +8,8 @@
 //   s[r,t]  = [q_lat | q_pe'][r] . [c_t | k_pe_t]    (query pre-scaled by scale*log2 e)
 //   masked for t > p (causal) and t >= ctx
 //   m, l, acc[r, 0:512] = online-softmax state of sum_t 2^(s[r,t]-m) c_t
-// and one (m, l, acc) partial per (row, split) is written for the combine pass.
+// and one partial per (row, split) is written for the combine pass: (m, l) and o = acc / l in
+// fp16 (a convex combination of cache values: |o| <= max |c|).
 //
 // How (gfx950 specifics):
 //  * A paged block is 16 tokens x 576 bf16 = 18,432 contiguous bytes.  Each wave streams its
@@ -125,7 +126,10 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 
   const int nblk = (ctx + BLK - 1) / BLK;
   const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
-  if (j >= ns) {  // a split past a short context: nothing to do once the query transfer has landed
+  if (j >= ns) {  // a split past a short context: marked empty for the combine (which reads every
+                  // split without the context length), after the query transfer has landed
+    if (w == 0 && lane < 16)
+      a.part_ml[(int64_t(row) * a.H + h0 + lane) * a.n_split + j] = make_float2(-INFINITY, 0.f);
     wait_vmcnt<0>();
     return;
   }
@@ -299,16 +303,21 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
     for (int t = 0; t < 16; ++t) slots[t * 64 + lane] = acc[t];
   }
   __syncthreads();
+  // the partial is stored normalised, o = acc / l, in fp16 (a convex combination of cache values)
   const int64_t pidx = (int64_t(row) * a.H + h0 + r16) * a.n_split + j;
-  float* dst = a.part_acc + pidx * DC + 4 * g;
+  uint16_t* dst = a.part_o16 + pidx * DC + 4 * g;
+  const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+  auto put = [&](int jj, f32x4_t v) {
+    v *= inv;
+    *reinterpret_cast<uint2*>(dst + 16 * jj) = make_uint2(cvt_pk_f16(v[0], v[1]), cvt_pk_f16(v[2], v[3]));
+  };
   // fixed order for every tile: wave 0's term first
   if (w == 0) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4_t*>(dst + 16 * t) = acc[t] + slots[t * 64 + lane];
+    for (int t = 0; t < 16; ++t) put(t, acc[t] + slots[t * 64 + lane]);
   } else {
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      *reinterpret_cast<f32x4_t*>(dst + 16 * (16 + t)) = slots[(16 + t) * 64 + lane] + acc[16 + t];
+    for (int t = 0; t < 16; ++t) put(16 + t, slots[(16 + t) * 64 + lane] + acc[16 + t]);
   }
   if (w == 0 && g == 0) a.part_ml[pidx] = make_float2(M, Ltot);
 }

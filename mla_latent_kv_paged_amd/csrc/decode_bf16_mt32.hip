@@ -361,18 +361,21 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       step(i, sv);
     }
 
-    // partial of this wave's rows: channel 32jt + 8q + 4h + e sits in acc[jt][4q + e]
+    // partial of this wave's rows: channel 32jt + 8q + 4h + e sits in acc[jt][4q + e]; stored
+    // normalised, o = acc / l, in fp16 (a convex combination of cache values)
     mfma_drain();
     lsum += __shfl_xor(lsum, 32, 64);
     const int64_t pidx = int64_t(pid) * RP + w * 32 + r32;
-    float* dst = a.part_acc + pidx * DC;
+    uint16_t* dst = a.part_o16 + pidx * DC;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int jt = 0; jt < 16; ++jt) {
       f32x16_t v = acc[jt];
       asm volatile("" : "+v"(v));  // one tile at a time out of the AGPRs
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4_t*>(dst + 32 * jt + 8 * q + 4 * h) = f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        *reinterpret_cast<uint2*>(dst + 32 * jt + 8 * q + 4 * h) =
+            make_uint2(cvt_pk_f16(v[4 * q] * inv, v[4 * q + 1] * inv), cvt_pk_f16(v[4 * q + 2] * inv, v[4 * q + 3] * inv));
     }
     if (h == 0) a.part_ml[pidx] = make_float2(m, lsum);
     lds_barrier();  // every wave is done with the stages before the next piece refills them

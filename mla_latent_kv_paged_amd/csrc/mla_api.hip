@@ -339,7 +339,7 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   {
     DecodeArgs da{batch,  kv_cache,       ctx->zero_block, num_blocks,    block_table, block_table_stride,
                   seq_lens, max_seq_len,  q_len,           H,             ctx->qcat,   ctx->part_acc,
-                  ctx->part_ml, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
+                  reinterpret_cast<uint16_t*>(ctx->part_acc), ctx->part_ml, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
                   ctx->piece_tbl};
     ProfScope ps(ctx, MLA_K_DECODE, s);
     e = t32 ? launch_decode_mt32(da, t32, s) : launch_decode(ctx->bf16, da, waves, s);
@@ -348,7 +348,7 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   {
     // output channels split over 4 workgroups only when the (head, 16 rows) grid is small
     const int v_parts = int64_t(H) * ((n_q + 15) / 16) >= 2 * ctx->cu_count ? 1 : 4;
-    CombineArgs ca{ctx->part_acc, ctx->part_ml, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split,
+    CombineArgs ca{ctx->part_acc, reinterpret_cast<const uint16_t*>(ctx->part_acc), ctx->part_ml, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split,
                    ctx->W_uv, ctx->W_uvT, out, t32 ? ctx->piece_tbl : nullptr, 32 * t32,
                    t32 ? n_rt / t32 : 0, v_parts};
     ProfScope ps(ctx, MLA_K_COMBINE, s);

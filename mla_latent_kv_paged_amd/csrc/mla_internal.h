@@ -72,8 +72,9 @@ struct DecodeArgs {
   int32_t q_len;
   int32_t H;
   const void* qcat;
-  float* part_acc;        // [n_q*H*n_split, DC]
-  float2* part_ml;        // [n_q*H*n_split] (running max in log2 units, sum)
+  float* part_acc;        // fp32 kernel: [n_q*H*n_split, DC] unnormalised accumulators
+  uint16_t* part_o16;     // bf16 kernels (same memory): [rows, DC] fp16 o = acc / l (0 when l = 0)
+  float2* part_ml;        // [rows] (running max in log2 units, sum); (-inf, 0): nothing visible
   int32_t split_blocks;
   int32_t n_split;
   int32_t n_rt;           // row tiles per sequence: of 16 rows ((H/16) * q_len), or of 32 for the 32-row kernel
@@ -82,7 +83,8 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-  const float* part_acc;
+  const float* part_acc;  // fp32 path
+  const uint16_t* part_o16;  // bf16 path: fp16 normalised partials (acc / l)
   const float2* part_ml;
   const int32_t* seq_lens;
   int32_t max_seq_len;
@@ -155,6 +157,15 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
+// Two floats -> packed fp16 pair (low half = lo), round to nearest even.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), f16x2_t));
+}
+__device__ __forceinline__ f32x2_t f16x2_to_f32(uint32_t v) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, v), f32x2_t);
 }
 
 // double -> bf16 with a single rounding (nearest even): round to odd at fp32 precision first
