@@ -67,7 +67,7 @@ template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   static_assert(NW == 2, "the query tile is moved by two waves");
   static_assert(NS >= 2 && NS <= 4, "a wave keeps at most 3 blocks in flight (vmcnt range)");
-  static_assert(NW * NS * kBlockBytes >= 32 * 64 * 16, "the merge reuses the rings");
+  static_assert(NW * NS * kBlockBytes >= 32 * 64 * 16 + 16 * 1024, "the merge reuses the rings");
   __shared__ __attribute__((aligned(16))) char ring_mem[NW * NS * kBlockBytes];
   __shared__ __attribute__((aligned(16))) char q_mem[kBlockBytes];
   __shared__ float m_lds[NW][16];
@@ -303,13 +303,16 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
     for (int t = 0; t < 16; ++t) slots[t * 64 + lane] = acc[t];
   }
   __syncthreads();
-  // the partial is stored normalised, o = acc / l, in fp16 (a convex combination of cache values)
-  const int64_t pidx = (int64_t(row) * a.H + h0 + r16) * a.n_split + j;
-  uint16_t* dst = a.part_o16 + pidx * DC + 4 * g;
+  // The partial is stored normalised, o = acc / l, in fp16 (a convex combination of cache
+  // values), through an LDS tile (16 rows x 1 KB after the exchange slots; granule G of row r at
+  // slot G ^ r) so that each store instruction writes one whole 1 KB row.
   const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
-  auto put = [&](int jj, f32x4_t v) {
+  lds_char_t* const otile = (lds_char_t*)ring_mem + 32 * 64 * 16;
+  auto put = [&](int jj, f32x4_t v) {  // channels 16 jj + 4 g .. + 3 of row r16: granule 2 jj + g / 2
     v *= inv;
-    *reinterpret_cast<uint2*>(dst + 16 * jj) = make_uint2(cvt_pk_f16(v[0], v[1]), cvt_pk_f16(v[2], v[3]));
+    const int G = 2 * jj + (g >> 1);
+    *(lds_u32x2_t*)(otile + r16 * 1024 + 16 * (G ^ r16) + 8 * (g & 1)) =
+        u32x2_t{cvt_pk_f16(v[0], v[1]), cvt_pk_f16(v[2], v[3])};
   };
   // fixed order for every tile: wave 0's term first
   if (w == 0) {
@@ -318,6 +321,14 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   } else {
 #pragma unroll
     for (int t = 0; t < 16; ++t) put(16 + t, slots[(16 + t) * 64 + lane] + acc[16 + t]);
+  }
+  __syncthreads();
+  const int64_t pidx = (int64_t(row) * a.H + h0 + r16) * a.n_split + j;  // this lane's row (r16)
+#pragma unroll
+  for (int r = 8 * w; r < 8 * w + 8; ++r) {  // wave w stores rows 8w..8w+7
+    const int64_t pr = (int64_t(row) * a.H + h0 + r) * a.n_split + j;
+    *reinterpret_cast<u32x4_t*>(a.part_o16 + pr * DC + 8 * lane) =
+        *(const lds_u32x4_t*)(otile + r * 1024 + 16 * (lane ^ r));
   }
   if (w == 0 && g == 0) a.part_ml[pidx] = make_float2(M, Ltot);
 }

@@ -61,6 +61,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   constexpr int RP = 32 * T;        // rows of a piece (one tile group)
   static_assert(kChunks % T == 0, "chunks split evenly over the waves");
   static_assert(NSTAGE >= 2, "a step is read while a later one is loaded");
+  static_assert(T * 32 * 1024 <= NSTAGE * kStageBytes, "the partial tiles fit the stages");
   static_assert(kIdCap >= 2 * kMt32MaxSteps, "a workgroup's block ids fit the LDS table");
   __shared__ __attribute__((aligned(16))) char stage_mem[NSTAGE * kStageBytes];
   __shared__ int ids_lds[kIdCap];
@@ -181,14 +182,18 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       pa = __builtin_amdgcn_readfirstlane(ids_lds[2 * i]);
       pb = __builtin_amdgcn_readfirstlane(ids_lds[min(2 * i + 1, nb - 1)]);
     };
-    auto ids_ready = [&](int& pa, int& pb) { (void)pa; (void)pb; };
 
     // DMA of step i into stage i % NSTAGE: wave w takes chunks K = w CPW .. w CPW + CPW - 1 (token
-    // groups tg = K / 9); lane l of chunk K reads token 8 tg + l % 8, granule 8 (K % 9) + l / 8
-    auto issue = [&](int i, int pa, int pb) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes + w * CPW * 1024)));
-      constexpr int NTG = (CPW + 8) / 9;  // token groups this wave touches (CPW is 9, 18 or 36)
+    // groups tg = K / 9); lane l of chunk K reads token 8 tg + l % 8, granule 8 (K % 9) + l / 8.
+    // prep() computes the wave's source rows for step i, put(c) issues its chunk w CPW + c.
+    constexpr int NTG = (CPW + 8) / 9;  // token groups this wave touches (CPW is 9, 18 or 36)
+    struct Xfer {
+      const char* src[NTG];
+      uint32_t dst;
+    };
+    auto prep = [&](int i, int pa, int pb) {
+      Xfer x;
+      x.dst = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes + w * CPW * 1024)));
 #pragma unroll
       for (int gi = 0; gi < NTG; ++gi) {
         const int tg = (w * CPW) / 9 + gi;     // token group of the step (uniform)
@@ -196,10 +201,15 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
         const int trow = 8 * (tg & 1) + lrow;   // token row within the block
         const int phys = (tg >> 1) ? pb : pa;
         const bool ok = bi < nb && unsigned(phys) < unsigned(a.num_blocks) && (kb0 + bi) * BLK + trow < ctx;
-        const char* src = (ok ? cache + (int64_t(phys) * BLK + trow) * (ROW * 2) : zero + trow * (ROW * 2)) + 16 * lgr;
-#pragma unroll
-        for (int gq = 0; gq < 9; ++gq) dma16(src + 128 * gq, dst + 1024 * (9 * gi + gq));
+        x.src[gi] = (ok ? cache + (int64_t(phys) * BLK + trow) * (ROW * 2) : zero + trow * (ROW * 2)) + 16 * lgr;
       }
+      return x;
+    };
+    auto put = [&](const Xfer& x, int c) { dma16(x.src[c / 9] + 128 * (c % 9), x.dst + 1024 * c); };
+    auto issue = [&](int i, int pa, int pb) {
+      const Xfer x = prep(i, pa, pb);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) put(x, c);
     };
 
     f32x16_t acc[16];
@@ -223,7 +233,11 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
 
     // scores of step i: S^T on v_mfma_f32_32x32x16_bf16, operand reads kept D ahead of the MFMAs;
     // masked only when the step reaches a row's limit (a uniform test)
-    auto scores = [&](int i, float (&sv)[16]) {
+    // When a transfer x is given, its CPW chunks are issued among the MFMAs (one after MFMA
+    // SP c + 1 for chunk c), so that a transfer held back by the memory pipeline stalls the wave
+    // between matrix instructions instead of in one block before them.
+    constexpr int SP = kChunks / CPW;
+    auto scores = [&](int i, float (&sv)[16], const Xfer* x) {
       uint32_t spa = stage_addr(i) + uint32_t(sc_off);
       asm volatile("" : "+v"(spa));  // one base per step: the 36 offsets fold into the reads
       lds_u32x4_t* sp = (lds_u32x4_t*)uintptr_t(spa);
@@ -234,17 +248,20 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       for (int k = 0; k < D; ++k) ring[k] = sp[16 * k];
 #pragma unroll
       for (int k = 0; k < kChunks; ++k) {
-        const u32x4_t x = ring[k % D];
+        const u32x4_t xr = ring[k % D];
         if (k + D < kChunks) ring[k % D] = sp[16 * (k + D)];
-        sc = mfma32x32(x, qreg[k], sc);
+        sc = mfma32x32(xr, qreg[k], sc);
+        if (x && k % SP == SP / 2) put(*x, k / SP);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+      if (!x) {
+        __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
 #pragma unroll
-      for (int k = 0; k < kChunks - D; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int k = 0; k < kChunks - D; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = sc[r];
       const int tok0 = (kb0 + 2 * i) * BLK;
@@ -335,49 +352,66 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       if (i < steps) {
         int pa, pb;
         ids(i, pa, pb);
-        ids_ready(pa, pb);
         issue(i, pa, pb);
       }
     }
     float sv[16];
-    for (int i = 0; i < steps; ++i) {
-      // ids of the step to load next, fetched under the wait below
-      const int inext = i + NSTAGE - 1;
-      int pa = 0, pb = 0;
-      if (inext < steps) ids(inext, pa, pb);
-      // step i's chunks have landed for this wave (newer steps' transfers may stay in flight),
-      // then for every wave; the barrier also retires the stage read at step i - 1, which then
-      // takes step i + NSTAGE - 1
+    // steady state: step i's chunks have landed for this wave (newer steps' transfers may stay in
+    // flight), then for every wave; the barrier also retires the stage read at step i - 1, which
+    // then takes step i + NSTAGE - 1, issued among the score MFMAs of step i
+    int i = 0;
+    for (; i + NSTAGE - 1 < steps; ++i) {
+      int pa, pb;
+      ids(i + NSTAGE - 1, pa, pb);
+      wait_vmcnt<(NSTAGE - 2) * CPW>();
+      lds_barrier();
+      const Xfer x = prep(i + NSTAGE - 1, pa, pb);
+      scores(i, sv, &x);
+      step(i, sv);
+    }
+    // the last NSTAGE - 1 steps: nothing left to load
+    for (; i < steps; ++i) {
       if (i + NSTAGE - 2 < steps)
         wait_vmcnt<(NSTAGE - 2) * CPW>();
       else
         wait_vmcnt<0>();
       lds_barrier();
-      if (inext < steps) {
-        ids_ready(pa, pb);
-        issue(inext, pa, pb);
-      }
-      scores(i, sv);
+      scores(i, sv, nullptr);
       step(i, sv);
     }
 
     // partial of this wave's rows: channel 32jt + 8q + 4h + e sits in acc[jt][4q + e]; stored
-    // normalised, o = acc / l, in fp16 (a convex combination of cache values)
+    // normalised, o = acc / l, in fp16 (a convex combination of cache values).  It goes through
+    // the (then idle) stages so that each store instruction writes one whole 1 KB row: written
+    // straight from the accumulator layout, a store touches 32 rows with 16 bytes each.  Tile of
+    // wave w: 32 rows x 1 KB at w * 32 KB, granule G of row r at slot G ^ r.
     mfma_drain();
     lsum += __shfl_xor(lsum, 32, 64);
-    const int64_t pidx = int64_t(pid) * RP + w * 32 + r32;
-    uint16_t* dst = a.part_o16 + pidx * DC;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    lds_barrier();  // every wave is done with the last step's stage
+    // (the swizzle keys are opaque here so that the 96 addresses are formed at their use, not
+    // hoisted out of the piece loop and spilled)
+    uint32_t wbase = uint32_t(uintptr_t(stages + w * (32 * 1024))) + r32 * 1024 + 8 * h, wkey = r32;
+    uint32_t rbase = uint32_t(uintptr_t(stages + w * (32 * 1024))), rkey = lane;
+    asm volatile("" : "+v"(wbase), "+v"(wkey), "+v"(rbase), "+v"(rkey));
 #pragma unroll
     for (int jt = 0; jt < 16; ++jt) {
       f32x16_t v = acc[jt];
       asm volatile("" : "+v"(v));  // one tile at a time out of the AGPRs
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2*>(dst + 32 * jt + 8 * q + 4 * h) =
-            make_uint2(cvt_pk_f16(v[4 * q] * inv, v[4 * q + 1] * inv), cvt_pk_f16(v[4 * q + 2] * inv, v[4 * q + 3] * inv));
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t G = 4 * jt + q;
+        *(lds_u32x2_t*)uintptr_t(wbase + 16 * (G ^ wkey)) =
+            u32x2_t{cvt_pk_f16(v[4 * q] * inv, v[4 * q + 1] * inv), cvt_pk_f16(v[4 * q + 2] * inv, v[4 * q + 3] * inv)};
+      }
     }
-    if (h == 0) a.part_ml[pidx] = make_float2(m, lsum);
+    const int64_t pidx = int64_t(pid) * RP + w * 32;
+    uint16_t* dst = a.part_o16 + pidx * DC + 8 * lane;
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+      *reinterpret_cast<u32x4_t*>(dst + r * DC) =
+          *(const lds_u32x4_t*)uintptr_t(rbase + r * 1024 + 16 * (rkey ^ uint32_t(r)));
+    if (h == 0) a.part_ml[pidx + r32] = make_float2(m, lsum);
     lds_barrier();  // every wave is done with the stages before the next piece refills them
   };
 

@@ -131,6 +131,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 // 16-byte granule as a native vector.  Register arrays of HIP's uint4 struct are copied with memcpy
 // and can be left in private memory; arrays of this type stay in registers.
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16].  Lane l holds A row l%16 and B column
 // l%16, with 8 consecutive K values per lane (K block l/16); D column l%16, rows 4(l/16)..+3.
@@ -187,6 +188,7 @@ __device__ __forceinline__ int clamp_ctx(int v, int q_len, int max_seq_len) {
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 
 // One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4): lane l's data lands at
 // lds + 16 l.  Issued from asm so that the compiler does not track it (it would wait for every
