@@ -74,17 +74,19 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   const int n_wg = a.units;
 
   // ---- balanced partition.  Stream (b, grp) = tile group grp of sequence b, L_b steps of two
-  // blocks; streams are ordered (b, grp) and the workgroups take equal contiguous ranges of the
-  // concatenated steps.  A range cuts streams into pieces; the piece of stream s done by workgroup
-  // g keeps its partial under id g + s (unique: between consecutive pieces g or s grows), so the
-  // pieces of a stream have consecutive ids.
+  // blocks, preceded by kPieceCost units that stand for a piece's setup; streams are ordered
+  // (b, grp) and the workgroups take equal contiguous ranges of the concatenated units.  A range
+  // cuts streams into pieces; the piece of stream s done by workgroup g keeps its partial under
+  // id g + s (unique: between consecutive pieces g or s grows), so the pieces of a stream have
+  // consecutive ids.
+  constexpr int c = kPieceCost;
   auto steps_of = [&](int b) {
     const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
     return (((ctx + BLK - 1) / BLK) + 1) >> 1;
   };
-  int S = 0;  // total steps (uniform)
+  int S = 0;  // total units (uniform)
   for (int c0 = 0; c0 < a.batch; c0 += 64) {
-    int v = c0 + lane < a.batch ? steps_of(c0 + lane) : 0;
+    int v = c0 + lane < a.batch ? steps_of(c0 + lane) + c : 0;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
     S += __builtin_amdgcn_readfirstlane(v);
@@ -93,21 +95,22 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   const int W = (S + n_wg - 1) / n_wg;
   const int lo = int(blockIdx.x) * W;
   const int hi = min(lo + W, S);
-  // the sequence holding step lo: the last b whose streams start at or before lo; workgroup 0
+  // the sequence holding unit lo: the last b whose streams start at or before lo; workgroup 0
   // also records each stream's first piece id and piece count for the combine
   int bstar = 0, Cstar = 0, Lstar = 0;
   {
-    int C = 0;  // steps of the sequences before this chunk, per tile group
+    int C = 0;  // units of the sequences before this chunk, per tile group
     for (int c0 = 0; c0 < a.batch; c0 += 64) {
       const int b = c0 + lane;
       const int L = b < a.batch ? steps_of(b) : 0;
-      int incl = L;
+      const int U = b < a.batch ? L + c : 0;
+      int incl = U;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(incl, o, 64);
         if (lane >= o) incl += y;
       }
-      const int pre = C + incl - L;  // steps before sequence b, per tile group
+      const int pre = C + incl - U;  // units before sequence b, per tile group
       const uint64_t before = __ballot(b < a.batch && n_grp * pre <= lo);
       if (before) {
         const int k = 63 - __builtin_clzll(before);  // the last such lane (prefixes grow with b)
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       }
       if (blockIdx.x == 0 && w == 0 && b < a.batch) {
         for (int grp = 0; grp < n_grp; ++grp) {
-          const int st = n_grp * pre + grp * L, s = b * n_grp + grp;
+          const int st = n_grp * pre + grp * U + c, s = b * n_grp + grp;  // first step's unit
           const int gf = st / W, gl = (st + L - 1) / W;
           a.piece_tbl[s] = make_int2(gf + s, gl - gf + 1);
         }
@@ -415,19 +418,20 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
     lds_barrier();  // every wave is done with the stages before the next piece refills them
   };
 
-  // ---- walk this workgroup's range piece by piece
+  // ---- walk this workgroup's range stream by stream: the steps of stream (b, grp) are units
+  // [st, st + L_b) with st = its first unit + c
   int b = bstar, Lb = Lstar;
-  int off = lo - n_grp * Cstar;  // position within sequence b's streams
-  int grp = off / Lb, k0 = off % Lb;
-  for (int q = lo; q < hi;) {
-    const int k1 = min(Lb, k0 + (hi - q));
-    piece(b, grp, k0, k1, int(blockIdx.x) + b * n_grp + grp);
-    q += k1 - k0;
-    k0 = 0;
+  int grp = (lo - n_grp * Cstar) / (Lb + c);
+  int pos = n_grp * Cstar + grp * (Lb + c);  // first unit of stream (b, grp)
+  while (pos < hi) {
+    const int st = pos + c;
+    const int k0 = max(lo, st) - st, k1 = min(hi, st + Lb) - st;
+    if (k1 > k0) piece(b, grp, k0, k1, int(blockIdx.x) + b * n_grp + grp);
+    pos += Lb + c;
     if (++grp == n_grp) {
       grp = 0;
-      ++b;
-      if (q < hi) Lb = steps_of(b);
+      if (++b == a.batch) break;
+      Lb = steps_of(b);
     }
   }
 }

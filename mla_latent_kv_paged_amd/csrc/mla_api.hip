@@ -204,7 +204,7 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
     // workgroups the 32-row kernel may need: a resident slot each, or enough that no range
     // exceeds kMt32MaxSteps steps at the caps (every stream at max_seq_len)
     const int64_t streams = std::max<int64_t>(1, int64_t(cfg->max_q_tokens) * H / 32);
-    const int64_t steps_max = streams * ((max_blocks + 1) / 2);
+    const int64_t steps_max = streams * ((max_blocks + 1) / 2 + kPieceCost);
     c->max_wg32 = int(std::max<int64_t>(2 * c->cu_count, (steps_max + kMt32MaxSteps - 1) / kMt32MaxSteps));
   }
   const size_t part_rows = std::max(rows * c->max_split, size_t(128) * c->max_wg32 + rows);
@@ -311,7 +311,7 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
     // and enough workgroups that no range exceeds the block ids one workgroup stages in LDS
     n_wg = ctx->cu_count * (t32 == 4 ? 1 : 2);
     if (ctx->forced_split_blocks > 0) n_wg = ctx->forced_split_blocks;  // tuning: workgroup count
-    const int64_t steps_max = int64_t(batch) * groups * ((max_blocks + 1) / 2);
+    const int64_t steps_max = int64_t(batch) * groups * ((max_blocks + 1) / 2 + kPieceCost);
     n_wg = int(std::max<int64_t>(n_wg, (steps_max + kMt32MaxSteps - 1) / kMt32MaxSteps));
     if (n_wg > ctx->max_wg32) return MLA_ECAP;
   } else {

@@ -117,6 +117,11 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 // 32 rows per sequence (a multiple of T); units = workgroups, enough that every workgroup's share
 // is at most kMt32MaxSteps steps of two blocks
 constexpr int kMt32MaxSteps = 1024;
+// The 32-row kernel's partition charges each stream this many steps for its setup (query tile,
+// pipeline fill, partial store), so that a workgroup that starts several short streams is not
+// the last to finish: every workgroup's share, setups included, is at most one setup above the
+// mean.
+constexpr int kPieceCost = 6;
 hipError_t launch_decode_mt32(const DecodeArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s);
 
