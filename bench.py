@@ -98,6 +98,14 @@ def copy_calibration():
                       "copies": 5}), flush=True)
 
 
+def kernel_source_sha(src):
+    """sha256 of a decode kernel's source followed by the internal header it includes."""
+    h = hashlib.sha256()
+    for f in (src, "mla_internal.h"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_entry(args):
     """HBM traffic of the decode kernel from the committed rocprofv3 --pmc summary of this workload
     (default sizes only), if it was taken on the current kernel source; else None."""
@@ -109,8 +117,7 @@ def traffic_entry(args):
         return None
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != sha:
+        if rec.get("kernel_source_sha256") != kernel_source_sha(src):
             return None
         return rec.get("traffic_bytes_per_launch")
     except Exception:
