@@ -4,8 +4,9 @@
 // result is the log-sum-exp merge
 //   o_lat = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,   M = max_j m_j,
 // and then out[n, h, :] = o_lat . W_uv[h]^T.  Splits are merged in index order: deterministic.
-// The fp32 path keeps acc_j; the bf16 kernels store o_j = acc_j / l_j in fp16, merged with the
-// weights 2^(m_j - M) l_j.  A split with m_j = -inf saw no token and weighs nothing.
+// The fp32 path keeps acc_j; the bf16 kernels store o_j = acc_j / l_j in fp16 (divided by a power
+// of two ps_j if its largest entry would not fit), merged with the weights 2^(m_j - M) l_j.  A
+// split with m_j = -inf saw no token and weighs nothing.
 //
 // One workgroup per (head, 16 query rows); merged o_lat rows are staged in LDS.
 // bf16 storage: the projection is a batched MFMA GEMM computed transposed,
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   }
   for (int j0 = 0; j0 < ns_max; j0 += 4) {
     float2 ml[4][4];
-    u32x4_t vo[4][4];  // fp16 o of channels 8 lane .. 8 lane + 7
+    float ps[4][4];
+    u32x4_t vo[4][4];  // fp16 o / ps of channels 8 lane .. 8 lane + 7
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
@@ -159,6 +161,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
         const int jc = min(j0 + jj, max(ns[rr] - 1, 0));
         const int64_t pi = base[rr] + int64_t(jc) * stride[rr];
         ml[rr][jj] = a.part_ml[pi];
+        ps[rr][jj] = a.part_scale[pi];
         vo[rr][jj] = *reinterpret_cast<const u32x4_t*>(a.part_o16 + pi * DC + 8 * lane);
       }
 #pragma unroll
@@ -181,11 +184,12 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
         // weight of split j: 2^(m_j - M) l_j (its o is already divided by l_j)
         const float wgt = __builtin_amdgcn_exp2f(ml[rr][jj].x - mc) * ml[rr][jj].y;
         den[rr] += wgt;
+        const float wo = wgt * ps[rr][jj];  // the stored row is o / ps (a power of two)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const f32x2_t x = f16x2_to_f32(vo[rr][jj][e]);
-          o[rr][2 * e] = fmaf(wgt, x[0], o[rr][2 * e]);
-          o[rr][2 * e + 1] = fmaf(wgt, x[1], o[rr][2 * e + 1]);
+          o[rr][2 * e] = fmaf(wo, x[0], o[rr][2 * e]);
+          o[rr][2 * e + 1] = fmaf(wo, x[1], o[rr][2 * e + 1]);
         }
       }
     }

@@ -72,6 +72,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char q_mem[kBlockBytes];
   __shared__ float m_lds[NW][16];
   __shared__ float l_lds[NW][16];
+  __shared__ float x_lds[NW][16];
 
   // Work unit u = (sequence b, split j, row tile rt), rt fastest.  Workgroup i is dispatched to
   // XCD i % 8; each XCD gets a contiguous range of units so that the row tiles and neighbouring
@@ -303,25 +304,42 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
     for (int t = 0; t < 16; ++t) slots[t * 64 + lane] = acc[t];
   }
   __syncthreads();
+  // this wave's half of the merged accumulator; fixed order for every tile: wave 0's term first
+  f32x4_t fin[16];
+  if (w == 0) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) fin[t] = acc[t] + slots[t * 64 + lane];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) fin[t] = slots[(16 + t) * 64 + lane] + acc[16 + t];
+  }
   // The partial is stored normalised, o = acc / l, in fp16 (a convex combination of cache
-  // values), through an LDS tile (16 rows x 1 KB after the exchange slots; granule G of row r at
-  // slot G ^ r) so that each store instruction writes one whole 1 KB row.
+  // values), divided by a power of two when the row's largest |o| would not fit fp16.  The row
+  // spans both waves (lanes r16 + 16 g of each): max over the lane's values, its row's four
+  // lanes, then the two waves through LDS.
+  float mx = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(fin[t][e]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (g == 0) x_lds[w][r16] = mx;
+  __syncthreads();
   const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+  const float down = fp16_fit_scale(fmaxf(x_lds[0][r16], x_lds[1][r16]) * inv);
+  const float sc = inv * down;
+  // through an LDS tile (16 rows x 1 KB after the exchange slots; granule G of row r at slot
+  // G ^ r) so that each store instruction writes one whole 1 KB row
   lds_char_t* const otile = (lds_char_t*)ring_mem + 32 * 64 * 16;
   auto put = [&](int jj, f32x4_t v) {  // channels 16 jj + 4 g .. + 3 of row r16: granule 2 jj + g / 2
-    v *= inv;
+    v *= sc;
     const int G = 2 * jj + (g >> 1);
     *(lds_u32x2_t*)(otile + r16 * 1024 + 16 * (G ^ r16) + 8 * (g & 1)) =
         u32x2_t{cvt_pk_f16(v[0], v[1]), cvt_pk_f16(v[2], v[3])};
   };
-  // fixed order for every tile: wave 0's term first
-  if (w == 0) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) put(t, acc[t] + slots[t * 64 + lane]);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) put(16 + t, slots[(16 + t) * 64 + lane] + acc[16 + t]);
-  }
+  for (int t = 0; t < 16; ++t) put(16 * w + t, fin[t]);
   __syncthreads();
   const int64_t pidx = (int64_t(row) * a.H + h0 + r16) * a.n_split + j;  // this lane's row (r16)
 #pragma unroll
@@ -330,6 +348,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
     *reinterpret_cast<u32x4_t*>(a.part_o16 + pr * DC + 8 * lane) =
         *(const lds_u32x4_t*)(otile + r * 1024 + 16 * (lane ^ r));
   }
+  if (w == 0 && g == 0) a.part_scale[pidx] = 1.f / down;
   if (w == 0 && g == 0) a.part_ml[pidx] = make_float2(M, Ltot);
 }
 

@@ -391,6 +391,19 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
     mfma_drain();
     lsum += __shfl_xor(lsum, 32, 64);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    // divided by a power of two when the row's largest |o| would not fit fp16 (the row's values
+    // sit in lanes r32 and r32 + 32)
+    float mx = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 16; ++jt) {
+      f32x16_t v = acc[jt];
+      asm volatile("" : "+v"(v));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    }
+    mx = row_max(mx);
+    const float down = fp16_fit_scale(mx * inv);
+    const float sc = inv * down;
     lds_barrier();  // every wave is done with the last step's stage
     // (the swizzle keys are opaque here so that the 96 addresses are formed at their use, not
     // hoisted out of the piece loop and spilled)
@@ -405,7 +418,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       for (int q = 0; q < 4; ++q) {
         const uint32_t G = 4 * jt + q;
         *(lds_u32x2_t*)uintptr_t(wbase + 16 * (G ^ wkey)) =
-            u32x2_t{cvt_pk_f16(v[4 * q] * inv, v[4 * q + 1] * inv), cvt_pk_f16(v[4 * q + 2] * inv, v[4 * q + 3] * inv)};
+            u32x2_t{cvt_pk_f16(v[4 * q] * sc, v[4 * q + 1] * sc), cvt_pk_f16(v[4 * q + 2] * sc, v[4 * q + 3] * sc)};
       }
     }
     const int64_t pidx = int64_t(pid) * RP + w * 32;
@@ -414,7 +427,10 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
     for (int r = 0; r < 32; ++r)
       *reinterpret_cast<u32x4_t*>(dst + r * DC) =
           *(const lds_u32x4_t*)uintptr_t(rbase + r * 1024 + 16 * (rkey ^ uint32_t(r)));
-    if (h == 0) a.part_ml[pidx + r32] = make_float2(m, lsum);
+    if (h == 0) {
+      a.part_ml[pidx + r32] = make_float2(m, lsum);
+      a.part_scale[pidx + r32] = 1.f / down;
+    }
     lds_barrier();  // every wave is done with the stages before the next piece refills them
   };
 

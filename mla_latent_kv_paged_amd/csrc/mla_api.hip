@@ -43,6 +43,7 @@ struct mla_ctx {
   void* qcat = nullptr;
   float* part_acc = nullptr;
   float2* part_ml = nullptr;
+  float* part_scale = nullptr;
   int2* piece_tbl = nullptr;  // 32-row kernel: per stream (first piece id, piece count)
   int32_t max_wg32 = 0;       // 32-row kernel: most workgroups the partial buffer holds pieces for
   int32_t max_split = 1;
@@ -68,6 +69,7 @@ void ctx_release(mla_ctx* c) {
   hipFree(c->qcat);
   hipFree(c->part_acc);
   hipFree(c->part_ml);
+  hipFree(c->part_scale);
   hipFree(c->piece_tbl);
   if (c->prof.created)
     for (int k = 0; k < MLA_K_COUNT; ++k)
@@ -210,6 +212,7 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
   const size_t part_rows = std::max(rows * c->max_split, size_t(128) * c->max_wg32 + rows);
   alloc(reinterpret_cast<void**>(&c->part_acc), part_rows * DC * sizeof(float));
   alloc(reinterpret_cast<void**>(&c->part_ml), part_rows * sizeof(float2));
+  alloc(reinterpret_cast<void**>(&c->part_scale), part_rows * sizeof(float));
   alloc(reinterpret_cast<void**>(&c->piece_tbl), (rows / 32 + 1) * sizeof(int2));
   if (e != hipSuccess) {
     ctx_release(c);
@@ -339,7 +342,7 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   {
     DecodeArgs da{batch,  kv_cache,       ctx->zero_block, num_blocks,    block_table, block_table_stride,
                   seq_lens, max_seq_len,  q_len,           H,             ctx->qcat,   ctx->part_acc,
-                  reinterpret_cast<uint16_t*>(ctx->part_acc), ctx->part_ml, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
+                  reinterpret_cast<uint16_t*>(ctx->part_acc), ctx->part_ml, ctx->part_scale, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
                   ctx->piece_tbl};
     ProfScope ps(ctx, MLA_K_DECODE, s);
     e = t32 ? launch_decode_mt32(da, t32, s) : launch_decode(ctx->bf16, da, waves, s);
@@ -348,7 +351,7 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   {
     // output channels split over 4 workgroups only when the (head, 16 rows) grid is small
     const int v_parts = int64_t(H) * ((n_q + 15) / 16) >= 2 * ctx->cu_count ? 1 : 4;
-    CombineArgs ca{ctx->part_acc, reinterpret_cast<const uint16_t*>(ctx->part_acc), ctx->part_ml, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split,
+    CombineArgs ca{ctx->part_acc, reinterpret_cast<const uint16_t*>(ctx->part_acc), ctx->part_ml, ctx->part_scale, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split,
                    ctx->W_uv, ctx->W_uvT, out, t32 ? ctx->piece_tbl : nullptr, 32 * t32,
                    t32 ? n_rt / t32 : 0, v_parts};
     ProfScope ps(ctx, MLA_K_COMBINE, s);

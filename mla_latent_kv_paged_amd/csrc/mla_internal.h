@@ -75,6 +75,7 @@ struct DecodeArgs {
   float* part_acc;        // fp32 kernel: [n_q*H*n_split, DC] unnormalised accumulators
   uint16_t* part_o16;     // bf16 kernels (same memory): [rows, DC] fp16 o = acc / l (0 when l = 0)
   float2* part_ml;        // [rows] (running max in log2 units, sum); (-inf, 0): nothing visible
+  float* part_scale;      // bf16 kernels: [rows] the power of two the fp16 row was divided by
   int32_t split_blocks;
   int32_t n_split;
   int32_t n_rt;           // row tiles per sequence: of 16 rows ((H/16) * q_len), or of 32 for the 32-row kernel
@@ -86,6 +87,7 @@ struct CombineArgs {
   const float* part_acc;  // fp32 path
   const uint16_t* part_o16;  // bf16 path: fp16 normalised partials (acc / l)
   const float2* part_ml;
+  const float* part_scale;  // bf16 path: the fp16 partial row times this is o
   const int32_t* seq_lens;
   int32_t max_seq_len;
   int32_t q_len;
@@ -163,6 +165,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
+// Power of two 2^-k (k >= 0) that brings x (>= 0) below 2^15, so that x * 2^-k fits fp16 with room to
+// spare; 1 for x < 2^15.  Exact scaling: it changes no mantissa bit.
+__device__ __forceinline__ float fp16_fit_scale(float x) {
+  const int E = int((__float_as_uint(x) >> 23) & 0xffu) - 126;  // x < 2^E for normal x
+  const int k = E > 15 ? E - 15 : 0;
+  return __uint_as_float(uint32_t(127 - (k > 126 ? 126 : k)) << 23);
 }
 
 // Two floats -> packed fp16 pair (low half = lo), round to nearest even.

@@ -93,6 +93,40 @@ def test_decode_only_from_generator_pool():
         run.free()
 
 
+@pytest.mark.parametrize("heads,q_len", [(16, 1), (32, 1), (16, 4)])
+def test_latent_beyond_fp16_range(heads, q_len):
+    """Latent cache entries far beyond fp16's range (the c part scaled by 2^17 > 65504, exact in
+    bf16) with W_uk scaled by 2^-17, so that every score is unchanged and the output scales by
+    exactly 2^17.  The bf16 kernels keep their split / piece partials in fp16; a partial row that
+    would not fit must be stored scaled, not overflow.  One case per bf16 decode kernel shape (16
+    rows; 32 rows with one and with two tiles per workgroup); compared after dividing by 2^17."""
+    from mla_latent_kv_paged_amd import MLAContext
+    w = W.custom("big", "bf16", heads, [40, 300, 77, 1000], q_len=q_len, seed=71)
+    _say("latent beyond fp16", "H", heads, "q_len", q_len)
+    big = 2.0 ** 17
+    pool = w.random_pool()
+    pool[..., :512] *= big
+    kvb = w.kv_b_proj().reshape(heads, 256, 512).copy()
+    kvb[:, :128, :] /= big  # W_uk rows
+    kvb = kvb.reshape(heads * 256, 512)
+    W_uk, W_uv = O.absorb(kvb.astype(np.float64), heads, 128, 128)
+    ref = O.decode_absorbed(w.queries(), pool.astype(np.float64), w.block_table, w.seq_lens, w.q_len, W_uk, W_uv,
+                            w.scale, w.theta)
+    mx = int(w.seq_lens.max())
+    ctx = MLAContext(dev(kvb, "bf16"), None, num_heads=heads, dtype="bf16", rms_eps=w.eps, rope_theta=w.theta,
+                     max_q_tokens=w.n_q, max_batch=w.batch, max_position=mx + 16, max_seq_len=mx + 16)
+    try:
+        for sb in (0, 5):  # the library's split, and short splits (many partials per row)
+            ctx.set_decode_tuning(sb, 0)
+            out = ctx.decode(dev(w.queries(), "bf16"), dev(pool, "bf16"), dev_i32(w.block_table),
+                             dev_i32(w.seq_lens), mx, q_len=w.q_len)
+            torch.cuda.synchronize()
+            got = out.to(torch.float32).cpu().numpy().astype(np.float64) / big
+            compare(got, ref / big, "bf16", f"latent x2^17 H={heads} q_len={q_len} split={sb}")
+    finally:
+        ctx.free()
+
+
 @pytest.mark.parametrize("heads,q_len", [(16, 1), (16, 2), (128, 1)])
 def test_large_score_jump(heads, q_len):
     """A score far above everything before it: the rope part of the token at position 200 is scaled
