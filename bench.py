@@ -269,12 +269,37 @@ def main():
                       ("combine", K_COMBINE)):
         tot, n = ctx.profile_read(kid)
         kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+    dec_samples = np.array(ctx.profile_samples(K_DECODE)) * 1e3
     ctx.profile_enable(False)
     shape = ctx.last_decode_shape()
+    # pass C: each step bracketed by its own events (distribution of the step time)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    step_samples = np.array([a_.elapsed_time(b_) for a_, b_ in ev]) * 1e3
+    # pass D: un-flushed, every step on the same pool (the previous step's cache may still sit in
+    # the 256 MB Infinity Cache)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        ctx.cache_write(nc, nk, npos, nslot, pools[0])
+        ctx.decode(q, pools[0], bt, sl, max_ctx, q_len=w.q_len, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    unflushed_us = e0.elapsed_time(e1) / args.steps * 1e3
+
+    def pct(x):
+        return {"p10": round(float(np.percentile(x, 10)), 2), "median": round(float(np.median(x)), 2),
+                "p90": round(float(np.percentile(x, 90)), 2)}
 
     latent_bytes = w.latent_bytes()
     decode_us = kern["decode"]["avg_us"]
     flops_attn = w.total_ctx * w.num_heads * w.q_len * 2 * (576 + 512)
+    flops_gemm = 2 * w.n_q * w.num_heads * 131072  # q_nope . W_uk and o_lat . W_uv^T
+    mla_decode_us = kern["q_absorb"]["avg_us"] + decode_us + kern["combine"]["avg_us"]
     achieved = latent_bytes / (decode_us * 1e-6) / 1e9
     traffic = traffic_entry(args)
     rows32 = (w.num_heads * w.q_len) % 32 == 0
@@ -283,7 +308,10 @@ def main():
                 "kernel": ("decode_bf16_mt32_kernel" if rows32 else "decode_bf16_kernel") if w.storage == "bf16"
                 else "decode_f32_kernel",
                 "algorithmic_bytes_per_launch": latent_bytes,
-                "mfma_tflops": round(flops_attn / (decode_us * 1e-6) / 1e12, 2)}
+                "mfma_tflops": round(flops_attn / (decode_us * 1e-6) / 1e12, 2),
+                "mfma_frac": round(flops_attn / (decode_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "mfma_frac_mla_decode": round((flops_attn + flops_gemm) / (mla_decode_us * 1e-6) / 1e12
+                                              / BF16_PEAK_TFLOPS, 4)}
     step_us = ms_per_step * 1e3
     res = {
         "metric": METRIC,
@@ -299,6 +327,9 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/512) kv_b_proj)",
         "config": describe(w),
         "decode_us": round(decode_us, 2),
+        "decode_us_dist": pct(dec_samples),
+        "step_us_dist": pct(step_samples),
+        "unflushed_us_per_step": round(unflushed_us, 2),
         "decode_latent_gbps": round(achieved, 1),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "split": shape,

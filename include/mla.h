@@ -179,6 +179,11 @@ mla_status mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* Synchronises the recorded events and returns the summed milliseconds and launch count of
  * kernel `kernel_id` since profiling was enabled. */
 mla_status mla_profile_read(mla_ctx* ctx, int32_t kernel_id, double* total_ms, int64_t* launches);
+/* Synchronises the recorded events and copies the durations (ms) of the most recent launches of
+ * kernel `kernel_id` (at most 1024 are kept, and at most `max` are copied, oldest first) to the
+ * host array `ms`; *n receives the number copied.  MLA_EINVAL for a bad id, max < 0, or NULL ms
+ * with max > 0. */
+mla_status mla_profile_samples(mla_ctx* ctx, int32_t kernel_id, float* ms, int32_t max, int32_t* n);
 
 #ifdef __cplusplus
 }

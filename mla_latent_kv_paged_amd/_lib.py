@@ -19,7 +19,8 @@ MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
 
 EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_free", "mla_status_string",
-           "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read")
+           "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",
+           "mla_profile_samples")
 
 
 class MLAConfig(ctypes.Structure):
@@ -68,6 +69,8 @@ def load(path=None):
     lib.mla_profile_enable.restype = i32
     lib.mla_profile_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     lib.mla_profile_read.restype = i32
+    lib.mla_profile_samples.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
+    lib.mla_profile_samples.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -203,6 +206,14 @@ class MLAContext:
         _check(self.lib.mla_profile_read(self.handle, int(kernel_id), ctypes.byref(ms), ctypes.byref(n)),
                "mla_profile_read")
         return ms.value, n.value
+
+    def profile_samples(self, kernel_id, max_n=1024):
+        """Durations (ms) of the most recent launches of a kernel, oldest first."""
+        buf = (ctypes.c_float * max_n)()
+        n = ctypes.c_int32()
+        _check(self.lib.mla_profile_samples(self.handle, int(kernel_id), buf, int(max_n), ctypes.byref(n)),
+               "mla_profile_samples")
+        return list(buf[:n.value])
 
 
 def default_scale():

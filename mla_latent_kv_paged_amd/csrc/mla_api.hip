@@ -417,4 +417,23 @@ mla_status mla_profile_read(mla_ctx* ctx, int32_t kernel_id, double* total_ms, i
   return MLA_OK;
 }
 
+mla_status mla_profile_samples(mla_ctx* ctx, int32_t kernel_id, float* ms, int32_t max, int32_t* n_out) {
+  if (n_out) *n_out = 0;
+  if (!ctx || kernel_id < 0 || kernel_id >= MLA_K_COUNT || max < 0 || (!ms && max > 0)) return MLA_EINVAL;
+  const int64_t n = ctx->prof.count[kernel_id];
+  int64_t first = n > kProfRing ? n - kProfRing : 0;
+  if (n - first > max) first = n - max;
+  int32_t m = 0;
+  for (int64_t i = first; i < n; ++i) {
+    const int slot = int(i % kProfRing);
+    float t = 0.f;
+    if (hipEventSynchronize(ctx->prof.ev[kernel_id][slot][1]) != hipSuccess ||
+        hipEventElapsedTime(&t, ctx->prof.ev[kernel_id][slot][0], ctx->prof.ev[kernel_id][slot][1]) != hipSuccess)
+      return MLA_EHIP;
+    ms[m++] = t;
+  }
+  if (n_out) *n_out = m;
+  return MLA_OK;
+}
+
 }  // extern "C"
