@@ -41,7 +41,10 @@ extern "C" {
 
 typedef struct mla_ctx mla_ctx; /* opaque, library-owned */
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+/* MLA_BF16_FP8: bf16 like MLA_BF16 for q, c_kv, k_pe, the weights, gamma and out; the cache holds
+ * FP8 rows (see mla_cache_write).  The vLLM learning book (ch. 07) lists an FP8 KV cache for MLA;
+ * the pages fix no scale convention or layout, so both are this library's. */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_BF16_FP8 = 2 } mla_dtype;
 
 typedef enum {
   MLA_OK = 0,
@@ -104,7 +107,18 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
  *  positions              device int32 [T] RoPE position of each token.
  *  slot_mapping           device int32 [T]; a negative slot skips the token (padding).
  *  num_tokens             T >= 0 (0 is a no-op).
- *  kv_cache, num_blocks   device [num_blocks, 16, 1, dc + dr] in the storage dtype.
+ *  kv_cache, num_blocks   device [num_blocks, 16, 1, dc + dr] in the storage dtype; with
+ *                         MLA_BF16_FP8, [num_blocks, 16, 1, 656] bytes, one row per slot:
+ *                           bytes   0..511  the normed latent as FP8 E4M3 codes (OCP: bias 7, max
+ *                                           448, no infinities), channel order;
+ *                           bytes 512..639  the rotated rope values, bf16 (round to nearest even);
+ *                           bytes 640..655  4 fp32 scales, one per group of 128 latent channels.
+ *                         Channel i holds e4m3(code_i) * scale[i / 128].  Per group, scale =
+ *                         fp32(amax / 448) (amax = largest |value|; stepped up one fp32 value if
+ *                         amax / scale would exceed 448; 1 for an all-zero group) and code_i =
+ *                         the E4M3 value nearest value_i / scale (quotient in fp64), ties to the
+ *                         even code.  A position outside 0..max_position writes NaN codes, rope
+ *                         values and scales.
  * Device-side handling: a slot at or beyond num_blocks*16 is skipped; a position outside
  * 0..max_position writes a row of NaN so that the error is visible downstream.
  * Slots not named in slot_mapping are not touched.  Two tokens naming one slot race.
@@ -131,7 +145,9 @@ mla_status mla_cache_write(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
  *
  *  q                    device [batch*q_len, H, dn + dr], per head [nope | rope] (rope un-rotated).
  *  batch, q_len         batch >= 1, 1 <= q_len; batch <= max_batch, batch*q_len <= max_q_tokens.
- *  kv_cache, num_blocks device [num_blocks, 16, 1, dc + dr] (already written for every t < ctx).
+ *  kv_cache, num_blocks device [num_blocks, 16, 1, dc + dr] (already written for every t < ctx);
+ *                       MLA_BF16_FP8: the 656-byte rows of mla_cache_write, whose latent values are
+ *                       e4m3(code) * scale exactly (the kernel rounds nothing on the way in).
  *  block_table, stride  device int32 [batch, stride]; entries for t >= ctx are not read.
  *  seq_lens             device int32 [batch]: context length ctx_b INCLUDING the q_len new
  *                       tokens (which must already be in the cache), q_len <= ctx_b <= max_seq_len.

@@ -14,7 +14,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla.so")
 
-MLA_F32, MLA_BF16 = 0, 1
+MLA_F32, MLA_BF16, MLA_BF16_FP8 = 0, 1, 2
+FP8_ROW_BYTES = 656  # FP8 cache row: 512 e4m3 codes | 64 bf16 rope values | 4 fp32 group scales
 MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2, -3, -4, -5
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
 
@@ -124,13 +125,18 @@ class MLAContext:
                  stream=None):
         torch = _torch()
         self.lib = load()
+        if dtype not in ("bf16", "f32", "fp8"):
+            raise ValueError("dtype must be 'bf16', 'f32' or 'fp8' (bf16 with an FP8 cache)")
         self.storage = dtype
-        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.tdtype = torch.float32 if dtype == "f32" else torch.bfloat16
+        # cache tensors: [n, 16, 1, 576] of the storage dtype, or [n, 16, 1, 656] bytes for fp8
+        self.cache_dtype = torch.uint8 if dtype == "fp8" else self.tdtype
+        self.cache_row = FP8_ROW_BYTES if dtype == "fp8" else 576
         self.num_heads = num_heads
         _need(kv_b_proj, "kv_b_proj", self.tdtype, shape=(num_heads * 256, 512))
         if gamma is not None:
             _need(gamma, "gamma", self.tdtype, shape=(512,))
-        cfg = MLAConfig(num_heads, 512, 128, 64, 128, 16, MLA_BF16 if dtype == "bf16" else MLA_F32,
+        cfg = MLAConfig(num_heads, 512, 128, 64, 128, 16, {"bf16": MLA_BF16, "f32": MLA_F32, "fp8": MLA_BF16_FP8}[dtype],
                         softmax_scale, rms_eps, rope_theta, max_q_tokens, max_batch, max_position, max_seq_len)
         self.cfg = cfg
         h = ctypes.c_void_p()
@@ -154,9 +160,9 @@ class MLAContext:
     def cache_write(self, c_kv, k_pe, positions, slot_mapping, kv_cache, stream=None):
         torch = _torch()
         T = int(positions.shape[0]) if positions is not None else 0
-        _need(kv_cache, "kv_cache", self.tdtype)
-        if kv_cache.dim() != 4 or tuple(kv_cache.shape[1:]) != (16, 1, 576):
-            raise ValueError("kv_cache must be [n_blocks, 16, 1, 576]")
+        _need(kv_cache, "kv_cache", self.cache_dtype)
+        if kv_cache.dim() != 4 or tuple(kv_cache.shape[1:]) != (16, 1, self.cache_row):
+            raise ValueError(f"kv_cache must be [n_blocks, 16, 1, {self.cache_row}]")
         if T:
             _need(c_kv, "c_kv", self.tdtype, contiguous=False)
             _need(k_pe, "k_pe", self.tdtype, contiguous=False)
@@ -174,7 +180,9 @@ class MLAContext:
         H = self.num_heads
         batch = int(seq_lens.shape[0])
         _need(q, "q", self.tdtype, shape=(batch * q_len, H, 192))
-        _need(kv_cache, "kv_cache", self.tdtype)
+        _need(kv_cache, "kv_cache", self.cache_dtype)
+        if kv_cache.dim() != 4 or tuple(kv_cache.shape[1:]) != (16, 1, self.cache_row):
+            raise ValueError(f"kv_cache must be [n_blocks, 16, 1, {self.cache_row}]")
         _need(block_table, "block_table", torch.int32)
         _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
         if block_table.dim() != 2 or block_table.shape[0] != batch:

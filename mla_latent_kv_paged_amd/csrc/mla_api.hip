@@ -29,7 +29,8 @@ struct Prof {
 
 struct mla_ctx {
   mla_config cfg;
-  bool bf16 = false;
+  bool bf16 = false;  // bf16 inputs, weights and outputs (MLA_BF16 and MLA_BF16_FP8)
+  bool fp8 = false;   // FP8 cache rows (MLA_BF16_FP8)
   int device = 0;
   int cu_count = 256;
   float qscale = 0.f;
@@ -154,7 +155,7 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
                               void* stream, mla_ctx** out) {
   if (out) *out = nullptr;
   if (!cfg || !kv_b_proj_w || !out) return MLA_EINVAL;
-  if (cfg->dtype != MLA_F32 && cfg->dtype != MLA_BF16) return MLA_EUNSUPPORTED;
+  if (cfg->dtype != MLA_F32 && cfg->dtype != MLA_BF16 && cfg->dtype != MLA_BF16_FP8) return MLA_EUNSUPPORTED;
   if (cfg->kv_lora_rank != DC || cfg->qk_rope_head_dim != DR || cfg->qk_nope_head_dim != DN ||
       cfg->v_head_dim != DV || cfg->block_size != BLK)
     return MLA_EUNSUPPORTED;
@@ -167,7 +168,8 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
   mla_ctx* c = new (std::nothrow) mla_ctx();
   if (!c) return MLA_ENOMEM;
   c->cfg = *cfg;
-  c->bf16 = cfg->dtype == MLA_BF16;
+  c->bf16 = cfg->dtype != MLA_F32;
+  c->fp8 = cfg->dtype == MLA_BF16_FP8;
   hipStream_t s = as_stream(stream);
   if (hipGetDevice(&c->device) != hipSuccess) {
     ctx_release(c);
@@ -282,7 +284,7 @@ mla_status mla_cache_write(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
                    kv_cache, int64_t(num_blocks) * BLK, ctx->gamma, ctx->rope, ctx->cfg.max_position,
                    double(ctx->cfg.rms_eps)};
   ProfScope ps(ctx, MLA_K_CACHE_WRITE, s);
-  return hip_status(launch_cache_write(ctx->bf16, a, s));
+  return hip_status(ctx->fp8 ? launch_cache_write_fp8(a, s) : launch_cache_write(ctx->bf16, a, s));
 }
 
 mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
@@ -304,7 +306,8 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   // bf16 kernels by rows per sequence: a multiple of 32 -> 32-row tiles, T of them per workgroup
   // (each block read once per workgroup); otherwise the one-tile kernel, 16-row tiles in the grid
   const int n_rt32 = (H * q_len) % 32 == 0 ? H * q_len / 32 : 0;
-  const int t32 = (ctx->bf16 && n_rt32 > 0) ? ((n_rt32 % 4 == 0) ? 4 : (n_rt32 % 2 == 0) ? 2 : 1) : 0;
+  // (FP8 cache rows: the 16-row FP8 kernel for every shape)
+  const int t32 = (ctx->bf16 && !ctx->fp8 && n_rt32 > 0) ? ((n_rt32 % 4 == 0) ? 4 : (n_rt32 % 2 == 0) ? 2 : 1) : 0;
   const int n_rt = t32 ? n_rt32 : n_rt16;
   const int waves = ctx->bf16 ? (t32 ? t32 : (ctx->forced_waves > 0 ? ctx->forced_waves : 2)) : 1;
   const int groups = t32 ? n_rt / t32 : n_rt;  // workgroups per (sequence, split)
@@ -345,7 +348,7 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
                   reinterpret_cast<uint16_t*>(ctx->part_acc), ctx->part_ml, ctx->part_scale, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
                   ctx->piece_tbl};
     ProfScope ps(ctx, MLA_K_DECODE, s);
-    e = t32 ? launch_decode_mt32(da, t32, s) : launch_decode(ctx->bf16, da, waves, s);
+    e = t32 ? launch_decode_mt32(da, t32, s) : ctx->fp8 ? launch_decode_fp8(da, s) : launch_decode(ctx->bf16, da, waves, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {

@@ -17,6 +17,9 @@ constexpr int ROW = DC + DR;   // 576 values per cache slot
 constexpr int QW = DN + DR;    // 192 values per head of q
 constexpr int BLK = 16;        // tokens per paged block
 constexpr int NPAIR = DR / 2;  // RoPE pairs
+// FP8 cache rows: [DC e4m3 codes | DR bf16 rope values | 4 fp32 group scales (128 channels each)]
+constexpr int kFp8Row = DC + 2 * DR + 16;  // 656 bytes
+constexpr int kFp8Block = BLK * kFp8Row;   // 10,496 bytes
 
 // ------------------------------------------------------------------------------ kernel arguments
 
@@ -111,10 +114,13 @@ struct CombineArgs {
 
 hipError_t launch_absorb(bool bf16, const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_cache_write(bool bf16, const CacheWriteArgs& a, hipStream_t s);
+hipError_t launch_cache_write_fp8(const CacheWriteArgs& a, hipStream_t s);  // bf16 inputs, fp8 rows
 hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s);
 // waves: waves per workgroup of the bf16 decode kernel (ignored in fp32 mode)
 hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+// FP8 cache rows (kFp8Row bytes), 16-row tiles; every H multiple of 16 and every q_len
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s);
 // bf16, 32-row tiles (H*q_len a multiple of 32), T in {1, 2, 4} tiles per workgroup; n_rt = tiles of
 // 32 rows per sequence (a multiple of T); units = workgroups, enough that every workgroup's share
 // is at most kMt32MaxSteps steps of two blocks
