@@ -38,6 +38,7 @@ CSRC = os.path.join(ROOT, "mla_latent_kv_paged_amd", "csrc")
 TRAFFIC = {"lite_b64": ("decode_bf16_lite_b64_s4096_traffic.json", "decode_bf16.hip"),
            "wide": ("decode_bf16_mt32_wide_h128_b128_traffic.json", "decode_bf16_mt32.hip"),
            "ragged": ("decode_bf16_mt32_ragged_b256_q4_traffic.json", "decode_bf16_mt32.hip")}
+TRAFFIC_FP8 = {"lite_b64": ("decode_fp8_lite_b64_s4096_traffic.json", "decode_fp8.hip")}
 
 
 def parse():
@@ -50,6 +51,9 @@ def parse():
                     "lite_b64: default 4096)")
     ap.add_argument("--batch", type=int, default=0, help="batch for lite_b64 (default 64)")
     ap.add_argument("--rotate", type=int, default=3, help="cache pool copies rotated between steps")
+    ap.add_argument("--cache", default="native", choices=["native", "fp8"],
+                    help="native: the workload's storage dtype (bf16 for the benchmark workloads); fp8: "
+                         "FP8 E4M3 latent rows of 656 bytes (MLA_BF16_FP8), bf16 everything else")
     ap.add_argument("--split-blocks", type=int, default=0, help="force the split size (0 = library choice)")
     ap.add_argument("--waves", type=int, default=0, help="force waves per decode workgroup (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -109,9 +113,10 @@ def kernel_source_sha(src):
 def traffic_entry(args):
     """HBM traffic of the decode kernel from the committed rocprofv3 --pmc summary of this workload
     (default sizes only), if it was taken on the current kernel source; else None."""
-    if args.workload not in TRAFFIC or args.seq_len or args.batch:
+    table = TRAFFIC_FP8 if getattr(args, "cache", "native") == "fp8" else TRAFFIC
+    if args.workload not in table or args.seq_len or args.batch:
         return None
-    fname, src = TRAFFIC[args.workload]
+    fname, src = table[args.workload]
     path = os.path.join(PROFILES, fname)
     if not os.path.exists(path):
         return None
@@ -124,11 +129,12 @@ def traffic_entry(args):
         return None
 
 
-def cpu_baseline(w, n_seq):
+def cpu_baseline(w, n_seq, fp8=False):
     """Time the fp64 oracle (absorbed form) on a bounded sample of the same workload: the step's
     cache write of each sampled sequence's new tokens plus its full decode."""
     import numpy as np
     from oracle import mla_oracle as O
+    from oracle import mla_fp8 as F
     try:
         from threadpoolctl import threadpool_limits, threadpool_info
     except Exception:  # pragma: no cover
@@ -147,8 +153,12 @@ def cpu_baseline(w, n_seq):
         nb = (ctx + 15) // 16
         c, k = w.history(b)
         hist = ctx - w.q_len
-        pool = O.cache_write(np.full((nb, 16, 1, 576), np.nan), c[:hist], k[:hist], np.arange(hist),
-                             np.arange(hist), gamma, w.eps, w.theta, w.storage)
+        if fp8:
+            pool = F.cache_write_fp8(np.zeros((nb, 16, 1, F.ROW_BYTES), np.uint8), c[:hist], k[:hist],
+                                     np.arange(hist), np.arange(hist), gamma, w.eps, w.theta)
+        else:
+            pool = O.cache_write(np.full((nb, 16, 1, 576), np.nan), c[:hist], k[:hist], np.arange(hist),
+                                 np.arange(hist), gamma, w.eps, w.theta, w.storage)
         prepared.append((b, ctx, nb, c[hist:], k[hist:], pool))
     # repeat the sampled step until about 10 s of CPU work has been timed (at least 3 runs, at most
     # 30 s), and report the median run
@@ -156,8 +166,12 @@ def cpu_baseline(w, n_seq):
     while len(times) < 3 or (sum(times) < 10.0 and len(times) < 200):
         t0 = time.perf_counter()
         for b, ctx, nb, cn, kn, pool in prepared:
-            cache = O.cache_write(pool, cn, kn, np.arange(ctx - w.q_len, ctx), np.arange(ctx - w.q_len, ctx),
-                                  gamma, w.eps, w.theta, w.storage)
+            if fp8:  # the FP8 write, then the values the decode sees
+                cache = F.dequantize_cache(F.cache_write_fp8(pool, cn, kn, np.arange(ctx - w.q_len, ctx),
+                                                             np.arange(ctx - w.q_len, ctx), gamma, w.eps, w.theta))
+            else:
+                cache = O.cache_write(pool, cn, kn, np.arange(ctx - w.q_len, ctx), np.arange(ctx - w.q_len, ctx),
+                                      gamma, w.eps, w.theta, w.storage)
             O.decode_absorbed(qall[b * w.q_len:(b + 1) * w.q_len], cache, np.arange(nb)[None, :],
                               np.array([ctx]), w.q_len, W_uk, W_uv, w.scale, w.theta)
         times.append(time.perf_counter() - t0)
@@ -172,7 +186,7 @@ def cpu_baseline(w, n_seq):
             pass
     if ctxmgr is not None:
         ctxmgr.unregister() if hasattr(ctxmgr, "unregister") else None
-    bytes_sample = sum(int(w.seq_lens[b]) for b in seqs) * 576 * w.elem_bytes
+    bytes_sample = sum(int(w.seq_lens[b]) for b in seqs) * (F.ROW_BYTES if fp8 else 576 * w.elem_bytes)
     return {"value": bytes_sample / t / 1e9, "unit": "GB/s", "cores": int(min(cores, blas_threads)),
             "kind": "oracle",
             "sample": f"{len(seqs)} of {w.batch} sequences (full context each); one step = cache write of the "
@@ -197,6 +211,9 @@ def main():
 
     w = make_workload(args)
     dt = torch.bfloat16 if w.storage == "bf16" else torch.float32
+    fp8 = args.cache == "fp8"
+    if fp8 and w.storage != "bf16":
+        raise SystemExit("--cache fp8 needs a bf16 workload")
 
     def dev(x):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda().to(dt)
@@ -209,12 +226,16 @@ def main():
     kvb = dev(w.kv_b_proj())
     torch.cuda.synchronize()
     ta = time.perf_counter()
-    ctx = MLAContext(kvb, None, num_heads=w.num_heads, dtype=w.storage, rms_eps=w.eps, rope_theta=w.theta,
+    ctx = MLAContext(kvb, None, num_heads=w.num_heads, dtype="fp8" if fp8 else w.storage, rms_eps=w.eps,
+                     rope_theta=w.theta,
                      max_q_tokens=w.n_q, max_batch=w.batch, max_position=max_ctx, max_seq_len=max_ctx)
     absorb_ms = (time.perf_counter() - ta) * 1e3
     if args.split_blocks or args.waves:
         ctx.set_decode_tuning(args.split_blocks, args.waves)
-    pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=dt, device="cuda")
+    if fp8:
+        pool = torch.zeros((w.n_blocks, 16, 1, 656), dtype=torch.uint8, device="cuda")
+    else:
+        pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=dt, device="cuda")
     new_c, new_k, new_pos, new_slot = [], [], [], []
     for b in range(w.batch):       # history fill through the library, one sequence at a time
         c, k = w.history(b)
@@ -295,7 +316,7 @@ def main():
         return {"p10": round(float(np.percentile(x, 10)), 2), "median": round(float(np.median(x)), 2),
                 "p90": round(float(np.percentile(x, 90)), 2)}
 
-    latent_bytes = w.latent_bytes()
+    latent_bytes = w.total_ctx * 656 if fp8 else w.latent_bytes()
     decode_us = kern["decode"]["avg_us"]
     flops_attn = w.total_ctx * w.num_heads * w.q_len * 2 * (576 + 512)
     flops_gemm = 2 * w.n_q * w.num_heads * 131072  # q_nope . W_uk and o_lat . W_uv^T
@@ -305,7 +326,8 @@ def main():
     rows32 = (w.num_heads * w.q_len) % 32 == 0
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": ("decode_bf16_mt32_kernel" if rows32 else "decode_bf16_kernel") if w.storage == "bf16"
+                "kernel": "decode_fp8_kernel" if fp8 else
+                ("decode_bf16_mt32_kernel" if rows32 else "decode_bf16_kernel") if w.storage == "bf16"
                 else "decode_f32_kernel",
                 "algorithmic_bytes_per_launch": latent_bytes,
                 "mfma_tflops": round(flops_attn / (decode_us * 1e-6) / 1e12, 2),
@@ -325,7 +347,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.storage == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/512) kv_b_proj)",
-        "config": describe(w),
+        "config": dict(describe(w), cache="fp8 e4m3, 656 B per token (MLA_BF16_FP8)" if fp8 else "native"),
         "decode_us": round(decode_us, 2),
         "decode_us_dist": pct(dec_samples),
         "step_us_dist": pct(step_samples),
@@ -339,7 +361,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample if not fp8 else min(args.cpu_sample, 8), fp8)
     ctx.free()
     print(json.dumps(res), flush=True)
 

@@ -177,7 +177,8 @@ void mla_free(mla_ctx* ctx);
 const char* mla_status_string(int32_t status);
 
 /* Force the decode launch shape for subsequent decodes: split size in 16-token blocks and
- * waves per workgroup of the 16-row bf16 kernel (2); 0 keeps the automatic choice for each.
+ * waves per workgroup of the 16-row kernels (2; the FP8-cache kernel also 4, its default);
+ * 0 keeps the automatic choice for each.
  * For the 32-row bf16 kernel the split size is read as its workgroup count.
  * Any split size gives the same result up to fp32 summation order.  Returns MLA_EINVAL for a
  * negative split size or an unsupported wave count. */

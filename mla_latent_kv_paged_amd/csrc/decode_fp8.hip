@@ -15,23 +15,35 @@
 // How:
 //  * A paged block is 16 rows of 656 bytes = 10,496 contiguous bytes.  Each wave streams its blocks
 //    HBM -> LDS with global_load_lds_dwordx4 (11 transfers of 1 KB, the last one partly into padding)
-//    into a private ring of NS stages, NS - 1 blocks ahead.
-//  * Per block, the wave converts its stage into a bf16 tile in the layout of the bf16 kernel (8 x 8
-//    chunks of 16-byte granules): v_cvt_scalef32_pk_bf16_fp8 with scale 1 for the codes (exact),
-//    a copy for the rope granules, zeros for tokens past the visible range.  From there the scores
-//    (v_mfma_f32_16x16x32_bf16, A by ds_read_b128) and P.C (v_mfma_f32_16x16x16_bf16, A by
-//    ds_read_b64_tr_b16) run as in the bf16 kernel, with the group scales of the lane's four
-//    tokens read once per block.
-//  * Merge, normalisation and the fp16 partial store are those of the bf16 kernel.
+//    into a private ring of NS stages, NS - 1 blocks ahead.  A 16-byte piece of a token past the
+//    visible range is read from the zero block instead (rows are 41 pieces), so nothing stale or
+//    NaN reaches the arithmetic.
+//  * The codes are converted to bf16 in registers where they are consumed (exact), never staged:
+//    - score MFMA k (v_mfma_f32_16x16x32_bf16, tokens on M): lane (t = l%16, g = l/16) reads the 8
+//      codes of token t, channels 32k + 8g..+7, with one ds_read_b64 at a per-lane base + 32 k;
+//    - P.C (v_mfma_f32_16x16x16_bf16): one ds_read_b64_tr_b8 gives lane i of group g the codes of
+//      tokens 4g..4g+3 for channel 16p + i (lanes 0-7 of the group point at those tokens) and for
+//      channel 16p + 64 + i (lanes 8-15 point 64 bytes further): the A operands of channel tiles
+//      p and p + 4, both in the same scale group.  B = P^T times that group's scale, in bf16.
+//    The rope part (bf16 as stored) is read with ds_read_b128 for the last two score MFMAs.
+//  * Group scales: the four latent groups and the rope part accumulate separately; the lane's four
+//    tokens' scales (one ds_read_b128 each) weigh the groups in fp32.
+//  * NW waves (2 or 4) share one query tile and take every NW-th block of the split; at the end
+//    they merge through LDS (each wave finalises 32 / NW channel tiles), then normalise and store
+//    the fp16 partial rows as the bf16 kernel does.
 #include "mla_internal.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kTileBytes = BLK * ROW * 2;        // a bf16 tile of 16 rows x 576 (block or query tile)
+constexpr int kQTile = BLK * ROW * 2;            // bf16 query tile: 16 rows x 576
 constexpr int kStage8 = 11 * 1024;               // fp8 stage: one block (10,496 B) + transfer padding
+constexpr int kPieces = kFp8Row / 16;            // 41 sixteen-byte pieces per row
 constexpr float kMaxSlack = 8.f;                 // lazy-rescale slack, as in the bf16 kernel
+
+typedef int int2v_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) int2v_t lds_i32x2_t;
 
 __device__ __forceinline__ void wait_blocks8(int n) {  // at most n blocks (11 transfers each) in flight
   if (n <= 0)
@@ -44,16 +56,28 @@ __device__ __forceinline__ void wait_blocks8(int n) {  // at most n blocks (11 t
     wait_vmcnt<33>();
 }
 
+// e4m3 codes -> bf16, exactly (every e4m3 value is a bf16 value); byte k of w -> element k
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
+}
+__device__ __forceinline__ u32x4_t codes8(u32x2_t c) {
+  return u32x4_t{cvt2<false>(c[0]), cvt2<true>(c[0]), cvt2<false>(c[1]), cvt2<true>(c[1])};
+}
+__device__ __forceinline__ s16x4_t codes4(uint32_t c) {
+  return __builtin_bit_cast(s16x4_t, make_uint2(cvt2<false>(c), cvt2<true>(c)));
+}
+
 }  // namespace
 
 template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
-  static_assert(NW == 2, "the query tile is moved by two waves");
+  static_assert(NW == 2 || NW == 4, "two or four waves share a query tile");
   static_assert(NS >= 2 && NS <= 4, "a wave keeps at most 3 blocks in flight");
-  static_assert(NW * NS * kStage8 >= 32 * 64 * 16 + 16 * 1024, "the merge reuses the rings");
+  constexpr int TPW = 32 / NW;  // channel tiles each wave finalises
+  static_assert(NW * NS * kStage8 >= NW * 32 * 1024, "the merge reuses the rings");
   __shared__ __attribute__((aligned(16))) char ring_mem[NW * NS * kStage8];
-  __shared__ __attribute__((aligned(16))) char tile_mem[NW * kTileBytes];
-  __shared__ __attribute__((aligned(16))) char q_mem[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char q_mem[kQTile];
   __shared__ float m_lds[NW][16];
   __shared__ float l_lds[NW][16];
   __shared__ float x_lds[NW][16];
@@ -80,7 +104,6 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
   const char* cache = static_cast<const char*>(a.cache);
   const char* zero = static_cast<const char*>(a.zero_block);  // >= 10,496 zero bytes
   lds_char_t* const ring = (lds_char_t*)ring_mem + w * (NS * kStage8);
-  lds_char_t* const tile = (lds_char_t*)tile_mem + w * kTileBytes;
 
   // start-up as in the bf16 kernel: context length, block ids and query tile requested together
   const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
@@ -89,7 +112,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
   const int nid = in_row > 0 ? (in_row + NW - 1) / NW : 0;
   const int phys_lo = lane < nid ? bt[kb0 + w + NW * lane] : 0;
   const int phys_hi = lane + 64 < nid ? bt[kb0 + w + NW * (lane + 64)] : 0;
-  {  // query tile -> LDS: wave w moves rows 8w..8w+7
+  if (w < 2) {  // query tile -> LDS: wave w moves rows 8w..8w+7 (the bf16 kernel's stage layout)
     const char* src = static_cast<const char*>(a.qcat) + (int64_t(row) * a.H + h0 + 8 * w + lrow) * (ROW * 2) +
                       16 * lgr;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_char_t*)q_mem)));
@@ -116,15 +139,24 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
   const int span = kb1 - kb0 - w;
   const int nwb = span > 0 ? (span + NW - 1) / NW : 0;
 
-  // transfer of the wave's block i into ring stage i % NS: 10 full kilobytes, then 256 bytes (lanes
-  // 16..63 of the last transfer re-read the block's start into the stage padding)
+  // transfer of the wave's block i into ring stage i % NS: 16-byte piece pc of the block (token
+  // pc / 41) comes from the zero block when that token is past the visible range or the block id
+  // is out of range; 10 full kilobytes, then pieces 640..655 (lanes 16..63 fill stage padding)
   auto issue = [&](int i) {
+    const int kb = kb0 + w + NW * i;
     const int phys = phys_of(i);
-    const char* blk = unsigned(phys) < unsigned(a.num_blocks) ? cache + int64_t(phys) * kFp8Block : zero;
+    const bool ok = unsigned(phys) < unsigned(a.num_blocks);
+    const char* blk = cache + int64_t(ok ? phys : 0) * kFp8Block;
+    int vis = (L - kb * BLK) * kPieces;
+    vis = !ok ? 0 : vis > BLK * kPieces ? BLK * kPieces : vis;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(ring + (i % NS) * kStage8)));
 #pragma unroll
-    for (int k = 0; k < 10; ++k) dma16(blk + 1024 * k + 16 * lane, dst + 1024 * k);
-    dma16(blk + (lane < 16 ? 10240 : 0) + 16 * lane, dst + 10240);
+    for (int k = 0; k < 10; ++k) {
+      const int pc = 64 * k + lane;
+      dma16((pc < vis ? blk : zero) + 16 * pc, dst + 1024 * k);
+    }
+    const int pc = lane < 16 ? 640 + lane : lane;
+    dma16((pc < vis ? blk : zero) + 16 * pc, dst + 10240);
   };
 
   const int pre = nwb < NS - 1 ? nwb : NS - 1;
@@ -132,20 +164,19 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
   wait_blocks8(pre);  // the query transfers precede the blocks'
   lds_barrier();
 
-  const int sc_off = 9216 * (r16 >> 3) + 128 * g + 16 * (r16 & 7);
-  const int tr_off = 9216 * (g >> 1) + 64 * (g & 1) + 128 * ((r16 >> 1) & 1) + 16 * (r16 >> 2) + 8 * (r16 & 1);
-  u32x4_t qreg[18];
+  u32x4_t qreg[18];  // B operand of score MFMA k: row r16, channels 32k + 8g .. + 7
   {
-    const lds_u32x4_t* qp = (const lds_u32x4_t*)((lds_char_t*)q_mem + sc_off);
+    const int q_off = 9216 * (r16 >> 3) + 128 * g + 16 * (r16 & 7);
+    const lds_u32x4_t* qp = (const lds_u32x4_t*)((lds_char_t*)q_mem + q_off);
 #pragma unroll
     for (int k = 0; k < 18; ++k) qreg[k] = qp[32 * k];
   }
 
-  // conversion lane roles: token ct = lane % 16, granules c = lane / 16 + 4 e (e = 0..17) of the
-  // bf16 tile (granule c of token t at chunk 9 (t / 8) + c / 8, slot 8 (c % 8) + t % 8)
-  const int ct = lane & 15;
-  const int cw_off = 9216 * (ct >> 3) + 16 * (ct & 7);       // + 1024 (c / 8) + 128 (c % 8)
-  const int cr_off = kFp8Row * ct;                           // token ct's row in the fp8 stage
+  // per-lane offsets inside a stage
+  const int s_off = kFp8Row * r16 + 8 * g;  // scores: token r16, codes 32k + 8g .. + 7
+  const int r_off = kFp8Row * r16 + DC + 16 * g;  // rope: + 64 (k - 16)
+  const int t_off = kFp8Row * (4 * g + ((lane >> 1) & 3)) + 8 * (lane & 1) + 64 * ((lane >> 3) & 1);  // P.C
+  const int c_off = kFp8Row * (4 * g) + DC + 2 * DR;  // scales of tokens 4g .. 4g + 3
 
   f32x4_t acc[32];
 #pragma unroll
@@ -158,64 +189,32 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
     wait_blocks8(ahead);
     asm volatile("" ::: "memory");
     const int kb = kb0 + w + NW * i;
-    lds_char_t* const st8 = ring + (i % NS) * kStage8;
+    uint32_t sbase = uint32_t(uintptr_t(ring + (i % NS) * kStage8));
+    asm volatile("" : "+v"(sbase));  // one base per block; the offsets stay per-lane constants
+    lds_char_t* const st8 = (lds_char_t*)uintptr_t(sbase);
 
-    // fp8 stage -> bf16 tile (this wave's own); tokens past the visible range become zeros
-    {
-      const bool vis = kb * BLK + ct < L;
-      const lds_char_t* src = st8 + cr_off;
-#pragma unroll
-      for (int e = 0; e < 18; ++e) {
-        const int c = g + 4 * e;
-        u32x4_t v;
-        if (e < 16) {  // latent granule: 8 codes -> 8 bf16
-          const u32x2_t cw = *(const __attribute__((address_space(3))) u32x2_t*)(src + 8 * c);
-          v = u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[0], 1.f, false)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[0], 1.f, true)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[1], 1.f, false)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[1], 1.f, true))};
-        } else {       // rope granule: 8 bf16 as stored
-          v = *(const lds_u32x4_t*)(src + DC + 16 * (c - 64));
-        }
-        if (!vis) v = u32x4_t{0u, 0u, 0u, 0u};
-        *(__attribute__((address_space(3))) u32x4_t*)(tile + cw_off + 1024 * (c >> 3) + 128 * (c & 7)) = v;
-      }
-    }
-    // group scales of this lane's tokens 4g + r (zero past the visible range, like their codes)
-    f32x4_t scl[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      scl[r] = *(const __attribute__((address_space(3))) f32x4_t*)(st8 + kFp8Row * (4 * g + r) + DC + 2 * DR);
-      if (kb * BLK + 4 * g + r >= L) scl[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is written before it is read
-
-    // scores: four latent groups (MFMA k = 4G .. 4G+3) and the rope part (k = 16, 17) in separate
-    // accumulators; lane holds tokens 4g + r of row r16
-    const uint32_t tbase = uint32_t(uintptr_t(tile));
-    uint32_t spa = tbase + uint32_t(sc_off);
-    asm volatile("" : "+v"(spa));
-    const lds_u32x4_t* sp = (const lds_u32x4_t*)uintptr_t(spa);
+    // scores: latent groups G (MFMA k = 4G .. 4G+3) and the rope part (k = 16, 17) accumulate
+    // apart; lane holds tokens 4g + t of row r16
+    const u32x4_t rope0 = *(const lds_u32x4_t*)(st8 + r_off);
+    const u32x4_t rope1 = *(const lds_u32x4_t*)(st8 + r_off + 64);
     constexpr int D = 4;
-    u32x4_t rg[D];
+    u32x2_t cg[D];
 #pragma unroll
-    for (int k = 0; k < D; ++k) rg[k] = sp[32 * k];
+    for (int k = 0; k < D; ++k) cg[k] = *(const lds_u32x2_t*)(st8 + s_off + 32 * k);
     f32x4_t scg[5];
 #pragma unroll
     for (int G = 0; G < 5; ++G) scg[G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 18; ++k) {
-      const u32x4_t x = rg[k % D];
-      if (k + D < 18) rg[k % D] = sp[32 * (k + D)];
+    for (int k = 0; k < 16; ++k) {
+      const u32x4_t x = codes8(cg[k % D]);
+      if (k + D < 16) cg[k % D] = *(const lds_u32x2_t*)(st8 + s_off + 32 * (k + D));
       scg[k >> 2] = mfma32v(x, qreg[k], scg[k >> 2]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+    scg[4] = mfma32v(rope0, qreg[16], scg[4]);
+    scg[4] = mfma32v(rope1, qreg[17], scg[4]);
+    f32x4_t scl[4];  // group scales of tokens 4g + t (zero past the visible range, as their codes)
 #pragma unroll
-    for (int k = 0; k < 18 - D; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+    for (int t = 0; t < 4; ++t) scl[t] = *(const __attribute__((address_space(3))) f32x4_t*)(st8 + c_off + kFp8Row * t);
     float sv[4];
     float mb = -INFINITY;
 #pragma unroll
@@ -240,38 +239,33 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = sv[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[t] - m);
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    s16x4_t pb[4];  // P of the lane's tokens times their group-G scale, as the B operand
+    s16x4_t pb[4];  // B operand: P of the lane's tokens times their group-G scale
 #pragma unroll
     for (int G = 0; G < 4; ++G)
       pb[G] = __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(p[0] * scl[0][G], p[1] * scl[1][G]),
                                                      cvt_pk_bf16(p[2] * scl[2][G], p[3] * scl[3][G])));
 
-    // P.C: channel tile jj (group jj / 8) by transposed LDS read of the bf16 tile
-    uint32_t tpa = tbase + uint32_t(tr_off);
-    asm volatile("" : "+v"(tpa));
-    lds_char_t* tp = (lds_char_t*)uintptr_t(tpa);
-    constexpr int DT = 8;
-    s16x4_t tv[DT];
+    // P.C: read q (q = 0..15) covers channel tiles p = 8 (q / 4) + q % 4 and p + 4 (group q / 4)
+    constexpr int DT = 4;
+    int2v_t tv[DT];
+    auto tread = [&](int q) {
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(st8 + t_off + 128 * (q >> 2) + 16 * (q & 3)));
+    };
 #pragma unroll
-    for (int jj = 0; jj < DT; ++jj) tv[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tp + 256 * jj));
+    for (int q = 0; q < DT; ++q) tv[q] = tread(q);
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) {
-      const s16x4_t av = tv[jj % DT];
-      if (jj + DT < 32)
-        tv[jj % DT] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tp + 256 * (jj + DT)));
-      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb[jj >> 3], acc[jj], 0, 0, 0);
+    for (int q = 0; q < 16; ++q) {
+      const int2v_t v = tv[q % DT];
+      if (q + DT < 16) tv[q % DT] = tread(q + DT);
+      const int pt = 8 * (q >> 2) + (q & 3);
+      acc[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(codes4(uint32_t(v[0])), pb[q >> 2], acc[pt], 0, 0, 0);
+      acc[pt + 4] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(codes4(uint32_t(v[1])), pb[q >> 2], acc[pt + 4], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);
-#pragma unroll
-    for (int jj = 0; jj < 32 - DT; ++jj) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // tile and stage reads done before reuse
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage reads done before its reuse
   }
 
-  // merge of the two waves and the fp16 partial store, as in the bf16 kernel
+  // merge of the waves: every wave leaves its 32 tiles in the rings, wave w sums tiles
+  // TPW w .. TPW w + TPW - 1 over the waves in wave order
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (g == 0) {
@@ -289,64 +283,67 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
     if (mw != -INFINITY) Ltot += __builtin_amdgcn_exp2f(mw - M) * l_lds[ww][r16];
   }
   const float sw = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  f32x4_t* slots = reinterpret_cast<f32x4_t*>(ring_mem);  // slot (wave, tile): 1 KB
 #pragma unroll
-  for (int jj = 0; jj < 32; ++jj) acc[jj] *= sw;
-
-  f32x4_t* slots = reinterpret_cast<f32x4_t*>(ring_mem);  // region r = tiles 16r..16r+15
-  if (w == 0) {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) slots[(16 + t) * 64 + lane] = acc[16 + t];
-  } else {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) slots[t * 64 + lane] = acc[t];
-  }
+  for (int t = 0; t < 32; ++t) slots[(w * 32 + t) * 64 + lane] = acc[t] * sw;
   __syncthreads();
-  f32x4_t fin[16];
-  if (w == 0) {
+  f32x4_t fin[TPW];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) fin[t] = acc[t] + slots[t * 64 + lane];
-  } else {
+  for (int t = 0; t < TPW; ++t) {
+    fin[t] = slots[(TPW * w + t) * 64 + lane];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) fin[t] = slots[(16 + t) * 64 + lane] + acc[16 + t];
+    for (int ww = 1; ww < NW; ++ww) fin[t] += slots[(ww * 32 + TPW * w + t) * 64 + lane];
   }
   float mx = 0.f;
 #pragma unroll
-  for (int t = 0; t < 16; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(fin[t][e]));
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   if (g == 0) x_lds[w][r16] = mx;
   __syncthreads();
+  float rmx = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) rmx = fmaxf(rmx, x_lds[ww][r16]);
   const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
-  const float down = fp16_fit_scale(fmaxf(x_lds[0][r16], x_lds[1][r16]) * inv);
+  const float down = fp16_fit_scale(rmx * inv);
   const float sc = inv * down;
-  lds_char_t* const otile = (lds_char_t*)ring_mem + 32 * 64 * 16;
-  auto put = [&](int jj, f32x4_t v) {
-    v *= sc;
-    const int G = 2 * jj + (g >> 1);
+  lds_char_t* const otile = (lds_char_t*)q_mem;  // 16 rows x 1 KB of fp16, granules swizzled by row
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const f32x4_t v = fin[t] * sc;
+    const int G = 2 * (TPW * w + t) + (g >> 1);
     *(lds_u32x2_t*)(otile + r16 * 1024 + 16 * (G ^ r16) + 8 * (g & 1)) =
         u32x2_t{cvt_pk_f16(v[0], v[1]), cvt_pk_f16(v[2], v[3])};
-  };
-#pragma unroll
-  for (int t = 0; t < 16; ++t) put(16 * w + t, fin[t]);
+  }
   __syncthreads();
-  const int64_t pidx = (int64_t(row) * a.H + h0 + r16) * a.n_split + j;
+  constexpr int RPW = 16 / NW;
 #pragma unroll
-  for (int r = 8 * w; r < 8 * w + 8; ++r) {
+  for (int r = RPW * w; r < RPW * w + RPW; ++r) {
     const int64_t pr = (int64_t(row) * a.H + h0 + r) * a.n_split + j;
     *reinterpret_cast<u32x4_t*>(a.part_o16 + pr * DC + 8 * lane) =
         *(const lds_u32x4_t*)(otile + r * 1024 + 16 * (lane ^ r));
   }
   if (w == 0 && g == 0) {
+    const int64_t pidx = (int64_t(row) * a.H + h0 + r16) * a.n_split + j;
     a.part_ml[pidx] = make_float2(M, Ltot);
     a.part_scale[pidx] = 1.f / down;
   }
 }
 
-hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s) {
   const int grid = ((a.units + 7) >> 3) << 3;
-  decode_fp8_kernel<2, 4><<<grid, 128, 0, s>>>(a);
+  switch (waves) {
+    case 2:
+      decode_fp8_kernel<2, 4><<<grid, 128, 0, s>>>(a);
+      break;
+    case 4:
+      decode_fp8_kernel<4, 3><<<grid, 256, 0, s>>>(a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

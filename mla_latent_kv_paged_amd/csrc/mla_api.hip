@@ -309,7 +309,11 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   // (FP8 cache rows: the 16-row FP8 kernel for every shape)
   const int t32 = (ctx->bf16 && !ctx->fp8 && n_rt32 > 0) ? ((n_rt32 % 4 == 0) ? 4 : (n_rt32 % 2 == 0) ? 2 : 1) : 0;
   const int n_rt = t32 ? n_rt32 : n_rt16;
-  const int waves = ctx->bf16 ? (t32 ? t32 : (ctx->forced_waves > 0 ? ctx->forced_waves : 2)) : 1;
+  const int waves = !ctx->bf16 ? 1
+                    : t32         ? t32
+                    : ctx->forced_waves > 0 ? ctx->forced_waves
+                    : ctx->fp8    ? 4
+                                  : 2;
   const int groups = t32 ? n_rt / t32 : n_rt;  // workgroups per (sequence, split)
   int sb = 0, n_split = 0, n_wg = 0;
   if (t32) {
@@ -348,7 +352,7 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
                   reinterpret_cast<uint16_t*>(ctx->part_acc), ctx->part_ml, ctx->part_scale, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
                   ctx->piece_tbl};
     ProfScope ps(ctx, MLA_K_DECODE, s);
-    e = t32 ? launch_decode_mt32(da, t32, s) : ctx->fp8 ? launch_decode_fp8(da, s) : launch_decode(ctx->bf16, da, waves, s);
+    e = t32 ? launch_decode_mt32(da, t32, s) : ctx->fp8 ? launch_decode_fp8(da, waves, s) : launch_decode(ctx->bf16, da, waves, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {
@@ -371,7 +375,8 @@ void mla_free(mla_ctx* ctx) {
 
 mla_status mla_set_decode_tuning(mla_ctx* ctx, int32_t split_blocks, int32_t waves_per_group) {
   if (!ctx || split_blocks < 0) return MLA_EINVAL;
-  if (waves_per_group != 0 && waves_per_group != 2)
+  // 2 for every 16-row kernel; 4 for the FP8 one only
+  if (waves_per_group != 0 && waves_per_group != 2 && !(waves_per_group == 4 && ctx->fp8))
     return MLA_EINVAL;
   ctx->forced_split_blocks = split_blocks;
   ctx->forced_waves = waves_per_group;

@@ -120,7 +120,7 @@ hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s);
 hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 // FP8 cache rows (kFp8Row bytes), 16-row tiles; every H multiple of 16 and every q_len
-hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s);
 // bf16, 32-row tiles (H*q_len a multiple of 32), T in {1, 2, 4} tiles per workgroup; n_rt = tiles of
 // 32 rows per sequence (a multiple of T); units = workgroups, enough that every workgroup's share
 // is at most kMt32MaxSteps steps of two blocks

@@ -55,12 +55,12 @@ class Fp8Run:
         self.bt = dev_i32(w.block_table)
         self.sl = dev_i32(w.seq_lens)
 
-    def decode(self, split_blocks=None):
-        if split_blocks is not None:
-            self.ctx.set_decode_tuning(split_blocks, 0)
+    def decode(self, split_blocks=None, waves=0):
+        if split_blocks is not None or waves:
+            self.ctx.set_decode_tuning(split_blocks or 0, waves)
         out = self.ctx.decode(self.q, self.pool, self.bt, self.sl, self.max_ctx, q_len=self.w.q_len)
         torch.cuda.synchronize()
-        if split_blocks is not None:
+        if split_blocks is not None or waves:
             self.ctx.set_decode_tuning(0, 0)
         return out
 
@@ -141,8 +141,10 @@ def test_fp8_cache_and_decode(name, make):
         ref = O.decode_absorbed(w.queries(), deq, w.block_table, w.seq_lens, w.q_len, W_uk, W_uv, w.scale, w.theta)
         out = run.decode()
         compare(out, ref, "bf16", f"fp8 {name}")
-        for sb in (1, 3):  # short splits: many partials per row, the empty-split markers
-            compare(run.decode(split_blocks=sb), ref, "bf16", f"fp8 {name} split {sb}")
+        for sb in (1, 3, 5):  # short splits: many partials per row, the empty-split markers
+            for waves in (2, 4):  # waves sharing a query tile (4 is the default)
+                compare(run.decode(split_blocks=sb, waves=waves), ref, "bf16", f"fp8 {name} split {sb} waves {waves}")
+        compare(run.decode(waves=2), ref, "bf16", f"fp8 {name} waves 2")
         out2 = run.decode()
         assert torch.equal(out, out2), "fp8 decode is not deterministic"
     finally:
