@@ -40,7 +40,7 @@ namespace {
 constexpr int kQTile = BLK * ROW * 2;            // bf16 query tile: 16 rows x 576
 constexpr int kStage8 = 11 * 1024;               // fp8 stage: one block (10,496 B) + transfer padding
 constexpr int kPieces = kFp8Row / 16;            // 41 sixteen-byte pieces per row
-constexpr float kMaxSlack = 8.f;                 // lazy-rescale slack, as in the bf16 kernel
+constexpr float kMaxSlack = 32.f;                // lazy-rescale slack (log2 units): P <= 2^32
 
 typedef int int2v_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) int2v_t lds_i32x2_t;
@@ -67,6 +67,29 @@ __device__ __forceinline__ u32x4_t codes8(u32x2_t c) {
 __device__ __forceinline__ s16x4_t codes4(uint32_t c) {
   return __builtin_bit_cast(s16x4_t, make_uint2(cvt2<false>(c), cvt2<true>(c)));
 }
+
+// P.C step on one accumulator tile pinned in AGPRs: with the builtin, the register allocator moves
+// all 32 tiles through VGPRs once per block.  The compiler does not see an MFMA here, so the wait
+// states are provided explicitly: s_nop 2 after the VALU that writes the A/B operands; a tile is
+// used again 31 MFMAs later at the earliest; VALU access to the tiles follows mfma_drain().
+__device__ __forceinline__ void mfma16_acc(f32x4_t& acc, s16x4_t a, s16x4_t b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// acc *= f for a tile in AGPRs, element by element inside the caller's block (a plain multiply
+// lets the allocator keep VGPR copies of every tile, refreshed once per block)
+__device__ __forceinline__ void acc_scale(f32x4_t& acc, float f) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x, y;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[e]));
+    x *= f;
+    asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(y) : "v"(x));
+    acc[e] = y;
+  }
+  asm volatile("" : "+a"(acc));
+}
+// wait states after the last asm MFMA before VALU touches its accumulator (more than the 19 of a 16-pass MFMA)
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 }  // namespace
 
@@ -150,13 +173,19 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
     int vis = (L - kb * BLK) * kPieces;
     vis = !ok ? 0 : vis > BLK * kPieces ? BLK * kPieces : vis;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(ring + (i % NS) * kStage8)));
+    const int pc_last = lane < 16 ? 640 + lane : lane;
+    if (vis == BLK * kPieces) {  // the common case: the whole block is visible
 #pragma unroll
-    for (int k = 0; k < 10; ++k) {
-      const int pc = 64 * k + lane;
-      dma16((pc < vis ? blk : zero) + 16 * pc, dst + 1024 * k);
+      for (int k = 0; k < 10; ++k) dma16(blk + 16 * (64 * k + lane), dst + 1024 * k);
+      dma16(blk + 16 * pc_last, dst + 10240);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 10; ++k) {
+        const int pc = 64 * k + lane;
+        dma16((pc < vis ? blk : zero) + 16 * pc, dst + 1024 * k);
+      }
+      dma16((pc_last < vis ? blk : zero) + 16 * pc_last, dst + 10240);
     }
-    const int pc = lane < 16 ? 640 + lane : lane;
-    dma16((pc < vis ? blk : zero) + 16 * pc, dst + 10240);
   };
 
   const int pre = nwb < NS - 1 ? nwb : NS - 1;
@@ -180,7 +209,10 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
 
   f32x4_t acc[32];
 #pragma unroll
-  for (int jj = 0; jj < 32; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int jj = 0; jj < 32; ++jj) {
+    acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    asm volatile("" : "+a"(acc[jj]));
+  }
   float m = -INFINITY, lsum = 0.f;
 
   for (int i = 0; i < nwb; ++i) {
@@ -195,44 +227,50 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
 
     // scores: latent groups G (MFMA k = 4G .. 4G+3) and the rope part (k = 16, 17) accumulate
     // apart; lane holds tokens 4g + t of row r16
+    // MFMA n takes channels 32 k, k = 4 (n % 4) + n / 4: consecutive MFMAs feed different groups
     const u32x4_t rope0 = *(const lds_u32x4_t*)(st8 + r_off);
     const u32x4_t rope1 = *(const lds_u32x4_t*)(st8 + r_off + 64);
     constexpr int D = 4;
+    auto kof = [](int n) { return 4 * (n & 3) + (n >> 2); };
     u32x2_t cg[D];
 #pragma unroll
-    for (int k = 0; k < D; ++k) cg[k] = *(const lds_u32x2_t*)(st8 + s_off + 32 * k);
+    for (int n = 0; n < D; ++n) cg[n] = *(const lds_u32x2_t*)(st8 + s_off + 32 * kof(n));
     f32x4_t scg[5];
 #pragma unroll
     for (int G = 0; G < 5; ++G) scg[G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const u32x4_t x = codes8(cg[k % D]);
-      if (k + D < 16) cg[k % D] = *(const lds_u32x2_t*)(st8 + s_off + 32 * (k + D));
-      scg[k >> 2] = mfma32v(x, qreg[k], scg[k >> 2]);
-    }
     scg[4] = mfma32v(rope0, qreg[16], scg[4]);
-    scg[4] = mfma32v(rope1, qreg[17], scg[4]);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int k = kof(n);
+      const u32x4_t x = codes8(cg[n % D]);
+      if (n + D < 16) cg[n % D] = *(const lds_u32x2_t*)(st8 + s_off + 32 * kof(n + D));
+      scg[k >> 2] = mfma32v(x, qreg[k], scg[k >> 2]);
+      if (n == 7) scg[4] = mfma32v(rope1, qreg[17], scg[4]);
+    }
     f32x4_t scl[4];  // group scales of tokens 4g + t (zero past the visible range, as their codes)
 #pragma unroll
     for (int t = 0; t < 4; ++t) scl[t] = *(const __attribute__((address_space(3))) f32x4_t*)(st8 + c_off + kFp8Row * t);
     float sv[4];
-    float mb = -INFINITY;
+    float ml = -INFINITY;  // this lane's max; m is the same in the four lanes of a row
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float s = scg[4][t];
 #pragma unroll
       for (int G = 0; G < 4; ++G) s = fmaf(scl[t][G], scg[G][t], s);
       sv[t] = (kb * BLK + 4 * g + t < L) ? s : -INFINITY;
-      mb = fmaxf(mb, sv[t]);
+      ml = fmaxf(ml, sv[t]);
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    if (__any(mb > m + kMaxSlack)) {
+    if (__any(ml > m + kMaxSlack)) {  // rare: a score rose by more than the slack above m
+      float mb = fmaxf(ml, __shfl_xor(ml, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
       const float mn = fmaxf(m, mb);
-      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-      lsum *= alpha;
+      if (!__all(m == -INFINITY)) {  // something accumulated: rescale it to the new reference
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        lsum *= alpha;
+        mfma_drain();
 #pragma unroll
-      for (int jj = 0; jj < 32; ++jj) acc[jj] *= alpha;
+        for (int jj = 0; jj < 32; ++jj) acc_scale(acc[jj], alpha);
+      }
       m = mn;
     }
     float p[4];
@@ -258,14 +296,15 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
       const int2v_t v = tv[q % DT];
       if (q + DT < 16) tv[q % DT] = tread(q + DT);
       const int pt = 8 * (q >> 2) + (q & 3);
-      acc[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(codes4(uint32_t(v[0])), pb[q >> 2], acc[pt], 0, 0, 0);
-      acc[pt + 4] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(codes4(uint32_t(v[1])), pb[q >> 2], acc[pt + 4], 0, 0, 0);
+      mfma16_acc(acc[pt], codes4(uint32_t(v[0])), pb[q >> 2]);
+      mfma16_acc(acc[pt + 4], codes4(uint32_t(v[1])), pb[q >> 2]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage reads done before its reuse
   }
 
   // merge of the waves: every wave leaves its 32 tiles in the rings, wave w sums tiles
   // TPW w .. TPW w + TPW - 1 over the waves in wave order
+  mfma_drain();
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (g == 0) {

@@ -169,3 +169,45 @@ def test_fp8_quantisation_error_is_bounded():
         assert rel <= 2.0 ** -4
     finally:
         run.free()
+
+
+def _fp8_pool_from_values(w, pool):
+    """FP8 byte pool holding the live rows of a float32 value pool (quantised by the oracle's
+    format code); every other row is 0xFF bytes (NaN codes, NaN rope values, NaN scales), so a
+    kernel that reads a row it should not see yields NaN."""
+    out = np.full((w.n_blocks, 16, 1, F.ROW_BYTES), 0xFF, dtype=np.uint8)
+    for b in range(w.batch):
+        for t in range(int(w.seq_lens[b])):
+            blk, off = int(w.block_table[b, t // 16]), t % 16
+            v = pool[blk, off, 0].astype(np.float64)
+            codes, scales = F.quantize_latent(v[:512])
+            out[blk, off, 0] = F.pack_row(codes, v[512:], scales)
+    return out
+
+
+@pytest.mark.parametrize("heads,q_len", [(16, 1), (16, 2)])
+def test_fp8_score_climb(heads, q_len):
+    """The steadily climbing scores of the bf16 test (test_gpu_parity.climb_case) over an FP8
+    cache, with both wave counts and the longest splits, against the oracle on the dequantised
+    bytes; the rows past each sequence's end are NaN bytes."""
+    from mla_latent_kv_paged_amd import MLAContext
+    from .test_gpu_parity import climb_case, climb_rows
+    w, q, kvb, pool = climb_case(heads, q_len, seed=82)
+    _say("fp8 score climb", "H", heads, "q_len", q_len)
+    pool8 = _fp8_pool_from_values(w, pool)
+    deq = F.dequantize_cache(pool8)
+    assert climb_rows(w, q, kvb, deq.astype(np.float32)) >= heads
+    W_uk, W_uv = O.absorb(kvb.astype(np.float64), heads, 128, 128)
+    ref = O.decode_absorbed(q, deq, w.block_table, w.seq_lens, w.q_len, W_uk, W_uv, w.scale, w.theta)
+    mx = int(w.seq_lens.max())
+    ctx = MLAContext(dev(kvb, "bf16"), None, num_heads=heads, dtype="fp8", rms_eps=w.eps, rope_theta=w.theta,
+                     max_q_tokens=w.n_q, max_batch=w.batch, max_position=mx + 16, max_seq_len=mx + 16)
+    try:
+        dpool = torch.from_numpy(pool8).to("cuda")
+        for sb, waves in ((0, 0), (160, 4), (160, 2), (3, 4)):
+            ctx.set_decode_tuning(sb, waves)
+            out = ctx.decode(dev(q, "bf16"), dpool, dev_i32(w.block_table), dev_i32(w.seq_lens), mx, q_len=w.q_len)
+            torch.cuda.synchronize()
+            compare(out, ref, "bf16", f"fp8 score climb H={heads} q_len={q_len} split={sb} waves={waves}")
+    finally:
+        ctx.free()
