@@ -16,8 +16,9 @@
 //    base plus immediate offsets (score operand k at + 256 k) and run at the LDS's full rate.
 //  * Scores S^T[32 tok x 32 rows] = C Q^T on v_mfma_f32_32x32x16_bf16: A = chunk k as read, B = the
 //    query tile's granules 2k, 2k+1.  Lane l then holds row l%32 at tokens 8(r/4) + 4(l/32) + r%4.
-//  * Causal mask per row; softmax against a per-row reference max that moves only by more than 64
-//    (log2 units), exp2; P is at most 2^64, well inside bf16 and fp32.
+//  * Causal mask per row; softmax against a per-row reference max that moves only when a score
+//    exceeds it by more than 64 (log2 units), exp2; P is at most 2^64, well inside bf16 and fp32.
+//    When it moves, what was accumulated is rescaled to the new reference.
 //  * P.C: acc^T[32 ch x 32 rows] += C^T[32 ch x 16 tok] P^T[16 tok x 32 rows], two K steps of 16
 //    tokens per step.  The K order inside a step is {4h..4h+3, 8+4h..8+4h+3} for lane half h, which
 //    is exactly the order in which the score registers hold P, so B is the score registers rounded
@@ -223,15 +224,18 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
     }
     float m = -INFINITY, lsum = 0.f;
 
-    // reference-max update for a step with row max mb: returns whether the row restarts with
-    // accumulated terms (its accumulator must then be cleared); sets m, lsum and the exponent base
-    auto ref_update = [&](float mb, float& msub) {
+    // reference-max update for a step with row max mb: returns whether the row's reference moves
+    // with terms accumulated (they must then be scaled by alpha = 2^(m_old - m_new): the latest of
+    // them may sit just below the new maximum, so they are rescaled, never dropped); sets m, lsum,
+    // alpha and the exponent base
+    auto ref_update = [&](float mb, float& msub, float& alpha) {
       const bool upd = mb > m + kReset;
-      const bool rst = upd && m != -INFINITY;
+      const bool rsc = upd && m != -INFINITY;
+      alpha = rsc ? __builtin_amdgcn_exp2f(m - mb) : 1.f;
+      lsum *= alpha;
       m = upd ? mb : m;
-      lsum = upd ? 0.f : lsum;
       msub = m == -INFINITY ? 0.f : m;  // a row with nothing visible yet: every p is exp2(-inf) = 0
-      return rst;
+      return rsc;
     };
 
     // scores of step i: S^T on v_mfma_f32_32x32x16_bf16, operand reads kept D ahead of the MFMAs;
@@ -287,17 +291,12 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       float t1 = fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]));
       float t2 = fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11]));
       float t3 = fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]));
-      float msub;
-      const bool rst = ref_update(row_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3))), msub);
-      if (__any(rst)) {  // the row restarts: everything accumulated so far is dropped
+      float msub, alpha;
+      const bool rsc = ref_update(row_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3))), msub, alpha);
+      if (__any(rsc)) {  // rare: a reference moved (rows whose reference stayed have alpha = 1)
         mfma_drain();
-        if (rst) {
 #pragma unroll
-          for (int jt = 0; jt < 16; ++jt) {
-            acc[jt] = f32x16_t{};
-            asm volatile("" : "+a"(acc[jt]));
-          }
-        }
+        for (int jt = 0; jt < 16; ++jt) acc_scale<f32x16_t, 16>(acc[jt], alpha);
       }
       uint32_t pw[8];
 #pragma unroll

@@ -75,19 +75,6 @@ __device__ __forceinline__ s16x4_t codes4(uint32_t c) {
 __device__ __forceinline__ void mfma16_acc(f32x4_t& acc, s16x4_t a, s16x4_t b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-// acc *= f for a tile in AGPRs, element by element inside the caller's block (a plain multiply
-// lets the allocator keep VGPR copies of every tile, refreshed once per block)
-__device__ __forceinline__ void acc_scale(f32x4_t& acc, float f) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float x, y;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[e]));
-    x *= f;
-    asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(y) : "v"(x));
-    acc[e] = y;
-  }
-  asm volatile("" : "+a"(acc));
-}
 // wait states after the last asm MFMA before VALU touches its accumulator (more than the 19 of a 16-pass MFMA)
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
@@ -269,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
         lsum *= alpha;
         mfma_drain();
 #pragma unroll
-        for (int jj = 0; jj < 32; ++jj) acc_scale(acc[jj], alpha);
+        for (int jj = 0; jj < 32; ++jj) acc_scale<f32x4_t, 4>(acc[jj], alpha);
       }
       m = mn;
     }

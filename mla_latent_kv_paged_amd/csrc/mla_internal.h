@@ -230,4 +230,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier ordering LDS only (the wave's own LDS accesses are complete when it arrives).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+
+// acc *= f for an accumulator vector held in AGPRs, element by element where it is called (a plain
+// multiply lets the register allocator keep a VGPR copy of every tile, refreshed each iteration).
+// The caller drains in-flight MFMAs that write acc before calling.
+template <typename V, int N>
+__device__ __forceinline__ void acc_scale(V& acc, float f) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    float x = acc[e], t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(t)
+                 : "v"(f));
+    acc[e] = x;
+  }
+  asm volatile("" : "+a"(acc));
+}
 }  // namespace mla

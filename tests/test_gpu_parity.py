@@ -179,6 +179,83 @@ def test_large_score_jump(heads, q_len):
         run.free()
 
 
+CLIMB_LOG2 = 72.0  # rise of every row's score over its sequence (log2 units)
+
+
+def climb_case(heads, q_len, seed):
+    """Inputs whose scores climb steadily along each sequence, by CLIMB_LOG2 in log2 units: latent
+    channel 0 of token t holds A t / (ctx - 1) and every query reads it with weight kappa (q_nope
+    component 0 is 1, W_uk row 0 is kappa e_0), on top of the usual random scores.  W_uv column 0
+    is zero, so channel 0 steers the softmax but adds nothing to the output.
+
+    A row's running max then rises past any fixed headroom above its first blocks while the terms
+    just below it still carry most of the weight: a kernel may rescale what it has accumulated or
+    drop it only where it is negligible.  Only one channel carries the climb, so the kernels' bf16
+    rounding of the scaled query moves score differences by at most 2^-9 relative: the case is
+    well conditioned.  Returns (workload, queries, kv_b_proj, pool) as float32 storage values."""
+    w = W.custom("climb", "bf16", heads, [300, 1000, 2500], q_len=q_len, seed=seed)
+    kappa = 4.0
+    amp = CLIMB_LOG2 / (kappa * w.scale / np.log(2.0))
+    q = w.queries().copy()
+    q[:, :, 0] = 1.0
+    kvb = w.kv_b_proj().reshape(heads, 256, 512).copy()
+    kvb[:, 0, :] = 0.0
+    kvb[:, 0, 0] = kappa
+    kvb[:, 128:, 0] = 0.0
+    kvb = kvb.reshape(heads * 256, 512)
+    pool = w.random_pool()
+    for b in range(w.batch):
+        ctx = int(w.seq_lens[b])
+        t = np.arange(ctx)
+        vals = W.bf16_bits_to_f32(W.f32_to_bf16_bits((amp * t / (ctx - 1)).astype(np.float32)))
+        pool[w.block_table[b, t // 16], t % 16, 0, 0] = vals
+    return w, q, kvb, pool
+
+
+def climb_rows(w, q, kvb, pool):
+    """Rows whose score max rises by more than 64 log2 units above their first two blocks (the
+    pattern the case is built for), from the fp64 oracle's scores."""
+    W_uk, _ = O.absorb(kvb.astype(np.float64), w.num_heads, 128, 128)
+    pool64 = pool.astype(np.float64)
+    n = 0
+    log2e = 1.0 / np.log(2.0)
+    for b in range(w.batch):
+        ctx = int(w.seq_lens[b])
+        C, R = O.gather_sequence(pool64, w.block_table[b], ctx, 512)
+        pos, row = ctx - 1, b * w.q_len + w.q_len - 1
+        for h in range(w.num_heads):
+            s2 = O._absorbed_scores(q[row, h].astype(np.float64), C, R, W_uk[h], pos, w.scale, w.theta)[:pos + 1]
+            s2 = s2 * log2e
+            n += np.max(s2) - np.max(s2[:32]) > 64.0
+    return n
+
+
+@pytest.mark.parametrize("heads,q_len", [(16, 1), (32, 1), (16, 2), (128, 1)])
+def test_score_climb(heads, q_len):
+    """Steadily climbing scores (climb_case): one case per bf16 decode kernel shape (16 rows; 32
+    rows with one and with four tiles per workgroup), at the library's split and at the longest
+    ranges the tuning allows, against the fp64 oracle on every row."""
+    from mla_latent_kv_paged_amd import MLAContext
+    w, q, kvb, pool = climb_case(heads, q_len, seed=81)
+    _say("score climb", "H", heads, "q_len", q_len)
+    assert climb_rows(w, q, kvb, pool) >= heads  # most rows of every sequence climb past 64
+    W_uk, W_uv = O.absorb(kvb.astype(np.float64), heads, 128, 128)
+    ref = O.decode_absorbed(q, pool.astype(np.float64), w.block_table, w.seq_lens, w.q_len, W_uk, W_uv, w.scale,
+                            w.theta)
+    mx = int(w.seq_lens.max())
+    ctx = MLAContext(dev(kvb, "bf16"), None, num_heads=heads, dtype="bf16", rms_eps=w.eps, rope_theta=w.theta,
+                     max_q_tokens=w.n_q, max_batch=w.batch, max_position=mx + 16, max_seq_len=mx + 16)
+    try:
+        for sb in (0, 1, 160):  # library choice; fewest 32-row workgroups; longest 16-row splits
+            ctx.set_decode_tuning(sb, 0)
+            out = ctx.decode(dev(q, "bf16"), dev(pool, "bf16"), dev_i32(w.block_table), dev_i32(w.seq_lens), mx,
+                             q_len=w.q_len)
+            torch.cuda.synchronize()
+            compare(out, ref, "bf16", f"score climb H={heads} q_len={q_len} tuning={sb}")
+    finally:
+        ctx.free()
+
+
 @pytest.mark.parametrize("storage,heads,q_len", [("bf16", 16, 2), ("f32", 16, 2), ("bf16", 128, 1), ("bf16", 16, 4)])
 def test_split_sweep_and_determinism(storage, heads, q_len):
     """Every split size from one block to the whole context (odd sizes end a two-block step past
