@@ -270,6 +270,44 @@ def decode_naive(q, cache, block_table, seq_lens, q_len, W_uk, W_uv, scale, thet
     return out
 
 
+def prefill_naive(q, cu_q_lens, cache, block_table, seq_lens, W_uk, W_uv, scale, theta):
+    """Chunked prefill in the naive form: K = [C W_uk^T | R] and V = C W_uv^T expanded once per
+    sequence and head ([P-mini] MLA 的数学结构 and 版本 1), causal softmax attention of every new
+    token over the cache ([P-mini] 踩坑记录 坑 2).
+
+    Sequence b owns query rows cu_q_lens[b] .. cu_q_lens[b+1]-1: its n_b new tokens, at positions
+    ctx_b - n_b .. ctx_b - 1, whose rows are already in the cache (as for the decode).  Row i of the
+    chunk sees cache tokens t <= its position.  Same inputs and output layout as decode_naive, with
+    per-sequence chunk lengths instead of one q_len.
+
+    q          : [total_q, H, dn + dr] un-rotated queries
+    cu_q_lens  : [B + 1] prefix sums of the chunk lengths
+    seq_lens   : [B] context length ctx_b including the chunk
+    returns    : [total_q, H, dv] float64
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H, dn, dc = W_uk.shape
+    dv = W_uv.shape[1]
+    cu = np.asarray(cu_q_lens, dtype=np.int64)
+    out = np.zeros((int(cu[-1]), H, dv), dtype=np.float64)
+    for b in range(len(seq_lens)):
+        ctx = int(seq_lens[b])
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        n = r1 - r0
+        if n == 0:
+            continue
+        C, R = gather_sequence(cache, block_table[b], ctx, dc)
+        pos = query_positions(ctx, n)                                   # [n]
+        vis = np.arange(ctx)[None, :] <= pos[:, None]                   # [n, ctx]
+        for h in range(H):
+            K = np.concatenate([C @ W_uk[h].T, R], axis=1)              # [ctx, dn + dr]
+            V = C @ W_uv[h].T                                           # [ctx, dv]
+            Q = np.concatenate([q[r0:r1, h, :dn], rope(q[r0:r1, h, dn:], pos, theta)], axis=1)
+            S = np.where(vis, scale * (Q @ K.T), -np.inf)                # [n, ctx]
+            out[r0:r1, h] = softmax(S) @ V
+    return out
+
+
 # ----------------------------------------------------------------------------------------------
 # Decode, absorbed form ([P-mini] 版本 3 reassociated; 设计取舍 two-part score)
 # ----------------------------------------------------------------------------------------------

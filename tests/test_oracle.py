@@ -378,3 +378,78 @@ def test_relative_position_shift_of_whole_sequence():
         outs.append(out)
     # the rotated k_pe rows are stored as fp32 (relative rounding <= 2^-24), nothing else differs
     assert np.max(np.abs(outs[0] - outs[1])) < 1e-6
+
+
+# ----------------------------------------------------------------------------- chunked prefill
+
+def _prefill(p, cu, **over):
+    args = dict(q=p["q"], cu_q_lens=cu, cache=p["cache"], block_table=p["block_table"], seq_lens=p["seq_lens"],
+                W_uk=p["W_uk"], W_uv=p["W_uv"], scale=p["scale"], theta=p["theta"])
+    args.update(over)
+    return O.prefill_naive(**args)
+
+
+@pytest.mark.parametrize("H,ctxs,q_len", [(2, (7, 9, 33), 1), (3, (13, 5), 5), (2, (16,), 16)])
+def test_prefill_equals_decode_forms_at_uniform_chunks(H, ctxs, q_len):
+    """With every chunk of length q_len, prefill_naive (K and V expanded once per sequence and head,
+    the softmax of whole rows) must equal decode_naive (K recomputed per query row) and
+    decode_absorbed (no expansion at all)."""
+    rng = np.random.default_rng(300 + H + q_len)
+    p = _small_problem(rng, H=H, dc=16, dr=8, dn=6, dv=5, ctx_list=ctxs, q_len=q_len, block=4)
+    cu = np.arange(len(ctxs) + 1) * q_len
+    a = _prefill(p, cu)
+    assert np.max(np.abs(a - _decode(O.decode_naive, p))) <= 1e-12
+    assert np.max(np.abs(a - _decode(O.decode_absorbed, p))) <= 1e-10
+
+
+def test_prefill_variable_chunks_equal_per_sequence_decodes():
+    """Chunk lengths 5, 0, 1 and 11 (an empty chunk included): each sequence's rows equal
+    decode_naive run on that sequence alone with its own q_len, so the row offsets, the
+    per-sequence positions and the empty chunk are all checked."""
+    rng = np.random.default_rng(310)
+    ctxs, lens = (12, 8, 3, 11), (5, 0, 1, 11)
+    p = _small_problem(rng, H=2, dc=16, dr=8, dn=6, dv=5, ctx_list=ctxs, q_len=1, block=4)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = rng.standard_normal((int(cu[-1]), 2, 14))
+    out = _prefill(p, cu, q=q)
+    for b, (ctx, n) in enumerate(zip(ctxs, lens)):
+        if n == 0:
+            continue
+        ref = O.decode_naive(q[cu[b]:cu[b + 1]], p["cache"], p["block_table"][b:b + 1], np.array([ctx]), n,
+                             p["W_uk"], p["W_uv"], p["scale"], p["theta"])
+        assert np.max(np.abs(out[cu[b]:cu[b + 1]] - ref)) <= 1e-12
+
+
+def test_prefill_fresh_sequence_first_row_is_value_projection():
+    """A chunk that is the whole context: its first row sees only token 0, so its output is
+    W_uv c_0 exactly (softmax of a single score), whatever the query."""
+    rng = np.random.default_rng(320)
+    ctx = 10
+    p = _small_problem(rng, H=3, dc=12, dr=4, dn=5, dv=6, ctx_list=(ctx,), q_len=ctx, block=4)
+    out = _prefill(p, np.array([0, ctx]))
+    dc = p["dims"][1]
+    c0 = p["cache"][p["block_table"][0, 0], 0, 0, :dc]
+    for h in range(3):
+        assert np.allclose(out[0, h], p["W_uv"][h] @ c0, rtol=1e-14, atol=1e-15)
+
+
+def test_prefill_causal_locality():
+    """Changing the chunk's last token changes only the chunk's last row; changing the token at
+    position ctx-3 leaves the rows before it unchanged and changes the rows after it."""
+    rng = np.random.default_rng(330)
+    ctx, n = 21, 6
+    p = _small_problem(rng, H=2, dc=16, dr=8, dn=6, dv=5, ctx_list=(ctx,), q_len=n, block=4)
+    cu = np.array([0, n])
+    base = _prefill(p, cu)
+    c2 = p["cache"].copy()
+    t = ctx - 1
+    c2[p["block_table"][0, t // 4], t % 4, 0, :] += 5.0
+    out = _prefill(p, cu, cache=c2)
+    assert np.array_equal(out[:n - 1], base[:n - 1])
+    assert np.max(np.abs(out[n - 1] - base[n - 1])) > 1e-3
+    c3 = p["cache"].copy()
+    t = ctx - 3                                  # position of chunk row n - 3
+    c3[p["block_table"][0, t // 4], t % 4, 0, :16] *= -1.0
+    out = _prefill(p, cu, cache=c3)
+    assert np.array_equal(out[:n - 3], base[:n - 3])
+    assert np.all(np.max(np.abs(out[n - 3:] - base[n - 3:]), axis=(1, 2)) > 1e-6)
