@@ -33,6 +33,7 @@
 #ifndef MLA_H_
 #define MLA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -164,6 +165,43 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
                       const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
 
 /*
+ * mla_prefill -- chunked prefill over the latent cache, naive form: K and V are expanded from the
+ * cached latent once per chunk and the new tokens attend to them causally, MHA-style.  The pages'
+ * naive MLA ([P-mini] MLA 的数学结构 and 版本 1: K_nope = C W_uk^T, V = C W_uv^T per head, K_pe
+ * shared by all heads) with the causal mask of [P-mini] 踩坑记录 坑 2, over the paged cache of
+ * [P-vllm] §2.3 and the block table of [P-hybrid] §2.1:
+ *   out[i, h] = softmax_{t <= p_i}(scale (q_nope . K_nope[t, h] + RoPE(q_pe, p_i) . k_pe_t)) V[t, h]
+ * Sequence b's n_b = cu_q_lens[b+1] - cu_q_lens[b] new tokens sit at positions ctx_b - n_b ..
+ * ctx_b - 1 and must already be in the cache (mla_cache_write), as for mla_decode.  bf16 storage
+ * (MLA_BF16) only.
+ *
+ *  q           device bf16 [total_q, H, dn + dr], un-rotated queries, rows in sequence order
+ *  cu_q_lens   device int32 [batch + 1], prefix sums of the chunk lengths (cu_q_lens[0] = 0,
+ *              cu_q_lens[batch] = total_q); every chunk length must be <= max_q_len
+ *  kv_cache .. max_seq_len   as in mla_decode (seq_lens[b] = ctx_b, the chunk included)
+ *  workspace   device memory of at least mla_prefill_workspace_size(...) bytes, caller-owned;
+ *              its contents on entry do not matter and are overwritten
+ *  out         device bf16 [total_q, H, dv]
+ * Asynchronous on `stream`; no host synchronisation and no allocation.  Device-resident values are
+ * trusted like mla_decode's; a chunk whose prefix sums are inconsistent is skipped (its rows are not
+ * written).  Returns MLA_EINVAL (null pointer, batch < 1, total_q < 1, max_q_len < 1,
+ * max_seq_len < max_q_len, num_blocks <= 0, stride smaller than ceil(max_seq_len/16), workspace too
+ * small), MLA_EUNSUPPORTED (a storage dtype other than MLA_BF16), MLA_ECAP (max_seq_len - 1 >
+ * max_position), MLA_EHIP.
+ */
+mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, int32_t batch, int32_t total_q,
+                       int32_t max_q_len, const void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                       int32_t block_table_stride, const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                       size_t workspace_bytes, void* out, void* stream);
+
+/* Bytes of workspace mla_prefill needs for `batch` sequences of contexts up to max_seq_len tokens
+ * and total_q new tokens: the prepared queries (total_q * H * 192 bf16) and the expanded rows
+ * [K_nope | k_pe | V] (batch * H * ceil256(max_seq_len) * 320 bf16).  MLA_EINVAL for a null
+ * pointer or a size < 1. */
+mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t total_q, int32_t max_seq_len,
+                                      size_t* bytes);
+
+/*
  * mla_free -- synchronises the device, then releases everything the context owns.
  * NULL is accepted.  Using the context afterwards is undefined.
  */
@@ -191,7 +229,16 @@ mla_status mla_last_decode_shape(const mla_ctx* ctx, int32_t* split_blocks, int3
 
 /* Kernel timing with HIP events recorded on the launch stream around each kernel.
  * enable != 0 starts recording (clears the totals); 0 stops.  Kernel ids: */
-enum { MLA_K_CACHE_WRITE = 0, MLA_K_Q_ABSORB = 1, MLA_K_DECODE = 2, MLA_K_COMBINE = 3, MLA_K_COUNT = 4 };
+enum {
+  MLA_K_CACHE_WRITE = 0,
+  MLA_K_Q_ABSORB = 1,
+  MLA_K_DECODE = 2,
+  MLA_K_COMBINE = 3,
+  MLA_K_PF_QPREP = 4,  /* mla_prefill: query preparation */
+  MLA_K_PF_EXPAND = 5, /* mla_prefill: K/V expansion */
+  MLA_K_PF_ATTN = 6,   /* mla_prefill: causal attention */
+  MLA_K_COUNT = 7
+};
 mla_status mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* Synchronises the recorded events and returns the summed milliseconds and launch count of
  * kernel `kernel_id` since profiling was enabled. */

@@ -18,10 +18,11 @@ MLA_F32, MLA_BF16, MLA_BF16_FP8 = 0, 1, 2
 FP8_ROW_BYTES = 656  # FP8 cache row: 512 e4m3 codes | 64 bf16 rope values | 4 fp32 group scales
 MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2, -3, -4, -5
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
+K_PF_QPREP, K_PF_EXPAND, K_PF_ATTN = 4, 5, 6
 
 EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_free", "mla_status_string",
            "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",
-           "mla_profile_samples")
+           "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size")
 
 
 class MLAConfig(ctypes.Structure):
@@ -58,6 +59,10 @@ def load(path=None):
     lib.mla_cache_write.restype = i32
     lib.mla_decode.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
     lib.mla_decode.restype = i32
+    lib.mla_prefill.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, vp, vp]
+    lib.mla_prefill.restype = i32
+    lib.mla_prefill_workspace_size.argtypes = [vp, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_workspace_size.restype = i32
     lib.mla_free.argtypes = [vp]
     lib.mla_free.restype = None
     lib.mla_status_string.argtypes = [i32]
@@ -196,6 +201,43 @@ class MLAContext:
         _check(st, "mla_decode")
         return out
 
+    def prefill_workspace_size(self, batch, total_q, max_seq_len):
+        n = ctypes.c_size_t()
+        _check(self.lib.mla_prefill_workspace_size(self.handle, int(batch), int(total_q), int(max_seq_len),
+                                                   ctypes.byref(n)), "mla_prefill_workspace_size")
+        return n.value
+
+    def prefill(self, q, cu_q_lens, kv_cache, block_table, seq_lens, max_seq_len, max_q_len, workspace=None,
+                out=None, stream=None):
+        """Chunked prefill (mla_prefill): q [total_q, H, 192]; cu_q_lens int32 [batch + 1] on the device.
+        A workspace of mla_prefill_workspace_size bytes is allocated here when none is given."""
+        torch = _torch()
+        H = self.num_heads
+        batch = int(seq_lens.shape[0])
+        total_q = int(q.shape[0])
+        _need(q, "q", self.tdtype, shape=(total_q, H, 192))
+        _need(cu_q_lens, "cu_q_lens", torch.int32, shape=(batch + 1,))
+        _need(kv_cache, "kv_cache", self.cache_dtype)
+        if kv_cache.dim() != 4 or tuple(kv_cache.shape[1:]) != (16, 1, self.cache_row):
+            raise ValueError(f"kv_cache must be [n_blocks, 16, 1, {self.cache_row}]")
+        _need(block_table, "block_table", torch.int32)
+        _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+        if block_table.dim() != 2 or block_table.shape[0] != batch:
+            raise ValueError("block_table must be [batch, stride]")
+        need = self.prefill_workspace_size(batch, total_q, max_seq_len)
+        if workspace is None:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+        _need(workspace, "workspace", torch.uint8)
+        if out is None:
+            out = torch.empty((total_q, H, 128), dtype=self.tdtype, device=q.device)
+        _need(out, "out", self.tdtype, shape=(total_q, H, 128))
+        st = self.lib.mla_prefill(self.handle, _ptr(q), _ptr(cu_q_lens), batch, total_q, int(max_q_len),
+                                  _ptr(kv_cache), int(kv_cache.shape[0]), _ptr(block_table), int(block_table.shape[1]),
+                                  _ptr(seq_lens), int(max_seq_len), _ptr(workspace), int(workspace.numel()),
+                                  _ptr(out), _stream_ptr(stream))
+        _check(st, "mla_prefill")
+        return out
+
     # -- helpers
     def set_decode_tuning(self, split_blocks=0, waves=0):
         _check(self.lib.mla_set_decode_tuning(self.handle, int(split_blocks), int(waves)), "mla_set_decode_tuning")
@@ -220,7 +262,7 @@ class MLAContext:
         buf = (ctypes.c_float * max_n)()
         n = ctypes.c_int32()
         _check(self.lib.mla_profile_samples(self.handle, int(kernel_id), buf, int(max_n), ctypes.byref(n)),
-               "mla_profile_samples")
+               "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size")
         return list(buf[:n.value])
 
 

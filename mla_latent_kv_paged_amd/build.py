@@ -40,7 +40,8 @@ def _hipcc():
 # AGPR half of the register file.  The 32-row kernel uses the flag for its score MFMAs and pins its
 # P.C accumulator to the AGPRs itself.
 PER_FILE = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-            "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+            "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+            "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src, extra, verbose):

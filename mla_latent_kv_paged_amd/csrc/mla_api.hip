@@ -367,6 +367,81 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   return hip_status(e);
 }
 
+namespace {
+constexpr int kPrefillTokPad = 256;  // expansion workgroup granularity
+int64_t prefill_tpad(int32_t max_seq_len) {
+  return (int64_t(max_seq_len) + kPrefillTokPad - 1) / kPrefillTokPad * kPrefillTokPad;
+}
+int64_t prefill_qp_bytes(const mla_ctx* c, int32_t total_q) {
+  return (int64_t(total_q) * c->cfg.num_heads * QW * 2 + 255) / 256 * 256;
+}
+}  // namespace
+
+mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t total_q, int32_t max_seq_len,
+                                      size_t* bytes) {
+  if (!ctx || !bytes || batch < 1 || total_q < 1 || max_seq_len < 1) return MLA_EINVAL;
+  const int64_t kv = int64_t(batch) * ctx->cfg.num_heads * prefill_tpad(max_seq_len) * (DN + DR + DV) * 2;
+  *bytes = size_t(prefill_qp_bytes(ctx, total_q) + kv);
+  return MLA_OK;
+}
+
+mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, int32_t batch, int32_t total_q,
+                       int32_t max_q_len, const void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                       int32_t block_table_stride, const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                       size_t workspace_bytes, void* out, void* stream) {
+  if (!ctx || !q || !cu_q_lens || !kv_cache || !block_table || !seq_lens || !workspace || !out) return MLA_EINVAL;
+  if (batch < 1 || total_q < 1 || max_q_len < 1 || num_blocks <= 0 || max_seq_len < max_q_len) return MLA_EINVAL;
+  if (!ctx->bf16 || ctx->fp8) return MLA_EUNSUPPORTED;
+  const mla_config& cf = ctx->cfg;
+  if (max_seq_len - 1 > cf.max_position) return MLA_ECAP;
+  const int max_blocks = (max_seq_len + BLK - 1) / BLK;
+  if (block_table_stride < max_blocks) return MLA_EINVAL;
+  size_t need = 0;
+  mla_prefill_workspace_size(ctx, batch, total_q, max_seq_len, &need);
+  if (workspace_bytes < need) return MLA_EINVAL;
+  hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  PrefillArgs pa{};
+  pa.batch = batch;
+  pa.H = cf.num_heads;
+  pa.q = q;
+  pa.cu_q_lens = cu_q_lens;
+  pa.total_q = total_q;
+  pa.max_q_len = max_q_len;
+  pa.cache = kv_cache;
+  pa.zero_block = ctx->zero_block;
+  pa.num_blocks = num_blocks;
+  pa.block_table = block_table;
+  pa.bt_stride = block_table_stride;
+  pa.seq_lens = seq_lens;
+  pa.max_seq_len = max_seq_len;
+  pa.max_position = cf.max_position;
+  pa.t_pad = int32_t(prefill_tpad(max_seq_len));
+  pa.rope = ctx->rope;
+  pa.qscale = ctx->qscale;
+  pa.W_uk = static_cast<const uint16_t*>(ctx->W_uk);
+  pa.W_uv = static_cast<const uint16_t*>(ctx->W_uv);
+  pa.qp = reinterpret_cast<uint16_t*>(ws);
+  pa.kv = reinterpret_cast<uint16_t*>(ws + prefill_qp_bytes(ctx, total_q));
+  pa.out = out;
+  hipError_t e;
+  {
+    ProfScope ps(ctx, MLA_K_PF_QPREP, s);
+    e = launch_prefill_qprep(pa, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  {
+    ProfScope ps(ctx, MLA_K_PF_EXPAND, s);
+    e = launch_prefill_expand(pa, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  {
+    ProfScope ps(ctx, MLA_K_PF_ATTN, s);
+    e = launch_prefill_attn(pa, s);
+  }
+  return hip_status(e);
+}
+
 void mla_free(mla_ctx* ctx) {
   if (!ctx) return;
   hipDeviceSynchronize();

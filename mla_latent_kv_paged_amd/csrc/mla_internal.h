@@ -86,6 +86,35 @@ struct DecodeArgs {
   int2* piece_tbl;        // 32-row kernel: per stream (first piece id, piece count), written by workgroup 0
 };
 
+// Chunked prefill (mla_prefill).  Sequence b owns query rows cu_q_lens[b] .. cu_q_lens[b+1]-1 at
+// positions ctx_b - n_b .. ctx_b - 1.  Workspace: qp [total_q, H, DN + DR] prepared queries and
+// kv [batch, H, t_pad, DN + DR + DV] expanded token rows [K_nope | k_pe | V] per (sequence, head).
+struct PrefillArgs {
+  int32_t batch;
+  int32_t H;
+  const void* q;               // [total_q, H, DN + DR] bf16, un-rotated
+  const int32_t* cu_q_lens;    // [batch + 1]
+  int32_t total_q;
+  int32_t max_q_len;           // an upper bound of every chunk length (sizes the grids)
+  const void* cache;           // bf16 [num_blocks, BLK, 1, ROW]
+  const void* zero_block;
+  int32_t num_blocks;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t max_position;
+  int32_t t_pad;               // token rows per (sequence, head) in kv: max_seq_len rounded up to 256
+  const double2* rope;
+  float qscale;                // softmax scale * log2(e)
+  const uint16_t* W_uk;        // [H, DN, DC]
+  const uint16_t* W_uv;        // [H, DV, DC]
+  uint16_t* qp;
+  uint16_t* kv;
+  void* out;                   // [total_q, H, DV] bf16
+  int32_t units;               // work items of the kernel being launched
+};
+
 struct CombineArgs {
   const float* part_acc;  // fp32 path
   const uint16_t* part_o16;  // bf16 path: fp16 normalised partials (acc / l)
@@ -121,6 +150,9 @@ hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 // FP8 cache rows (kFp8Row bytes), 16-row tiles; every H multiple of 16 and every q_len
 hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s);
+hipError_t launch_prefill_qprep(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_expand(PrefillArgs a, hipStream_t s);
+hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s);
 // bf16, 32-row tiles (H*q_len a multiple of 32), T in {1, 2, 4} tiles per workgroup; n_rt = tiles of
 // 32 rows per sequence (a multiple of T); units = workgroups, enough that every workgroup's share
 // is at most kMt32MaxSteps steps of two blocks

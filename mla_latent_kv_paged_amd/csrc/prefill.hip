@@ -1,0 +1,356 @@
+// Chunked prefill over the latent cache, naive form: K and V are expanded from the cached latent
+// once per chunk and the new tokens attend to them causally, MHA-style.
+//
+// What is computed (mini-infer 17 "MLA Attention：从 KV Cache 压缩到矩阵吸收", MLA 的数学结构 and
+// 版本 1; 踩坑记录 坑 2 causal mask; vLLM learning book ch. 07 §2.3 paged cache shape, §2.4
+// Decoupled RoPE; bxzpzcl.cn hybrid KV-cache page §2.1 block table):
+//   K_nope[t, h] = W_uk[h] c_t,  V[t, h] = W_uv[h] c_t,  K[t, h] = [K_nope[t, h] | k_pe_t]
+//   out[i, h]    = softmax_{t <= p_i}(scale (q_nope[i,h] . K_nope[t,h] + RoPE(q_pe[i,h], p_i) . k_pe_t)) V[t, h]
+// for the n_b new tokens of sequence b at positions p_i = ctx_b - n_b + i, whose rows are already in
+// the cache.  Per (row, token) this costs 2 (192 + 128) flops, against 2 (576 + 512) for the
+// absorbed form the decode uses: with many query rows per token the expansion pays for itself.
+//
+// Three kernels:
+//  * qprep: q_nope and RoPE(q_pe) (fp64 table, as the decode) scaled by scale * log2(e), in bf16.
+//  * expand: per (sequence, 256 tokens, head, K or V): W_uk[h] or W_uv[h] (128 x 512) is staged in
+//    LDS once (XOR-swizzled granules, conflict-free reads), the tokens' latent rows are the
+//    B operand straight from the paged cache; v_mfma_f32_16x16x32_bf16 with the 128 output
+//    dimensions on M and 16 tokens on N.  Part K also copies the tokens' rope keys.  Output rows
+//    [K_nope | k_pe | V] (320 bf16) per (sequence, head, token), rounded to bf16 once.
+//  * attn: one workgroup per (sequence, head, 64 query rows), four waves of 16 rows.  Key tiles of
+//    64 tokens move HBM -> LDS by DMA, each wave one 16-token sub-block, into NS shared stages
+//    (one barrier per tile).  The stage layout is the decode kernel's (8 x 8 chunks of 16-byte
+//    granules, token rows of 40 granules here).  Scores on v_mfma_f32_16x16x32_bf16 (tokens on M,
+//    K = 192); the online softmax is lane-local in the decode kernel's way; P.V takes two 16-token
+//    sub-blocks per v_mfma_f32_16x16x32_bf16 through a K permutation: both operands hold tokens
+//    4g .. 4g+3 of the first sub-block, then of the second, in lane group g (A by two transposed
+//    reads of V, B = the score registers).  Tiles past a row's position are skipped; the diagonal
+//    tiles are masked per element.
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kKV = DN + DR + DV;          // 320 values per expanded token row
+constexpr int kKVBytes = kKV * 2;          // 640
+constexpr int kGQ = kKV / 64;              // 5 granule groups (8 granules of 8 values) per token row
+constexpr int kSubBytes = 16 * kKVBytes;   // a 16-token sub-block in LDS: 2 x 5 chunks of 1 KiB
+constexpr int kTileBytes = 4 * kSubBytes;  // 64 tokens
+constexpr int kQTile = 64;                 // query rows per attention workgroup
+constexpr int kExpandTokens = 256;         // tokens per expansion workgroup
+constexpr float kMaxSlack = 8.f;           // lazy-rescale slack (log2 units), as in the decode
+
+// chunk length of sequence b, clamped to the launch bound; 0 for an inconsistent prefix sum
+__device__ __forceinline__ int chunk_of(const PrefillArgs& a, int b, int* first) {
+  const int c0 = a.cu_q_lens[b];
+  int n = a.cu_q_lens[b + 1] - c0;
+  if (c0 < 0 || n < 0 || c0 > a.total_q || n > a.total_q - c0) n = 0;
+  *first = c0;
+  return n < a.max_q_len ? n : a.max_q_len;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------ qprep
+
+__global__ __launch_bounds__(256) void prefill_qprep_kernel(PrefillArgs a) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 4 + int(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int c0;
+  const int n = chunk_of(a, b, &c0);
+  if (i >= n) return;
+  const int ctx = clamp_ctx(a.seq_lens[b], n, a.max_seq_len);
+  const int pos = ctx - n + i;
+  const bool ok = pos >= 0 && pos <= a.max_position;
+  const uint16_t* src = static_cast<const uint16_t*>(a.q) + int64_t(c0 + i) * a.H * QW;
+  uint16_t* dst = a.qp + int64_t(c0 + i) * a.H * QW;
+  for (int idx = lane; idx < a.H * DN; idx += 64) {
+    const int h = idx / DN, d = idx % DN;
+    dst[h * QW + d] = f32_to_bf16(bf16_to_f32(src[h * QW + d]) * a.qscale);
+  }
+  for (int idx = lane; idx < a.H * NPAIR; idx += 64) {
+    const int h = idx / NPAIR, p = idx % NPAIR;
+    float y0 = __builtin_nanf(""), y1 = __builtin_nanf("");
+    if (ok) {
+      const double x0 = bf16_to_f32(src[h * QW + DN + 2 * p]), x1 = bf16_to_f32(src[h * QW + DN + 2 * p + 1]);
+      const double2 cs = a.rope[int64_t(pos) * NPAIR + p];
+      y0 = float((x0 * cs.x - x1 * cs.y) * double(a.qscale));
+      y1 = float((x0 * cs.y + x1 * cs.x) * double(a.qscale));
+    }
+    dst[h * QW + DN + 2 * p] = f32_to_bf16(y0);
+    dst[h * QW + DN + 2 * p + 1] = f32_to_bf16(y1);
+  }
+}
+
+hipError_t launch_prefill_qprep(const PrefillArgs& a, hipStream_t s) {
+  dim3 grid((a.max_q_len + 3) / 4, a.batch);
+  prefill_qprep_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------- expand
+
+__global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
+  // W_uk[h] or W_uv[h]: 128 rows of 512 values; granule c (8 values) of row r at slot c ^ (r % 16)
+  __shared__ __attribute__((aligned(16))) char wl[DN * DC * 2];
+  static_assert(DN == DV, "one staging buffer for both parts");
+  const int nck = a.t_pad / kExpandTokens;
+  int u = blockIdx.x;
+  const int part = u & 1;  // 0: K (W_uk, also the rope keys), 1: V (W_uv)
+  u >>= 1;
+  const int h = u % a.H;
+  u /= a.H;
+  const int ck = u % nck;
+  const int b = u / nck;
+  if (b >= a.batch) return;
+  int c0;
+  const int n = chunk_of(a, b, &c0);
+  if (n == 0) return;
+  const int ctx = clamp_ctx(a.seq_lens[b], n, a.max_seq_len);
+  const int t0 = ck * kExpandTokens;
+  if (t0 >= ctx) return;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  {  // stage the weight part: wave w moves rows 32w .. 32w+31, one 1 KiB row per transfer
+    const char* W = reinterpret_cast<const char*>((part ? a.W_uv : a.W_uk) + int64_t(h) * DN * DC);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_char_t*)wl)));
+#pragma unroll 4
+    for (int rr = 0; rr < 32; ++rr) {
+      const int r = 32 * w + rr;
+      dma16(W + r * (DC * 2) + 16 * (lane ^ (r & 15)), base + r * (DC * 2));
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+  const char* cache = static_cast<const char*>(a.cache);
+  const int* bt = a.block_table + int64_t(b) * a.bt_stride;
+  uint16_t* kvrow0 = a.kv + (int64_t(b) * a.H + h) * a.t_pad * kKV;
+  // A operand of MFMA (dim tile jt, K step s): row 16 jt + r16, granule 4 s + g
+  const lds_char_t* wa = (const lds_char_t*)wl + r16 * (DC * 2);
+
+  // wave w: tokens t0 + 64 w + 16 st + (lane % 16), st = 0..3
+  for (int st = 0; st < 4; ++st) {
+    const int tb = t0 + 64 * w + 16 * st;
+    if (tb >= ctx) break;
+    const int tok = tb + r16;
+    const bool tv = tok < ctx;
+    int phys = tv ? bt[tok / BLK] : -1;
+    const bool ok = unsigned(phys) < unsigned(a.num_blocks);
+    const char* crow = cache + (int64_t(ok ? phys : 0) * BLK + tok % BLK) * (ROW * 2);
+    u32x4_t bq[16];  // B operand, K step s: the token's latent values 32 s + 8 g .. + 7
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      bq[s] = ok ? *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * g) : u32x4_t{0u, 0u, 0u, 0u};
+    f32x4_t acc[8];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) {
+        const u32x4_t av = *(const lds_u32x4_t*)(wa + jt * 16 * (DC * 2) + 16 * ((4 * s + g) ^ r16));
+        acc[jt] = mfma32v(av, bq[s], acc[jt]);
+      }
+    }
+    // D[dim][token]: lane (token r16, g) holds dims 16 jt + 4 g .. + 3
+    if (tv) {
+      uint16_t* dst = kvrow0 + int64_t(tok) * kKV + (part ? DN + DR : 0) + 4 * g;
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt)
+        *reinterpret_cast<u32x2_t*>(dst + 16 * jt) =
+            u32x2_t{cvt_pk_bf16(acc[jt][0], acc[jt][1]), cvt_pk_bf16(acc[jt][2], acc[jt][3])};
+    }
+    if (part == 0) {  // rope keys of the 16 tokens: lane -> token lane / 4, values 16 (lane % 4) .. + 15
+      const int rt = tb + (lane >> 2);
+      if (rt < ctx) {
+        const int rp = bt[rt / BLK];
+        const bool rok = unsigned(rp) < unsigned(a.num_blocks);
+        u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+        if (rok) {
+          const char* src = cache + (int64_t(rp) * BLK + rt % BLK) * (ROW * 2) + DC * 2 + 32 * (lane & 3);
+          v0 = *reinterpret_cast<const u32x4_t*>(src);
+          v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
+        }
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(kvrow0 + int64_t(rt) * kKV + DN + 16 * (lane & 3));
+        dst[0] = v0;
+        dst[1] = v1;
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill_expand(PrefillArgs a, hipStream_t s) {
+  const int64_t units = int64_t(a.batch) * (a.t_pad / kExpandTokens) * a.H * 2;
+  if (units > 0x7fffffff) return hipErrorInvalidValue;
+  a.units = int32_t(units);
+  prefill_expand_kernel<<<a.units, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------- attn
+
+template <int NS>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
+  static_assert(NS == 2 || NS == 3, "two or three shared stages");
+  __shared__ __attribute__((aligned(16))) char ring_mem[NS * kTileBytes];
+
+  // unit u = (sequence, head, query tile), query tiles longest first; contiguous ranges per XCD so
+  // that the query tiles of one (sequence, head) share an L2
+  const int per_xcd = (a.units + 7) >> 3;
+  const int u = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
+  if (u >= a.units) return;
+  const int nqt = (a.max_q_len + kQTile - 1) / kQTile;
+  const int qt = nqt - 1 - u % nqt;
+  const int h = (u / nqt) % a.H;
+  const int b = u / (nqt * a.H);
+  int c0;
+  const int n = chunk_of(a, b, &c0);
+  const int r0 = qt * kQTile;
+  if (r0 >= n) return;  // uniform per workgroup: before any barrier
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int lrow = lane & 7, lgr = lane >> 3;
+  const int ctx = clamp_ctx(a.seq_lens[b], n, a.max_seq_len);
+  const int p0 = ctx - n;                                   // position of chunk row 0
+  const int rw = r0 + 16 * w + r16;                         // this lane's row (of the chunk)
+  const int rl = rw < n ? rw : n - 1;                       // rows past the chunk compute row n - 1
+  const int p_row = p0 + rl;
+  const int lw = r0 + 16 * w + 15;
+  const int p_wave = p0 + (lw < n ? lw : n - 1);            // last position among the wave's rows
+  const int lg = r0 + kQTile - 1;
+  const int p_wg = p0 + (lg < n ? lg : n - 1);
+  const int ntile = p_wg / 64 + 1;                          // key tiles 0 .. ntile - 1
+
+  // query rows in registers: B operand of score MFMA k (granules 4k + g of row r16)
+  u32x4_t qreg[6];
+  {
+    const u32x4_t* qs = reinterpret_cast<const u32x4_t*>(a.qp + (int64_t(c0 + rl) * a.H + h) * QW);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) qreg[k] = qs[4 * k + g];
+  }
+#pragma unroll
+  for (int k = 0; k < 6; ++k) asm volatile("" ::"v"(qreg[k]));  // complete before the transfers
+
+  const char* kvb = reinterpret_cast<const char*>(a.kv + (int64_t(b) * a.H + h) * a.t_pad * kKV);
+  const char* zero = static_cast<const char*>(a.zero_block);  // >= 640 zero bytes
+  lds_char_t* const ring = (lds_char_t*)ring_mem;
+  // transfer of tile i: wave w moves sub-block w, chunk (tg, gq) = tokens 8 tg .. + 7 x granules
+  // 8 gq .. + 7; rows past the context read the zero block
+  auto issue = [&](int i) {
+    const int tok = 64 * i + 16 * w;
+    const uint32_t dst =
+        __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(ring + (i % NS) * kTileBytes + w * kSubBytes)));
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      const int t = tok + 8 * tg + lrow;
+      const char* src = (t < ctx ? kvb + int64_t(t) * kKVBytes : zero) + 16 * lgr;
+#pragma unroll
+      for (int gq = 0; gq < kGQ; ++gq) dma16(src + 128 * gq, dst + 1024 * (kGQ * tg + gq));
+    }
+  };
+
+  // per-lane LDS offsets inside a sub-block: score operand k (token r16, granule 4k + g) at
+  // sc_off + 512 k; transposed read of V tile jj (tokens 4g .. 4g+3, dims 16 jj + r16) at
+  // tr_off + 256 jj (V starts at granule 24: + 3072)
+  const int sc_off = 1024 * kGQ * (r16 >> 3) + 128 * g + 16 * (r16 & 7);
+  const int tr_off = 1024 * kGQ * (g >> 1) + 64 * (g & 1) + 128 * ((r16 >> 1) & 1) + 16 * (r16 >> 2) + 8 * (r16 & 1) +
+                     3072;
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  const int pre = ntile < NS - 1 ? ntile : NS - 1;
+  for (int i = 0; i < pre; ++i) issue(i);
+  for (int i = 0; i < ntile; ++i) {
+    const int ahead = ntile - 1 - i < NS - 2 ? ntile - 1 - i : NS - 2;  // tiles issued after i
+    if (ahead <= 0)
+      wait_vmcnt<0>();
+    else
+      wait_vmcnt<2 * kGQ>();
+    lds_barrier();  // every wave's part of tile i has landed; every wave is done with tile i - 1
+    if (i + NS - 1 < ntile) issue(i + NS - 1);
+    const uint32_t stage = uint32_t(uintptr_t(ring + (i % NS) * kTileBytes));
+
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {  // sub-blocks 2 pr and 2 pr + 1
+      const int tpair = 64 * i + 32 * pr;
+      if (tpair > p_wave) break;  // nothing visible to this wave's rows from here on
+      uint32_t sa = stage + uint32_t(2 * pr * kSubBytes);
+      asm volatile("" : "+v"(sa));
+      const lds_char_t* sub0 = (const lds_char_t*)uintptr_t(sa);
+      const lds_char_t* sub1 = sub0 + kSubBytes;
+      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        s0 = mfma32v(*(const lds_u32x4_t*)(sub0 + sc_off + 512 * k), qreg[k], s0);
+        s1 = mfma32v(*(const lds_u32x4_t*)(sub1 + sc_off + 512 * k), qreg[k], s1);
+      }
+      // lane (r16, g) holds tokens 4g + e of each sub-block for row r16; causal mask t <= p_row
+      float sv[8];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = (tpair + 4 * g + e <= p_row) ? s0[e] : -INFINITY;
+        sv[4 + e] = (tpair + 16 + 4 * g + e <= p_row) ? s1[e] : -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mb = fmaxf(mb, sv[e]);
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      if (__any(mb > m + kMaxSlack)) {
+        const float mn = fmaxf(m, mb);
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[jj] *= alpha;
+        m = mn;
+      }
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m);
+      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      const u32x4_t pb = u32x4_t{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                                 cvt_pk_bf16(p[6], p[7])};
+      // P.V: K = the 32 tokens of the pair, in the order of pb
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub0 + tr_off + 256 * jj));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub1 + tr_off + 256 * jj));
+        const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0), a1 = __builtin_bit_cast(u32x2_t, v1);
+        acc[jj] = mfma32v(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pb, acc[jj]);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // out = acc / l for the rows of the chunk; lane (r16, g) holds dims 16 jj + 4g .. + 3
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (rw < n) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(c0 + rw) * a.H + h) * DV + 4 * g;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      *reinterpret_cast<u32x2_t*>(o + 16 * jj) =
+          u32x2_t{cvt_pk_bf16(acc[jj][0] * inv, acc[jj][1] * inv), cvt_pk_bf16(acc[jj][2] * inv, acc[jj][3] * inv)};
+  }
+}
+
+hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s) {
+  const int64_t units = int64_t(a.batch) * a.H * ((a.max_q_len + kQTile - 1) / kQTile);
+  if (units > 0x7ffffff0) return hipErrorInvalidValue;
+  a.units = int32_t(units);
+  const int grid = ((a.units + 7) >> 3) << 3;
+  prefill_attn_kernel<2><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

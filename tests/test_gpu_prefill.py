@@ -1,0 +1,138 @@
+"""GPU parity of the chunked prefill (mla_prefill) through the C ABI against the fp64 oracle's
+prefill_naive (oracle/mla_oracle.py), to the bf16 tolerance (max abs 2e-2, relative L2 5e-3).
+
+Each case writes every context token with mla_cache_write (the chunk's tokens included, as a serving
+engine does before attention), then runs one prefill whose chunk of sequence b is its last n_b
+tokens.  The oracle reads its own cache (oracle cache_write of the same seeded tokens).  The queries
+are the seeded workload's chunk queries (one row per chunk token, in sequence order).
+Unused pool slots are NaN, so a read of a token the kernels should not see poisons the output."""
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from workloads import mla_inputs as W
+
+from ._harness import GpuRun, compare, dev, dev_i32, oracle_weights
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mla_latent_kv_paged_amd import load
+    load()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _cu(chunks):
+    return np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+
+
+def _oracle_prefill(w, chunks):
+    W_uk, W_uv = oracle_weights(w)
+    tok = w.all_tokens()
+    cache = O.cache_write(np.full((w.n_blocks, 16, 1, 576), np.nan), tok["c_kv"], tok["k_pe"], tok["positions"],
+                          tok["slot_mapping"], w.gamma().astype(np.float64), w.eps, w.theta, w.storage)
+    return O.prefill_naive(w.chunk_queries(chunks), _cu(chunks), cache, w.block_table, w.seq_lens, W_uk, W_uv,
+                           w.scale, w.theta)
+
+
+def _run_prefill(run, chunks, max_q_len=None):
+    w = run.w
+    q = dev(w.chunk_queries(chunks), w.storage)
+    mq = int(max_q_len or max(max(chunks), 1))
+    out = run.ctx.prefill(q, dev_i32(_cu(chunks)), run.pool, run.bt, run.sl, run.max_ctx, mq)
+    torch.cuda.synchronize()
+    return out
+
+
+PREFILL_CASES = [
+    # name, heads, context lengths, chunk lengths (the last n_b tokens of each context)
+    ("mixed_h16", 16, [300, 77, 129], [64, 77, 1]),        # a fresh prefill, a one-token chunk
+    ("h128", 128, [150, 90], [100, 90]),
+    ("ragged_h16", 16, [513, 1000, 40], [257, 333, 0]),   # tails off every tile size, an empty chunk
+    ("h32_q", 32, [200, 65], [130, 64]),
+]
+
+
+@pytest.mark.parametrize("name,heads,ctxs,chunks", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_parity(name, heads, ctxs, chunks):
+    w = W.custom("pf_" + name, "bf16", heads, ctxs, q_len=1, seed=90 + heads)
+    _say("prefill", name, "H", heads, "ctx", ctxs, "chunks", chunks)
+    ref = _oracle_prefill(w, chunks)
+    run = GpuRun(w)
+    try:
+        out = _run_prefill(run, chunks)
+        compare(out, ref, "bf16", f"prefill {name}")
+        out2 = _run_prefill(run, chunks, max_q_len=max(chunks) + 37)  # a looser launch bound
+        assert torch.equal(out, out2), "prefill result depends on the launch bound"
+        assert torch.equal(out, _run_prefill(run, chunks)), "prefill is not deterministic"
+    finally:
+        run.free()
+
+
+def test_prefill_gamma_and_long_fresh_chunk():
+    """A 2,048-token chunk that is the whole context (every query tile, the longest first, and the
+    diagonal tiles), with gamma != 1 in the cache write."""
+    w = W.custom("pf_long", "bf16", 16, [2048], q_len=1, seed=95, gamma_noise=0.1)
+    _say("prefill long fresh chunk 2048, gamma noise")
+    ref = _oracle_prefill(w, [2048])
+    run = GpuRun(w)
+    try:
+        compare(_run_prefill(run, [2048]), ref, "bf16", "prefill 2048 fresh")
+    finally:
+        run.free()
+
+
+def test_prefill_one_token_chunks_match_decode():
+    """Chunks of one token are a decode: the prefill (expanded K/V, MHA-style) and mla_decode (the
+    absorbed form) reach the same result by different arithmetic; both against the oracle, and
+    against each other to twice the tolerance."""
+    w = W.custom("pf_dec", "bf16", 16, [700, 33, 258], q_len=1, seed=96)
+    _say("prefill one-token chunks vs decode")
+    ref = _oracle_prefill(w, [1, 1, 1])
+    run = GpuRun(w)
+    try:
+        pf = _run_prefill(run, [1, 1, 1])
+        dc = run.ctx.decode(dev(w.chunk_queries([1, 1, 1]), "bf16"), run.pool, run.bt, run.sl, run.max_ctx, q_len=1)
+        torch.cuda.synchronize()
+        compare(pf, ref, "bf16", "prefill one-token chunks")
+        compare(dc, ref, "bf16", "decode")
+        d = (pf.float() - dc.float()).abs().max().item()
+        assert d <= 4e-2, d
+    finally:
+        run.free()
+
+
+def test_prefill_status_codes():
+    """Host-side validation through the C ABI: a workspace one byte short, a chunk bound above the
+    context bound, and an FP8-cache context (unsupported) are refused before any launch."""
+    from mla_latent_kv_paged_amd import MLAError, MLAContext
+    w = W.custom("pf_err", "bf16", 16, [40], q_len=1, seed=97)
+    run = GpuRun(w)
+    cu = _cu([8])
+    q = dev(w.chunk_queries([8]), "bf16")
+    try:
+        need = run.ctx.prefill_workspace_size(1, 8, run.max_ctx)
+        ws = torch.empty((need - 1,), dtype=torch.uint8, device="cuda")
+        with pytest.raises(MLAError):
+            run.ctx.prefill(q, dev_i32(cu), run.pool, run.bt, run.sl, run.max_ctx, 8, workspace=ws)
+        with pytest.raises(MLAError):
+            run.ctx.prefill(q, dev_i32(cu), run.pool, run.bt, run.sl, 4, 8)
+    finally:
+        run.free()
+    ctx8 = MLAContext(dev(w.kv_b_proj(), "bf16"), None, num_heads=16, dtype="fp8", max_q_tokens=8, max_batch=1,
+                      max_position=64, max_seq_len=64)
+    try:
+        pool8 = torch.zeros((w.n_blocks, 16, 1, 656), dtype=torch.uint8, device="cuda")
+        with pytest.raises(MLAError):
+            ctx8.prefill(q, dev_i32(cu), pool8, dev_i32(w.block_table), dev_i32(w.seq_lens), 48, 8)
+    finally:
+        ctx8.free()

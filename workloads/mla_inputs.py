@@ -38,7 +38,7 @@ BLOCK_SIZE = 16
 ROW = KV_LORA_RANK + QK_ROPE_HEAD_DIM
 
 # tags for independent seed streams
-_T_WEIGHT, _T_GAMMA, _T_Q, _T_STRUCT, _T_HIST, _T_POOL = range(6)
+_T_WEIGHT, _T_GAMMA, _T_Q, _T_STRUCT, _T_HIST, _T_POOL, _T_QCHUNK = range(7)
 
 
 def f32_to_bf16_bits(x):
@@ -125,6 +125,13 @@ class Workload:
         """[B*q_len, H, dn+dr] un-rotated queries ([nope | rope] per head)."""
         q = _rng(self.seed, _T_Q).standard_normal(
             (self.n_q, self.num_heads, self.qk_nope_head_dim + self.qk_rope_head_dim), dtype=np.float32)
+        return self._store(q)[0]
+
+    def chunk_queries(self, chunks):
+        """[sum(chunks), H, dn+dr] un-rotated queries for a chunked prefill in which sequence b has
+        chunks[b] new tokens (rows in sequence order), drawn from a stream of their own."""
+        q = _rng(self.seed, _T_QCHUNK).standard_normal(
+            (int(np.sum(chunks)), self.num_heads, self.qk_nope_head_dim + self.qk_rope_head_dim), dtype=np.float32)
         return self._store(q)[0]
 
     def history(self, b):
