@@ -59,7 +59,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences in the oracle's timed sample (capped at "
                     "the batch)")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only"],
+    ap.add_argument("--pf-batch", type=int, default=4, help="prefill mode: sequences")
+    ap.add_argument("--pf-len", type=int, default=4096, help="prefill mode: tokens per sequence, all new (fresh "
+                    "prefill: the chunk is the whole context)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only", "prefill",
+                                                        "prefill-only"],
                     help="copy-calibration: run a plain 256 MiB device copy (for counter scaling); "
                          "decode-only: run just the decode loop (for profilers)")
     return ap.parse_args()
@@ -195,6 +199,123 @@ def cpu_baseline(w, n_seq, fp8=False):
             "seconds_per_sample_step": t}
 
 
+def prefill_flops(ctxs, chunks, H):
+    """Algorithmic flops of a chunked prefill in the naive form: attention 2 (192 + 128) per (row,
+    visible token) and head, expansion 2 * 512 * 256 per context token and head."""
+    att = 0
+    for ctx, n in zip(ctxs, chunks):
+        p0 = ctx - n  # visible tokens of chunk row i: p0 + i + 1
+        att += n * p0 + n * (n + 1) // 2
+    return att * H * 2 * (192 + 128), sum(ctxs) * H * 2 * 512 * 256
+
+
+def prefill_cpu_baseline(w, tokens=1024):
+    """The fp64 oracle's prefill_naive on a bounded sample: sequence 0's first `tokens` tokens as a
+    fresh chunk (identity-paged local cache, written by the oracle, not timed)."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    kvb = w.kv_b_proj().astype(np.float64)
+    W_uk, W_uv = O.absorb(kvb, w.num_heads, w.qk_nope_head_dim, w.v_head_dim)
+    c, k = w.history(0)
+    n = min(tokens, int(w.seq_lens[0]))
+    nb = (n + 15) // 16
+    cache = O.cache_write(np.full((nb, 16, 1, 576), np.nan), c[:n], k[:n], np.arange(n), np.arange(n),
+                          w.gamma().astype(np.float64), w.eps, w.theta, w.storage)
+    q = w.chunk_queries([n] + [0] * (w.batch - 1))[:n]
+    times = []
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 100):
+        t0 = time.perf_counter()
+        O.prefill_naive(q, np.array([0, n]), cache, np.arange(nb)[None, :], np.array([n]), W_uk, W_uv, w.scale,
+                        w.theta)
+        times.append(time.perf_counter() - t0)
+        if sum(times) > 30:
+            break
+    t = float(np.median(times))
+    fa, fe = prefill_flops([n], [n], w.num_heads)
+    return {"value": (fa + fe) / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"sequence 0, first {n} tokens as a fresh chunk (oracle prefill_naive, fp64); median of "
+                      f"{len(times)} runs, {t:.3f} s per run; host threads available {cores}"}
+
+
+def prefill_main(args):
+    """Chunked prefill measurement: `--pf-batch` sequences, each a fresh chunk of `--pf-len` tokens
+    (16 heads, V2-Lite shapes), after a cache write of all their tokens."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_paged_amd import MLAContext, K_PF_QPREP, K_PF_EXPAND, K_PF_ATTN
+    from workloads import mla_inputs as W
+    B, S = args.pf_batch, args.pf_len
+    w = W.custom(f"prefill_b{B}_s{S}", "bf16", 16, [S] * B, q_len=1, seed=1240)
+    chunks = [S] * B
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+    def dev_i(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+    ctx = MLAContext(dev(w.kv_b_proj()), None, num_heads=16, dtype="bf16", rms_eps=w.eps, rope_theta=w.theta,
+                     max_q_tokens=B, max_batch=B, max_position=S, max_seq_len=S)
+    pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for b in range(B):
+        c, k = w.history(b)
+        ctx.cache_write(dev(c), dev(k), dev_i(np.arange(S)), dev_i(w.slots(b, 0, S)), pool)
+    q = dev(w.chunk_queries(chunks))
+    cu = dev_i(np.concatenate([[0], np.cumsum(chunks)]))
+    bt, sl = dev_i(w.block_table), dev_i(w.seq_lens)
+    ws = torch.empty((ctx.prefill_workspace_size(B, B * S, S),), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B * S, 16, 128), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        ctx.prefill(q, cu, pool, bt, sl, S, S, workspace=ws, out=out)
+
+    if args.mode == "prefill-only":
+        for _ in range(args.warmup + args.steps):
+            run()
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "prefill-only", "launches": args.warmup + args.steps, "workload": w.name}),
+              flush=True)
+        return
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ctx.profile_enable(True)
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    kus = {}
+    for name, kid in (("qprep", K_PF_QPREP), ("expand", K_PF_EXPAND), ("attn", K_PF_ATTN)):
+        t, n = ctx.profile_read(kid)
+        kus[name] = round(1e3 * t / max(n, 1), 2)
+    ctx.profile_enable(False)
+    fa, fe = prefill_flops([S] * B, chunks, 16)
+    res = {"metric": f"MLA chunked prefill TFLOP/s, V2-Lite b={B} chunk={S} (fresh)", "value": round((fa + fe) / ms / 1e9, 2),
+           "unit": "TFLOP/s", "mode": "prefill", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_prefill": round(ms, 4), "higher_is_better": True, "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) activations, N(0,1/512) kv_b_proj)",
+           "config": {"workload": f"prefill_b{B}_s{S}: {B} sequences, each a fresh chunk of {S} tokens, 16 heads, "
+                                  "kv_lora_rank 512 + rope 64, naive form (K/V expanded once per chunk)",
+                      "batch": B, "chunk": S, "num_heads": 16},
+           "flops": {"attention": fa, "expansion": fe}, "kernels_us": kus,
+           "roofline": {"bound": "mfma", "achieved": round(fa / (kus["attn"] * 1e-6) / 1e12, 2),
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(fa / (kus["attn"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "prefill_attn_kernel",
+                        "expand_tflops": round(fe / (kus["expand"] * 1e-6) / 1e12, 2)}}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(w)
+    ctx.free()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -206,6 +327,9 @@ def main():
     import torch
     if args.mode == "copy-calibration":
         copy_calibration()
+        return
+    if args.mode in ("prefill", "prefill-only"):
+        prefill_main(args)
         return
     from mla_latent_kv_paged_amd import MLAContext, K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE
 
