@@ -243,7 +243,7 @@ def prefill_main(args):
     (16 heads, V2-Lite shapes), after a cache write of all their tokens."""
     import numpy as np
     import torch
-    from mla_latent_kv_paged_amd import MLAContext, K_PF_QPREP, K_PF_EXPAND, K_PF_ATTN
+    from mla_latent_kv_paged_amd import MLAContext, K_PF_EXPAND, K_PF_ATTN
     from workloads import mla_inputs as W
     B, S = args.pf_batch, args.pf_len
     w = W.custom(f"prefill_b{B}_s{S}", "bf16", 16, [S] * B, q_len=1, seed=1240)
@@ -292,7 +292,7 @@ def prefill_main(args):
         run()
     torch.cuda.synchronize()
     kus = {}
-    for name, kid in (("qprep", K_PF_QPREP), ("expand", K_PF_EXPAND), ("attn", K_PF_ATTN)):
+    for name, kid in (("expand", K_PF_EXPAND), ("attn", K_PF_ATTN)):
         t, n = ctx.profile_read(kid)
         kus[name] = round(1e3 * t / max(n, 1), 2)
     ctx.profile_enable(False)

@@ -195,9 +195,8 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
                        size_t workspace_bytes, void* out, void* stream);
 
 /* Bytes of workspace mla_prefill needs for `batch` sequences of contexts up to max_seq_len tokens
- * and total_q new tokens: the prepared queries (total_q * H * 192 bf16) and the expanded rows
- * [K_nope | k_pe | V] (batch * H * ceil256(max_seq_len) * 320 bf16).  MLA_EINVAL for a null
- * pointer or a size < 1. */
+ * and total_q new tokens: the expanded rows [K_nope | k_pe | V], batch * H * ceil256(max_seq_len)
+ * * 320 bf16 (total_q does not enter at present).  MLA_EINVAL for a null pointer or a size < 1. */
 mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t total_q, int32_t max_seq_len,
                                       size_t* bytes);
 
@@ -234,10 +233,9 @@ enum {
   MLA_K_Q_ABSORB = 1,
   MLA_K_DECODE = 2,
   MLA_K_COMBINE = 3,
-  MLA_K_PF_QPREP = 4,  /* mla_prefill: query preparation */
-  MLA_K_PF_EXPAND = 5, /* mla_prefill: K/V expansion */
-  MLA_K_PF_ATTN = 6,   /* mla_prefill: causal attention */
-  MLA_K_COUNT = 7
+  MLA_K_PF_EXPAND = 4, /* mla_prefill: K/V expansion */
+  MLA_K_PF_ATTN = 5,   /* mla_prefill: causal attention (queries prepared in it) */
+  MLA_K_COUNT = 6
 };
 mla_status mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* Synchronises the recorded events and returns the summed milliseconds and launch count of

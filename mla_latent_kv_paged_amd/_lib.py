@@ -18,7 +18,7 @@ MLA_F32, MLA_BF16, MLA_BF16_FP8 = 0, 1, 2
 FP8_ROW_BYTES = 656  # FP8 cache row: 512 e4m3 codes | 64 bf16 rope values | 4 fp32 group scales
 MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2, -3, -4, -5
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
-K_PF_QPREP, K_PF_EXPAND, K_PF_ATTN = 4, 5, 6
+K_PF_EXPAND, K_PF_ATTN = 4, 5
 
 EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_free", "mla_status_string",
            "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",

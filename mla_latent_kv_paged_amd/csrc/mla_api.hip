@@ -372,16 +372,13 @@ constexpr int kPrefillTokPad = 256;  // expansion workgroup granularity
 int64_t prefill_tpad(int32_t max_seq_len) {
   return (int64_t(max_seq_len) + kPrefillTokPad - 1) / kPrefillTokPad * kPrefillTokPad;
 }
-int64_t prefill_qp_bytes(const mla_ctx* c, int32_t total_q) {
-  return (int64_t(total_q) * c->cfg.num_heads * QW * 2 + 255) / 256 * 256;
-}
 }  // namespace
 
 mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t total_q, int32_t max_seq_len,
                                       size_t* bytes) {
   if (!ctx || !bytes || batch < 1 || total_q < 1 || max_seq_len < 1) return MLA_EINVAL;
   const int64_t kv = int64_t(batch) * ctx->cfg.num_heads * prefill_tpad(max_seq_len) * (DN + DR + DV) * 2;
-  *bytes = size_t(prefill_qp_bytes(ctx, total_q) + kv);
+  *bytes = size_t(kv);
   return MLA_OK;
 }
 
@@ -421,15 +418,9 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
   pa.qscale = ctx->qscale;
   pa.W_uk = static_cast<const uint16_t*>(ctx->W_uk);
   pa.W_uv = static_cast<const uint16_t*>(ctx->W_uv);
-  pa.qp = reinterpret_cast<uint16_t*>(ws);
-  pa.kv = reinterpret_cast<uint16_t*>(ws + prefill_qp_bytes(ctx, total_q));
+  pa.kv = reinterpret_cast<uint16_t*>(ws);
   pa.out = out;
   hipError_t e;
-  {
-    ProfScope ps(ctx, MLA_K_PF_QPREP, s);
-    e = launch_prefill_qprep(pa, s);
-  }
-  if (e != hipSuccess) return hip_status(e);
   {
     ProfScope ps(ctx, MLA_K_PF_EXPAND, s);
     e = launch_prefill_expand(pa, s);

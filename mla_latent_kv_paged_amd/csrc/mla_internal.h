@@ -87,8 +87,8 @@ struct DecodeArgs {
 };
 
 // Chunked prefill (mla_prefill).  Sequence b owns query rows cu_q_lens[b] .. cu_q_lens[b+1]-1 at
-// positions ctx_b - n_b .. ctx_b - 1.  Workspace: qp [total_q, H, DN + DR] prepared queries and
-// kv [batch, H, t_pad, DN + DR + DV] expanded token rows [K_nope | k_pe | V] per (sequence, head).
+// positions ctx_b - n_b .. ctx_b - 1.  Workspace: kv [batch, H, t_pad, DN + DR + DV] expanded
+// token rows [K_nope | k_pe | V] per (sequence, head).
 struct PrefillArgs {
   int32_t batch;
   int32_t H;
@@ -109,7 +109,6 @@ struct PrefillArgs {
   float qscale;                // softmax scale * log2(e)
   const uint16_t* W_uk;        // [H, DN, DC]
   const uint16_t* W_uv;        // [H, DV, DC]
-  uint16_t* qp;
   uint16_t* kv;
   void* out;                   // [total_q, H, DV] bf16
   int32_t units;               // work items of the kernel being launched
@@ -150,7 +149,6 @@ hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 // FP8 cache rows (kFp8Row bytes), 16-row tiles; every H multiple of 16 and every q_len
 hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s);
-hipError_t launch_prefill_qprep(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_expand(PrefillArgs a, hipStream_t s);
 hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s);
 // bf16, 32-row tiles (H*q_len a multiple of 32), T in {1, 2, 4} tiles per workgroup; n_rt = tiles of

@@ -10,14 +10,14 @@
 // the cache.  Per (row, token) this costs 2 (192 + 128) flops, against 2 (576 + 512) for the
 // absorbed form the decode uses: with many query rows per token the expansion pays for itself.
 //
-// Three kernels:
-//  * qprep: q_nope and RoPE(q_pe) (fp64 table, as the decode) scaled by scale * log2(e), in bf16.
+// Two kernels:
 //  * expand: per (sequence, 256 tokens, head, K or V): W_uk[h] or W_uv[h] (128 x 512) is staged in
 //    LDS once (XOR-swizzled granules, conflict-free reads), the tokens' latent rows are the
 //    B operand straight from the paged cache; v_mfma_f32_16x16x32_bf16 with the 128 output
 //    dimensions on M and 16 tokens on N.  Part K also copies the tokens' rope keys.  Output rows
 //    [K_nope | k_pe | V] (320 bf16) per (sequence, head, token), rounded to bf16 once.
-//  * attn: one workgroup per (sequence, head, 64 query rows), four waves of 16 rows.  Key tiles of
+//  * attn: one workgroup per (sequence, head, 128 query rows), four waves of 32 rows (two 16-row
+//    tiles, so that every key and value operand read from LDS feeds two MFMAs).  Key tiles of
 //    64 tokens move HBM -> LDS by DMA, each wave one 16-token sub-block, into NS shared stages
 //    (one barrier per tile).  The stage layout is the decode kernel's (8 x 8 chunks of 16-byte
 //    granules, token rows of 40 granules here).  Scores on v_mfma_f32_16x16x32_bf16 (tokens on M,
@@ -25,7 +25,8 @@
 //    sub-blocks per v_mfma_f32_16x16x32_bf16 through a K permutation: both operands hold tokens
 //    4g .. 4g+3 of the first sub-block, then of the second, in lane group g (A by two transposed
 //    reads of V, B = the score registers).  Tiles past a row's position are skipped; the diagonal
-//    tiles are masked per element.
+//    tiles are masked per element.  The queries are prepared as they are loaded: q_nope scaled by
+//    scale * log2(e), RoPE(q_pe) at the row's position in fp64 (the decode's table), both in bf16.
 #include "mla_internal.h"
 
 namespace mla {
@@ -37,7 +38,7 @@ constexpr int kKVBytes = kKV * 2;          // 640
 constexpr int kGQ = kKV / 64;              // 5 granule groups (8 granules of 8 values) per token row
 constexpr int kSubBytes = 16 * kKVBytes;   // a 16-token sub-block in LDS: 2 x 5 chunks of 1 KiB
 constexpr int kTileBytes = 4 * kSubBytes;  // 64 tokens
-constexpr int kQTile = 64;                 // query rows per attention workgroup
+constexpr int kQTile = 128;                // query rows per attention workgroup (32 per wave)
 constexpr int kExpandTokens = 256;         // tokens per expansion workgroup
 constexpr float kMaxSlack = 8.f;           // lazy-rescale slack (log2 units), as in the decode
 
@@ -51,44 +52,6 @@ __device__ __forceinline__ int chunk_of(const PrefillArgs& a, int b, int* first)
 }
 
 }  // namespace
-
-// ------------------------------------------------------------------------------------------ qprep
-
-__global__ __launch_bounds__(256) void prefill_qprep_kernel(PrefillArgs a) {
-  const int b = blockIdx.y;
-  const int i = blockIdx.x * 4 + int(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  int c0;
-  const int n = chunk_of(a, b, &c0);
-  if (i >= n) return;
-  const int ctx = clamp_ctx(a.seq_lens[b], n, a.max_seq_len);
-  const int pos = ctx - n + i;
-  const bool ok = pos >= 0 && pos <= a.max_position;
-  const uint16_t* src = static_cast<const uint16_t*>(a.q) + int64_t(c0 + i) * a.H * QW;
-  uint16_t* dst = a.qp + int64_t(c0 + i) * a.H * QW;
-  for (int idx = lane; idx < a.H * DN; idx += 64) {
-    const int h = idx / DN, d = idx % DN;
-    dst[h * QW + d] = f32_to_bf16(bf16_to_f32(src[h * QW + d]) * a.qscale);
-  }
-  for (int idx = lane; idx < a.H * NPAIR; idx += 64) {
-    const int h = idx / NPAIR, p = idx % NPAIR;
-    float y0 = __builtin_nanf(""), y1 = __builtin_nanf("");
-    if (ok) {
-      const double x0 = bf16_to_f32(src[h * QW + DN + 2 * p]), x1 = bf16_to_f32(src[h * QW + DN + 2 * p + 1]);
-      const double2 cs = a.rope[int64_t(pos) * NPAIR + p];
-      y0 = float((x0 * cs.x - x1 * cs.y) * double(a.qscale));
-      y1 = float((x0 * cs.y + x1 * cs.x) * double(a.qscale));
-    }
-    dst[h * QW + DN + 2 * p] = f32_to_bf16(y0);
-    dst[h * QW + DN + 2 * p + 1] = f32_to_bf16(y1);
-  }
-}
-
-hipError_t launch_prefill_qprep(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid((a.max_q_len + 3) / 4, a.batch);
-  prefill_qprep_kernel<<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
 
 // ----------------------------------------------------------------------------------------- expand
 
@@ -217,25 +180,22 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   const int r16 = lane & 15, g = lane >> 4;
   const int lrow = lane & 7, lgr = lane >> 3;
   const int ctx = clamp_ctx(a.seq_lens[b], n, a.max_seq_len);
-  const int p0 = ctx - n;                                   // position of chunk row 0
-  const int rw = r0 + 16 * w + r16;                         // this lane's row (of the chunk)
-  const int rl = rw < n ? rw : n - 1;                       // rows past the chunk compute row n - 1
-  const int p_row = p0 + rl;
-  const int lw = r0 + 16 * w + 15;
-  const int p_wave = p0 + (lw < n ? lw : n - 1);            // last position among the wave's rows
+  const int p0 = ctx - n;  // position of chunk row 0
+  // this wave's rows: r0 + 32 w + 16 rt + r16, rt = 0, 1 (two 16-row tiles); rows past the chunk
+  // compute row n - 1 and are not stored
+  int rw[2], p_row[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    rw[rt] = r0 + 32 * w + 16 * rt + r16;
+    p_row[rt] = p0 + (rw[rt] < n ? rw[rt] : n - 1);
+  }
+  const int lw = r0 + 32 * w + 31;
+  const int p_wave = p0 + (lw < n ? lw : n - 1);  // last position among the wave's rows
+  const int fw = r0 + 32 * w;
+  const int p_wmin = p0 + (fw < n ? fw : n - 1);  // first position among them
   const int lg = r0 + kQTile - 1;
   const int p_wg = p0 + (lg < n ? lg : n - 1);
-  const int ntile = p_wg / 64 + 1;                          // key tiles 0 .. ntile - 1
-
-  // query rows in registers: B operand of score MFMA k (granules 4k + g of row r16)
-  u32x4_t qreg[6];
-  {
-    const u32x4_t* qs = reinterpret_cast<const u32x4_t*>(a.qp + (int64_t(c0 + rl) * a.H + h) * QW);
-#pragma unroll
-    for (int k = 0; k < 6; ++k) qreg[k] = qs[4 * k + g];
-  }
-#pragma unroll
-  for (int k = 0; k < 6; ++k) asm volatile("" ::"v"(qreg[k]));  // complete before the transfers
+  const int ntile = p_wg / 64 + 1;  // key tiles 0 .. ntile - 1
 
   const char* kvb = reinterpret_cast<const char*>(a.kv + (int64_t(b) * a.H + h) * a.t_pad * kKV);
   const char* zero = static_cast<const char*>(a.zero_block);  // >= 640 zero bytes
@@ -262,13 +222,62 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   const int tr_off = 1024 * kGQ * (g >> 1) + 64 * (g & 1) + 128 * ((r16 >> 1) & 1) + 16 * (r16 >> 2) + 8 * (r16 & 1) +
                      3072;
 
-  f32x4_t acc[8];
+  f32x4_t acc[2][8];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[rt][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
   const int pre = ntile < NS - 1 ? ntile : NS - 1;
   for (int i = 0; i < pre; ++i) issue(i);
+
+  // query rows in registers: B operand of score MFMA k (granules 4k + g of row r16 of tile rt),
+  // prepared here: q_nope scaled by scale * log2(e), q_pe rotated in fp64 at the row's position
+  // (the decode's RoPE table) and scaled, both rounded to bf16 once
+  u32x4_t qreg[2][6];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const u32x4_t* qs =
+        reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) + (int64_t(c0 + p_row[rt] - p0) * a.H + h) * QW);
+    u32x4_t raw[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) raw[k] = qs[4 * k + g];
+    const int pos = p_row[rt];
+    const bool ok = pos >= 0 && pos <= a.max_position;
+    double2 cs[2][4];
+#pragma unroll
+    for (int k = 4; k < 6; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cs[k - 4][e] = ok ? a.rope[int64_t(pos) * NPAIR + 4 * (4 * k + g - 16) + e] : double2{0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qreg[rt][k][e] = uint32_t(f32_to_bf16(__uint_as_float(raw[k][e] << 16) * a.qscale)) |
+                         (uint32_t(f32_to_bf16(__uint_as_float(raw[k][e] & 0xffff0000u) * a.qscale)) << 16);
+#pragma unroll
+    for (int k = 4; k < 6; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y0 = __builtin_nanf(""), y1 = __builtin_nanf("");
+        if (ok) {
+          const double x0 = __uint_as_float(raw[k][e] << 16), x1 = __uint_as_float(raw[k][e] & 0xffff0000u);
+          const double2 c = cs[k - 4][e];
+          y0 = float((x0 * c.x - x1 * c.y) * double(a.qscale));
+          y1 = float((x0 * c.y + x1 * c.x) * double(a.qscale));
+        }
+        qreg[rt][k][e] = uint32_t(f32_to_bf16(y0)) | (uint32_t(f32_to_bf16(y1)) << 16);
+      }
+  }
+
+  // the query loads are complete before the loop (the compiler cannot tell them from the transfers
+  // in flight and would otherwise wait for all of them inside it); the first tiles, issued above,
+  // land meanwhile
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int k = 0; k < 6; ++k) asm volatile("" ::"v"(qreg[rt][k]));
   for (int i = 0; i < ntile; ++i) {
     const int ahead = ntile - 1 - i < NS - 2 ? ntile - 1 - i : NS - 2;  // tiles issued after i
     if (ahead <= 0)
@@ -287,60 +296,93 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
       asm volatile("" : "+v"(sa));
       const lds_char_t* sub0 = (const lds_char_t*)uintptr_t(sa);
       const lds_char_t* sub1 = sub0 + kSubBytes;
-      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      // scores of both row tiles from one read of each key operand
+      f32x4_t sc[2][2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) sc[rt][0] = sc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
-        s0 = mfma32v(*(const lds_u32x4_t*)(sub0 + sc_off + 512 * k), qreg[k], s0);
-        s1 = mfma32v(*(const lds_u32x4_t*)(sub1 + sc_off + 512 * k), qreg[k], s1);
+        const u32x4_t k0 = *(const lds_u32x4_t*)(sub0 + sc_off + 512 * k);
+        const u32x4_t k1 = *(const lds_u32x4_t*)(sub1 + sc_off + 512 * k);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          sc[rt][0] = mfma32v(k0, qreg[rt][k], sc[rt][0]);
+          sc[rt][1] = mfma32v(k1, qreg[rt][k], sc[rt][1]);
+        }
       }
-      // lane (r16, g) holds tokens 4g + e of each sub-block for row r16; causal mask t <= p_row
-      float sv[8];
-      float mb = -INFINITY;
+      // lane (r16, g) holds tokens 4g + e of each sub-block for row r16 of each tile.  A pair wholly
+      // visible to every row of the wave (all but the diagonal pairs) needs no mask, and only the
+      // lane's own maximum is compared with the reference; the row maximum is reduced across the
+      // lane groups only when some score passes it by the slack (the reference, moved only there,
+      // stays the same in the four lanes of a row)
+      u32x4_t pb[2];
+      const bool full = tpair + 31 <= p_wmin;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sv[e] = (tpair + 4 * g + e <= p_row) ? s0[e] : -INFINITY;
-        sv[4 + e] = (tpair + 16 + 4 * g + e <= p_row) ? s1[e] : -INFINITY;
+      for (int rt = 0; rt < 2; ++rt) {
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = sc[rt][0][e];
+          sv[4 + e] = sc[rt][1][e];
+        }
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[e] = (tpair + 4 * g + e <= p_row[rt]) ? sv[e] : -INFINITY;
+            sv[4 + e] = (tpair + 16 + 4 * g + e <= p_row[rt]) ? sv[4 + e] : -INFINITY;
+          }
+        }
+        float ml = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        if (__any(ml > m[rt] + kMaxSlack)) {
+          float mb = fmaxf(ml, __shfl_xor(ml, 16, 64));
+          mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+          const float mn = fmaxf(m[rt], mb);
+          const float alpha = (m[rt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mn);
+          lsum[rt] *= alpha;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) acc[rt][jj] *= alpha;
+          m[rt] = mn;
+        }
+        float p[8];
+        if (full) {  // every score finite, and m finite after the check above
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m[rt]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m[rt]);
+        }
+        lsum[rt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pb[rt] = u32x4_t{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                         cvt_pk_bf16(p[6], p[7])};
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mb = fmaxf(mb, sv[e]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      if (__any(mb > m + kMaxSlack)) {
-        const float mn = fmaxf(m, mb);
-        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-        lsum *= alpha;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc[jj] *= alpha;
-        m = mn;
-      }
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m);
-      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      const u32x4_t pb = u32x4_t{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
-                                 cvt_pk_bf16(p[6], p[7])};
-      // P.V: K = the 32 tokens of the pair, in the order of pb
+      // P.V: K = the 32 tokens of the pair, in the order of pb; one read of V feeds both tiles
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub0 + tr_off + 256 * jj));
         const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub1 + tr_off + 256 * jj));
         const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0), a1 = __builtin_bit_cast(u32x2_t, v1);
-        acc[jj] = mfma32v(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pb, acc[jj]);
+        const u32x4_t av = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt][jj] = mfma32v(av, pb[rt], acc[rt][jj]);
       }
     }
     asm volatile("" ::: "memory");
   }
 
   // out = acc / l for the rows of the chunk; lane (r16, g) holds dims 16 jj + 4g .. + 3
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (rw < n) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(c0 + rw) * a.H + h) * DV + 4 * g;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      *reinterpret_cast<u32x2_t*>(o + 16 * jj) =
-          u32x2_t{cvt_pk_bf16(acc[jj][0] * inv, acc[jj][1] * inv), cvt_pk_bf16(acc[jj][2] * inv, acc[jj][3] * inv)};
+  for (int rt = 0; rt < 2; ++rt) {
+    float l = lsum[rt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (rw[rt] < n) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(c0 + rw[rt]) * a.H + h) * DV + 4 * g;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        *reinterpret_cast<u32x2_t*>(o + 16 * jj) = u32x2_t{cvt_pk_bf16(acc[rt][jj][0] * inv, acc[rt][jj][1] * inv),
+                                                          cvt_pk_bf16(acc[rt][jj][2] * inv, acc[rt][jj][3] * inv)};
+    }
   }
 }
 
@@ -349,7 +391,7 @@ hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s) {
   if (units > 0x7ffffff0) return hipErrorInvalidValue;
   a.units = int32_t(units);
   const int grid = ((a.units + 7) >> 3) << 3;
-  prefill_attn_kernel<2><<<grid, 256, 0, s>>>(a);
+  prefill_attn_kernel<2><<<grid, 256, 0, s>>>(a);  // two stages: 80 KiB, two workgroups per CU
   return hipGetLastError();
 }
 
