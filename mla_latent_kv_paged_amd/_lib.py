@@ -262,7 +262,7 @@ class MLAContext:
         buf = (ctypes.c_float * max_n)()
         n = ctypes.c_int32()
         _check(self.lib.mla_profile_samples(self.handle, int(kernel_id), buf, int(max_n), ctypes.byref(n)),
-               "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size")
+               "mla_profile_samples")
         return list(buf[:n.value])
 
 

@@ -343,3 +343,26 @@ def test_abi_status_codes_on_device():
         assert e.value.status == -2
     finally:
         run.free()
+
+
+def test_profiling_helpers_on_device():
+    """The inspection helpers the benchmark reads, through the binding: per-kernel event totals and
+    samples after profiled decodes, and the last launch shape."""
+    from mla_latent_kv_paged_amd import K_CACHE_WRITE, K_COMBINE, K_DECODE, K_Q_ABSORB
+    w = W.custom("prof", "bf16", 16, [300, 40], seed=52)
+    run = GpuRun(w)
+    try:
+        run.ctx.profile_enable(True)
+        for _ in range(3):
+            run.decode()
+        for kid in (K_Q_ABSORB, K_DECODE, K_COMBINE):
+            ms, n = run.ctx.profile_read(kid)
+            assert n == 3 and ms > 0.0, (kid, ms, n)
+            samples = run.ctx.profile_samples(kid)
+            assert len(samples) == 3 and all(x > 0.0 for x in samples), (kid, samples)
+        assert run.ctx.profile_read(K_CACHE_WRITE)[1] == 0
+        run.ctx.profile_enable(False)
+        shape = run.ctx.last_decode_shape()
+        assert shape["n_split"] >= 1 and shape["waves"] >= 1, shape
+    finally:
+        run.free()
