@@ -90,24 +90,42 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
     lds_barrier();
   }
   const char* cache = static_cast<const char*>(a.cache);
+  const char* zero = static_cast<const char*>(a.zero_block);  // >= 1,152 zero bytes
   const int* bt = a.block_table + int64_t(b) * a.bt_stride;
   uint16_t* kvrow0 = a.kv + (int64_t(b) * a.H + h) * a.t_pad * kKV;
   // A operand of MFMA (dim tile jt, K step s): row 16 jt + r16, granule 4 s + g
   const lds_char_t* wa = (const lds_char_t*)wl + r16 * (DC * 2);
 
-  // wave w: tokens t0 + 64 w + 16 st + (lane % 16), st = 0..3
+  // wave w: tokens t0 + 64 w + 16 st + (lane % 16), st = 0..3; the next sub-tile's latent rows are
+  // loaded while the current one is multiplied
+  // sub-tile st is paged block (t0 + 64 w) / 16 + st: its id, read once here
+  int bid[4];
+#pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int tb = t0 + 64 * w + 16 * st;
-    if (tb >= ctx) break;
-    const int tok = tb + r16;
-    const bool tv = tok < ctx;
-    int phys = tv ? bt[tok / BLK] : -1;
-    const bool ok = unsigned(phys) < unsigned(a.num_blocks);
-    const char* crow = cache + (int64_t(ok ? phys : 0) * BLK + tok % BLK) * (ROW * 2);
-    u32x4_t bq[16];  // B operand, K step s: the token's latent values 32 s + 8 g .. + 7
+    bid[st] = tb < ctx ? bt[tb / BLK] : -1;
+  }
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      bq[s] = ok ? *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * g) : u32x4_t{0u, 0u, 0u, 0u};
+  for (int st = 0; st < 4; ++st) asm volatile("" ::"v"(bid[st]));  // complete before the row loads
+  auto load_b = [&](int st, u32x4_t (&bq)[16]) {
+    const int tok = t0 + 64 * w + 16 * st + r16;
+    const int phys = tok < ctx ? bid[st] : -1;
+    const bool ok = unsigned(phys) < unsigned(a.num_blocks);
+    // rows past the context or of an invalid block read the zero block: no divergent loads, which
+    // would make the compiler wait for every load in flight
+    const char* crow = ok ? cache + (int64_t(phys) * BLK + tok % BLK) * (ROW * 2) : zero;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) bq[s] = *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * g);
+  };
+  u32x4_t bq[2][16];  // B operand, K step s: the token's latent values 32 s + 8 g .. + 7
+  load_b(0, bq[0]);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int tb = t0 + 64 * w + 16 * st;
+    if (st + 1 < 4) load_b(st + 1, bq[(st + 1) & 1]);  // unconditional (zero rows past the context)
+    if (tb >= ctx) continue;
+    const u32x4_t(&cb)[16] = bq[st & 1];
+    const int tok = tb + r16;
     f32x4_t acc[8];
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -116,11 +134,11 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
         const u32x4_t av = *(const lds_u32x4_t*)(wa + jt * 16 * (DC * 2) + 16 * ((4 * s + g) ^ r16));
-        acc[jt] = mfma32v(av, bq[s], acc[jt]);
+        acc[jt] = mfma32v(av, cb[s], acc[jt]);
       }
     }
     // D[dim][token]: lane (token r16, g) holds dims 16 jt + 4 g .. + 3
-    if (tv) {
+    if (tok < ctx) {
       uint16_t* dst = kvrow0 + int64_t(tok) * kKV + (part ? DN + DR : 0) + 4 * g;
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt)
@@ -130,14 +148,11 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
     if (part == 0) {  // rope keys of the 16 tokens: lane -> token lane / 4, values 16 (lane % 4) .. + 15
       const int rt = tb + (lane >> 2);
       if (rt < ctx) {
-        const int rp = bt[rt / BLK];
+        const int rp = bid[st];
         const bool rok = unsigned(rp) < unsigned(a.num_blocks);
-        u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-        if (rok) {
-          const char* src = cache + (int64_t(rp) * BLK + rt % BLK) * (ROW * 2) + DC * 2 + 32 * (lane & 3);
-          v0 = *reinterpret_cast<const u32x4_t*>(src);
-          v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
-        }
+        const char* src = (rok ? cache + (int64_t(rp) * BLK + rt % BLK) * (ROW * 2) + DC * 2 : zero) + 32 * (lane & 3);
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src);
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(kvrow0 + int64_t(rt) * kKV + DN + 16 * (lane & 3));
         dst[0] = v0;
         dst[1] = v1;
