@@ -368,9 +368,8 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
 }
 
 namespace {
-constexpr int kPrefillTokPad = 256;  // expansion workgroup granularity
-int64_t prefill_tpad(int32_t max_seq_len) {
-  return (int64_t(max_seq_len) + kPrefillTokPad - 1) / kPrefillTokPad * kPrefillTokPad;
+int64_t prefill_tpad(int32_t max_seq_len) {  // a whole number of expansion workgroups
+  return (int64_t(max_seq_len) + kPrefillTokens - 1) / kPrefillTokens * kPrefillTokens;
 }
 }  // namespace
 

@@ -89,6 +89,9 @@ struct DecodeArgs {
 // Chunked prefill (mla_prefill).  Sequence b owns query rows cu_q_lens[b] .. cu_q_lens[b+1]-1 at
 // positions ctx_b - n_b .. ctx_b - 1.  Workspace: kv [batch, H, t_pad, DN + DR + DV] expanded
 // token rows [K_nope | k_pe | V] per (sequence, head).
+// tokens per expansion workgroup; the workspace's rows per (sequence, head) are a multiple of it
+constexpr int kPrefillTokens = 1024;
+
 struct PrefillArgs {
   int32_t batch;
   int32_t H;
@@ -104,7 +107,7 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   int32_t max_seq_len;
   int32_t max_position;
-  int32_t t_pad;               // token rows per (sequence, head) in kv: max_seq_len rounded up to 256
+  int32_t t_pad;               // token rows per (sequence, head) in kv: max_seq_len rounded up to kPrefillTokens
   const double2* rope;
   float qscale;                // softmax scale * log2(e)
   const uint16_t* W_uk;        // [H, DN, DC]

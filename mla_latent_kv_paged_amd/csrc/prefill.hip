@@ -39,7 +39,8 @@ constexpr int kGQ = kKV / 64;              // 5 granule groups (8 granules of 8 
 constexpr int kSubBytes = 16 * kKVBytes;   // a 16-token sub-block in LDS: 2 x 5 chunks of 1 KiB
 constexpr int kTileBytes = 4 * kSubBytes;  // 64 tokens
 constexpr int kQTile = 128;                // query rows per attention workgroup (32 per wave)
-constexpr int kExpandTokens = 256;         // tokens per expansion workgroup
+constexpr int kExpandTokens = kPrefillTokens;  // tokens per expansion workgroup (256 per wave)
+constexpr int kSubPerWave = kExpandTokens / 64;  // 16-token sub-tiles per wave
 constexpr float kMaxSlack = 8.f;           // lazy-rescale slack (log2 units), as in the decode
 
 // chunk length of sequence b, clamped to the launch bound; 0 for an inconsistent prefix sum
@@ -96,35 +97,27 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
   // A operand of MFMA (dim tile jt, K step s): row 16 jt + r16, granule 4 s + g
   const lds_char_t* wa = (const lds_char_t*)wl + r16 * (DC * 2);
 
-  // wave w: tokens t0 + 64 w + 16 st + (lane % 16), st = 0..3; the next sub-tile's latent rows are
-  // loaded while the current one is multiplied
-  // sub-tile st is paged block (t0 + 64 w) / 16 + st: its id, read once here
-  int bid[4];
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int tb = t0 + 64 * w + 16 * st;
-    bid[st] = tb < ctx ? bt[tb / BLK] : -1;
-  }
-#pragma unroll
-  for (int st = 0; st < 4; ++st) asm volatile("" ::"v"(bid[st]));  // complete before the row loads
+  // wave w: tokens t0 + 16 kSubPerWave w + 16 st + (lane % 16); the next sub-tile's latent rows are
+  // loaded while the current one is multiplied (two register buffers, the loop unrolled by two)
+  const int tw = t0 + 16 * kSubPerWave * w;
+  // sub-tile st is one paged block: the wave's kSubPerWave block ids, read once (lane st holds id st)
+  static_assert(kSubPerWave <= 64, "one id per lane");
+  const int ids = (lane < kSubPerWave && tw + 16 * lane < ctx) ? bt[tw / BLK + lane] : -1;
+  asm volatile("" ::"v"(ids));  // complete before the row loads
   auto load_b = [&](int st, u32x4_t (&bq)[16]) {
-    const int tok = t0 + 64 * w + 16 * st + r16;
-    const int phys = tok < ctx ? bid[st] : -1;
-    const bool ok = unsigned(phys) < unsigned(a.num_blocks);
+    const int tb = tw + 16 * st;
+    const int tok = tb + r16;
+    const int phys = __builtin_amdgcn_readlane(ids, st);  // st <= kSubPerWave < 64: -1 past the range
+    const bool ok = tok < ctx && unsigned(phys) < unsigned(a.num_blocks);
     // rows past the context or of an invalid block read the zero block: no divergent loads, which
     // would make the compiler wait for every load in flight
     const char* crow = ok ? cache + (int64_t(phys) * BLK + tok % BLK) * (ROW * 2) : zero;
 #pragma unroll
     for (int s = 0; s < 16; ++s) bq[s] = *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * g);
+    return phys;
   };
-  u32x4_t bq[2][16];  // B operand, K step s: the token's latent values 32 s + 8 g .. + 7
-  load_b(0, bq[0]);
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int tb = t0 + 64 * w + 16 * st;
-    if (st + 1 < 4) load_b(st + 1, bq[(st + 1) & 1]);  // unconditional (zero rows past the context)
-    if (tb >= ctx) continue;
-    const u32x4_t(&cb)[16] = bq[st & 1];
+  auto step = [&](int st, const u32x4_t (&cb)[16], int phys) {
+    const int tb = tw + 16 * st;
     const int tok = tb + r16;
     f32x4_t acc[8];
 #pragma unroll
@@ -148,15 +141,30 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
     if (part == 0) {  // rope keys of the 16 tokens: lane -> token lane / 4, values 16 (lane % 4) .. + 15
       const int rt = tb + (lane >> 2);
       if (rt < ctx) {
-        const int rp = bid[st];
-        const bool rok = unsigned(rp) < unsigned(a.num_blocks);
-        const char* src = (rok ? cache + (int64_t(rp) * BLK + rt % BLK) * (ROW * 2) + DC * 2 : zero) + 32 * (lane & 3);
+        const bool rok = unsigned(phys) < unsigned(a.num_blocks);
+        const char* src = (rok ? cache + (int64_t(phys) * BLK + rt % BLK) * (ROW * 2) + DC * 2 : zero) + 32 * (lane & 3);
         const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src);
         const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(kvrow0 + int64_t(rt) * kKV + DN + 16 * (lane & 3));
         dst[0] = v0;
         dst[1] = v1;
       }
+    }
+  };
+  if (tw >= ctx) return;
+  // groups of four sub-tiles; within a group the buffers alternate at compile time, and the
+  // prefetch is unconditional (past the wave's range it reads the zero block: lane kSubPerWave's id
+  // is -1), so that no branch guards a load
+  u32x4_t bq[2][16];
+  int ph[2];
+  ph[0] = load_b(0, bq[0]);
+  for (int G = 0; G < kSubPerWave / 4; ++G) {
+    if (tw + 64 * G >= ctx) break;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int cur = 4 * G + st;
+      ph[(st + 1) & 1] = load_b(cur + 1, bq[(st + 1) & 1]);
+      if (tw + 16 * cur < ctx) step(cur, bq[st & 1], ph[st & 1]);
     }
   }
 }
