@@ -180,7 +180,7 @@ hipError_t launch_prefill_expand(PrefillArgs a, hipStream_t s) {
 // ------------------------------------------------------------------------------------------- attn
 
 template <int NS>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   static_assert(NS == 2 || NS == 3, "two or three shared stages");
   __shared__ __attribute__((aligned(16))) char ring_mem[NS * kTileBytes];
 
@@ -311,33 +311,58 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
     if (i + NS - 1 < ntile) issue(i + NS - 1);
     const uint32_t stage = uint32_t(uintptr_t(ring + (i % NS) * kTileBytes));
 
+    // LDS reads run ahead of their use: a pair's twelve key operands before its score MFMAs, its
+    // value operands right after them, and the next pair's key operands before this pair's softmax
+    uint32_t sa = stage;
+    asm volatile("" : "+v"(sa));
+    const lds_char_t* const st0 = (const lds_char_t*)uintptr_t(sa);
+    auto load_k = [&](int pr, u32x4_t (&kk)[12]) {
+      const lds_char_t* sub0 = st0 + 2 * pr * kSubBytes;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        kk[k] = *(const lds_u32x4_t*)(sub0 + sc_off + 512 * k);
+        kk[6 + k] = *(const lds_u32x4_t*)(sub0 + kSubBytes + sc_off + 512 * k);
+      }
+    };
+    u32x4_t kr[12];  // one buffer: the next pair's reads are issued after this pair's score MFMAs
+    if (64 * i <= p_wave) load_k(0, kr);
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {  // sub-blocks 2 pr and 2 pr + 1
       const int tpair = 64 * i + 32 * pr;
       if (tpair > p_wave) break;  // nothing visible to this wave's rows from here on
-      uint32_t sa = stage + uint32_t(2 * pr * kSubBytes);
-      asm volatile("" : "+v"(sa));
-      const lds_char_t* sub0 = (const lds_char_t*)uintptr_t(sa);
+      const lds_char_t* sub0 = st0 + 2 * pr * kSubBytes;
       const lds_char_t* sub1 = sub0 + kSubBytes;
       // scores of both row tiles from one read of each key operand
+      // the accumulators start at -msub (msub = the row's reference, 0 before it has one), so that
+      // the MFMAs produce the exponents s - m directly
       f32x4_t sc[2][2];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) sc[rt][0] = sc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < 2; ++rt) {
+        const float ms = m[rt] == -INFINITY ? 0.f : -m[rt];
+        sc[rt][0] = sc[rt][1] = f32x4_t{ms, ms, ms, ms};
+      }
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
-        const u32x4_t k0 = *(const lds_u32x4_t*)(sub0 + sc_off + 512 * k);
-        const u32x4_t k1 = *(const lds_u32x4_t*)(sub1 + sc_off + 512 * k);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          sc[rt][0] = mfma32v(k0, qreg[rt][k], sc[rt][0]);
-          sc[rt][1] = mfma32v(k1, qreg[rt][k], sc[rt][1]);
+          sc[rt][0] = mfma32v(kr[k], qreg[rt][k], sc[rt][0]);
+          sc[rt][1] = mfma32v(kr[6 + k], qreg[rt][k], sc[rt][1]);
         }
       }
-      // lane (r16, g) holds tokens 4g + e of each sub-block for row r16 of each tile.  A pair wholly
-      // visible to every row of the wave (all but the diagonal pairs) needs no mask, and only the
-      // lane's own maximum is compared with the reference; the row maximum is reduced across the
-      // lane groups only when some score passes it by the slack (the reference, moved only there,
-      // stays the same in the four lanes of a row)
+      u32x4_t vt[8];  // A operands of P.V: V tile jj, tokens of both sub-blocks (K permutation)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub0 + tr_off + 256 * jj));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub1 + tr_off + 256 * jj));
+        const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0), a1 = __builtin_bit_cast(u32x2_t, v1);
+        vt[jj] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+      }
+      if (pr == 0 && tpair + 32 <= p_wave) load_k(1, kr);
+      // lane (r16, g) holds s - msub for tokens 4g + e of each sub-block, row r16 of each tile.  A
+      // pair wholly visible to every row of the wave (all but the diagonal pairs) needs no mask, and
+      // only the lane's own maximum is compared with the reference; the row maximum is reduced
+      // across the lane groups only when some score passes it by the slack or the row has no
+      // reference yet (the reference, moved only there, stays the same in the four lanes of a row)
       u32x4_t pb[2];
       const bool full = tpair + 31 <= p_wmin;
 #pragma unroll
@@ -355,39 +380,36 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
             sv[4 + e] = (tpair + 16 + 4 * g + e <= p_row[rt]) ? sv[4 + e] : -INFINITY;
           }
         }
-        float ml = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        if (__any(ml > m[rt] + kMaxSlack)) {
+        const float ml = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        const bool need = m[rt] == -INFINITY ? ml > -INFINITY : ml > kMaxSlack;
+        if (__any(need)) {
+          const float msub = m[rt] == -INFINITY ? 0.f : m[rt];
           float mb = fmaxf(ml, __shfl_xor(ml, 16, 64));
           mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-          const float mn = fmaxf(m[rt], mb);
-          const float alpha = (m[rt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mn);
-          lsum[rt] *= alpha;
+          const float mn = fmaxf(m[rt], mb + msub);  // -inf only for a row with nothing visible yet
+          if (mn != -INFINITY) {
+            const float alpha = (m[rt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mn);
+            lsum[rt] *= alpha;
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) acc[rt][jj] *= alpha;
-          m[rt] = mn;
+            for (int jj = 0; jj < 8; ++jj) acc[rt][jj] *= alpha;
+            const float d = msub - mn;  // re-base the exponents on the new reference
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[e] += d;
+            m[rt] = mn;
+          }
         }
         float p[8];
-        if (full) {  // every score finite, and m finite after the check above
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m[rt]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m[rt]);
-        }
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e]);  // exp2(-inf) = 0
         lsum[rt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pb[rt] = u32x4_t{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
                          cvt_pk_bf16(p[6], p[7])};
       }
       // P.V: K = the 32 tokens of the pair, in the order of pb; one read of V feeds both tiles
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub0 + tr_off + 256 * jj));
-        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub1 + tr_off + 256 * jj));
-        const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0), a1 = __builtin_bit_cast(u32x2_t, v1);
-        const u32x4_t av = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+      for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) acc[rt][jj] = mfma32v(av, pb[rt], acc[rt][jj]);
-      }
+        for (int rt = 0; rt < 2; ++rt) acc[rt][jj] = mfma32v(vt[jj], pb[rt], acc[rt][jj]);
     }
     asm volatile("" ::: "memory");
   }
