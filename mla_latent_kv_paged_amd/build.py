@@ -38,10 +38,11 @@ def _hipcc():
 # Per-source flags.  The decode kernels keep their MFMA accumulators in VGPRs so that the online
 # softmax rescale runs on them in place (no AGPR<->VGPR copies); their block buffers then take the
 # AGPR half of the register file.  The 32-row kernel uses the flag for its score MFMAs and pins its
-# P.C accumulator to the AGPRs itself.
+# P.C accumulator to the AGPRs itself.  The prefill kernels build without it: the attention kernel's
+# code is the same either way (two waves per SIMD leave no AGPRs), and the expansion kernel (one
+# wave per SIMD) keeps its accumulators in AGPRs, which leaves VGPRs for reading ahead.
 PER_FILE = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-            "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-            "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+            "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src, extra, verbose):

@@ -14,7 +14,8 @@
 //  * expand: per (sequence, 256 tokens, head, K or V): W_uk[h] or W_uv[h] (128 x 512) is staged in
 //    LDS once (XOR-swizzled granules, conflict-free reads), the tokens' latent rows are the
 //    B operand straight from the paged cache; v_mfma_f32_16x16x32_bf16 with the 128 output
-//    dimensions on M and 16 tokens on N.  Part K also copies the tokens' rope keys.  Output rows
+//    dimensions on M and 16 tokens on N, the A operands of the next K step read from LDS while the
+//    current step's MFMAs run.  Part K also copies the tokens' rope keys.  Output rows
 //    [K_nope | k_pe | V] (320 bf16) per (sequence, head, token), rounded to bf16 once.
 //  * attn: one workgroup per (sequence, head, 128 query rows), four waves of 32 rows (two 16-row
 //    tiles, so that every key and value operand read from LDS feeds two MFMAs).  Keys move
@@ -79,7 +80,9 @@ __device__ __forceinline__ float add_pk_bf16(uint32_t x, float acc) {
 
 // ----------------------------------------------------------------------------------------- expand
 
-__global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
+// 128 KiB of LDS: one workgroup, so one wave per SIMD, per CU; the compiler is told so, and may use
+// the whole register file for reading ahead
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_expand_kernel(PrefillArgs a) {
   // W_uk[h] or W_uv[h]: 128 rows of 512 values; granule c (8 values) of row r at slot c ^ (r % 16)
   __shared__ __attribute__((aligned(16))) char wl[DN * DC * 2];
   static_assert(DN == DV, "one staging buffer for both parts");
@@ -145,13 +148,19 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
     f32x4_t acc[8];
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the eight A operands of K step s + 1 are read while the MFMAs of step s run
+    u32x4_t av[2][8];
+    auto load_a = [&](int s, u32x4_t (&d)[8]) {
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) d[jt] = *(const lds_u32x4_t*)(wa + jt * 16 * (DC * 2) + 16 * ((4 * s + g) ^ r16));
+    };
+    load_a(0, av[0]);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
+      if (s + 1 < 16) load_a(s + 1, av[(s + 1) & 1]);
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        const u32x4_t av = *(const lds_u32x4_t*)(wa + jt * 16 * (DC * 2) + 16 * ((4 * s + g) ^ r16));
-        acc[jt] = mfma32v(av, cb[s], acc[jt]);
-      }
+      for (int jt = 0; jt < 8; ++jt) acc[jt] = mfma32v(av[s & 1][jt], cb[s], acc[jt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // D[dim][token]: lane (token r16, g) holds dims 16 jt + 4 g .. + 3
     if (tok < ctx) {
