@@ -56,6 +56,9 @@ def parse():
                          "FP8 E4M3 latent rows of 656 bytes (MLA_BF16_FP8), bf16 everything else")
     ap.add_argument("--split-blocks", type=int, default=0, help="force the split size (0 = library choice)")
     ap.add_argument("--waves", type=int, default=0, help="force waves per decode workgroup (0 = library choice)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="step as mla_cache_write + mla_decode (two calls) instead of mla_decode_step, which "
+                         "runs the cache write in the query absorption's launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences in the oracle's timed sample (capped at "
                     "the batch)")
@@ -331,7 +334,7 @@ def main():
     if args.mode in ("prefill", "prefill-only"):
         prefill_main(args)
         return
-    from mla_latent_kv_paged_amd import MLAContext, K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE
+    from mla_latent_kv_paged_amd import MLAContext, K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE, K_PREP
 
     w = make_workload(args)
     dt = torch.bfloat16 if w.storage == "bf16" else torch.float32
@@ -379,10 +382,13 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
 
-    def step(i):
-        p = pools[i % len(pools)]
-        ctx.cache_write(nc, nk, npos, nslot, p)
-        ctx.decode(q, p, bt, sl, max_ctx, q_len=w.q_len, out=out)
+    def step(i, p=None):
+        p = pools[i % len(pools)] if p is None else p
+        if args.separate_write:
+            ctx.cache_write(nc, nk, npos, nslot, p)
+            ctx.decode(q, p, bt, sl, max_ctx, q_len=w.q_len, out=out)
+        else:
+            ctx.decode_step(nc, nk, npos, nslot, q, p, bt, sl, max_ctx, q_len=w.q_len, out=out)
 
     if args.mode == "decode-only":
         for i in range(args.warmup + args.steps):
@@ -410,8 +416,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
     kern = {}
-    for name, kid in (("cache_write", K_CACHE_WRITE), ("q_absorb", K_Q_ABSORB), ("decode", K_DECODE),
-                      ("combine", K_COMBINE)):
+    # the step's first launch: cache write + query absorption (mla_decode_step), or the two apart
+    first = (("prep", K_PREP),) if not args.separate_write else (("cache_write", K_CACHE_WRITE),
+                                                                   ("q_absorb", K_Q_ABSORB))
+    for name, kid in first + (("decode", K_DECODE), ("combine", K_COMBINE)):
         tot, n = ctx.profile_read(kid)
         kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
     dec_samples = np.array(ctx.profile_samples(K_DECODE)) * 1e3
@@ -430,8 +438,7 @@ def main():
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
-        ctx.cache_write(nc, nk, npos, nslot, pools[0])
-        ctx.decode(q, pools[0], bt, sl, max_ctx, q_len=w.q_len, out=out)
+        step(i, pools[0])
     e1.record()
     torch.cuda.synchronize()
     unflushed_us = e0.elapsed_time(e1) / args.steps * 1e3
@@ -444,7 +451,8 @@ def main():
     decode_us = kern["decode"]["avg_us"]
     flops_attn = w.total_ctx * w.num_heads * w.q_len * 2 * (576 + 512)
     flops_gemm = 2 * w.n_q * w.num_heads * 131072  # q_nope . W_uk and o_lat . W_uv^T
-    mla_decode_us = kern["q_absorb"]["avg_us"] + decode_us + kern["combine"]["avg_us"]
+    # (with mla_decode_step the first launch also writes the new tokens' rows)
+    mla_decode_us = kern["prep" if "prep" in kern else "q_absorb"]["avg_us"] + decode_us + kern["combine"]["avg_us"]
     achieved = latent_bytes / (decode_us * 1e-6) / 1e9
     traffic = traffic_entry(args)
     rows32 = (w.num_heads * w.q_len) % 32 == 0
@@ -478,6 +486,7 @@ def main():
         "unflushed_us_per_step": round(unflushed_us, 2),
         "decode_latent_gbps": round(achieved, 1),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+        "step_calls": "mla_cache_write + mla_decode" if args.separate_write else "mla_decode_step",
         "split": shape,
         "absorb_weights_ms_once": round(absorb_ms, 2),
         "rotated_pools": len(pools),

@@ -165,6 +165,23 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
                       const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
 
 /*
+ * mla_decode_step -- one decode step of the layer ([P-vllm] §2.2 wrapper forward: the new tokens'
+ * cache write by slot_mapping, then attention): exactly mla_cache_write(ctx, c_kv, ..., num_tokens,
+ * kv_cache, num_blocks) followed by mla_decode(ctx, q, ..., kv_cache, num_blocks, ...), with the
+ * same arguments, semantics and results (cache rows and out bit for bit).  With bf16 storage (and
+ * MLA_BF16_FP8 rows) the cache write runs in the query absorption's launch: the two are
+ * independent, and only the attention kernel after them reads the new rows.  fp32 storage
+ * launches them one after the other.  num_tokens may be 0 (no write).
+ * Every argument is checked before anything is launched: a failing call writes nothing.
+ * Returns what either call returns for its arguments.
+ */
+mla_status mla_decode_step(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
+                           int64_t k_pe_row_stride, const int32_t* positions, const int32_t* slot_mapping,
+                           int32_t num_tokens, const void* q, int32_t batch, int32_t q_len, void* kv_cache,
+                           int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                           const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
+
+/*
  * mla_prefill -- chunked prefill over the latent cache, naive form: K and V are expanded from the
  * cached latent once per chunk and the new tokens attend to them causally, MHA-style.  The pages'
  * naive MLA ([P-mini] MLA 的数学结构 and 版本 1: K_nope = C W_uk^T, V = C W_uv^T per head, K_pe
@@ -235,7 +252,8 @@ enum {
   MLA_K_COMBINE = 3,
   MLA_K_PF_EXPAND = 4, /* mla_prefill: K/V expansion */
   MLA_K_PF_ATTN = 5,   /* mla_prefill: causal attention (queries prepared in it) */
-  MLA_K_COUNT = 6
+  MLA_K_PREP = 6,      /* mla_decode_step: cache write and query absorption in one launch */
+  MLA_K_COUNT = 7
 };
 mla_status mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* Synchronises the recorded events and returns the summed milliseconds and launch count of

@@ -18,9 +18,9 @@ MLA_F32, MLA_BF16, MLA_BF16_FP8 = 0, 1, 2
 FP8_ROW_BYTES = 656  # FP8 cache row: 512 e4m3 codes | 64 bf16 rope values | 4 fp32 group scales
 MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2, -3, -4, -5
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
-K_PF_EXPAND, K_PF_ATTN = 4, 5
+K_PF_EXPAND, K_PF_ATTN, K_PREP = 4, 5, 6
 
-EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_free", "mla_status_string",
+EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_decode_step", "mla_free", "mla_status_string",
            "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",
            "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size")
 
@@ -59,6 +59,8 @@ def load(path=None):
     lib.mla_cache_write.restype = i32
     lib.mla_decode.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
     lib.mla_decode.restype = i32
+    lib.mla_decode_step.argtypes = [vp, vp, i64, vp, i64, vp, vp, i32, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
+    lib.mla_decode_step.restype = i32
     lib.mla_prefill.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, vp, vp]
     lib.mla_prefill.restype = i32
     lib.mla_prefill_workspace_size.argtypes = [vp, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
@@ -163,6 +165,11 @@ class MLAContext:
 
     # -- the two per-step calls
     def cache_write(self, c_kv, k_pe, positions, slot_mapping, kv_cache, stream=None):
+        w = self._write_args(c_kv, k_pe, positions, slot_mapping, kv_cache)
+        st = self.lib.mla_cache_write(self.handle, *w, _ptr(kv_cache), int(kv_cache.shape[0]), _stream_ptr(stream))
+        _check(st, "mla_cache_write")
+
+    def _write_args(self, c_kv, k_pe, positions, slot_mapping, kv_cache):
         torch = _torch()
         T = int(positions.shape[0]) if positions is not None else 0
         _need(kv_cache, "kv_cache", self.cache_dtype)
@@ -175,10 +182,30 @@ class MLAContext:
             _need(slot_mapping, "slot_mapping", torch.int32, shape=(T,))
             if c_kv.shape != (T, 512) or c_kv.stride(1) != 1 or k_pe.shape != (T, 64) or k_pe.stride(1) != 1:
                 raise ValueError("c_kv must be [T, 512] and k_pe [T, 64] with unit inner stride")
-        st = self.lib.mla_cache_write(self.handle, _ptr(c_kv), c_kv.stride(0) if T else 512, _ptr(k_pe),
-                                      k_pe.stride(0) if T else 64, _ptr(positions), _ptr(slot_mapping), T,
-                                      _ptr(kv_cache), int(kv_cache.shape[0]), _stream_ptr(stream))
-        _check(st, "mla_cache_write")
+        return (_ptr(c_kv), c_kv.stride(0) if T else 512, _ptr(k_pe), k_pe.stride(0) if T else 64, _ptr(positions),
+                _ptr(slot_mapping), T)
+
+    def decode_step(self, c_kv, k_pe, positions, slot_mapping, q, kv_cache, block_table, seq_lens, max_seq_len,
+                    q_len=1, out=None, stream=None):
+        """cache_write(c_kv, k_pe, positions, slot_mapping, kv_cache) then decode(q, kv_cache, ...), as one
+        call (mla_decode_step): the same results, the cache write in the query absorption's launch."""
+        torch = _torch()
+        w = self._write_args(c_kv, k_pe, positions, slot_mapping, kv_cache)
+        H = self.num_heads
+        batch = int(seq_lens.shape[0])
+        _need(q, "q", self.tdtype, shape=(batch * q_len, H, 192))
+        _need(block_table, "block_table", torch.int32)
+        _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+        if block_table.dim() != 2 or block_table.shape[0] != batch:
+            raise ValueError("block_table must be [batch, stride]")
+        if out is None:
+            out = torch.empty((batch * q_len, H, 128), dtype=self.tdtype, device=q.device)
+        _need(out, "out", self.tdtype, shape=(batch * q_len, H, 128))
+        st = self.lib.mla_decode_step(self.handle, *w, _ptr(q), batch, q_len, _ptr(kv_cache), int(kv_cache.shape[0]),
+                                      _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+                                      int(max_seq_len), _ptr(out), _stream_ptr(stream))
+        _check(st, "mla_decode_step")
+        return out
 
     def decode(self, q, kv_cache, block_table, seq_lens, max_seq_len, q_len=1, out=None, stream=None):
         torch = _torch()

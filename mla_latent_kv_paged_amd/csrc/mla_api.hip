@@ -287,9 +287,15 @@ mla_status mla_cache_write(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
   return hip_status(ctx->fp8 ? launch_cache_write_fp8(a, s) : launch_cache_write(ctx->bf16, a, s));
 }
 
-mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
-                      int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
-                      const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+// mla_decode; with cw, the cache write cw first (mla_decode_step): in the query absorption's launch
+// for bf16 storage, else as its own launch before it
+mla_status decode_impl(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                       const int32_t* seq_lens, int32_t max_seq_len, void* out, hipStream_t s,
+                       const CacheWriteArgs* cw) {
   if (!ctx || !q || !kv_cache || !block_table || !seq_lens || !out) return MLA_EINVAL;
   if (batch < 1 || q_len < 1 || num_blocks <= 0 || max_seq_len < q_len) return MLA_EINVAL;
   const mla_config& cf = ctx->cfg;
@@ -298,7 +304,6 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
     return MLA_ECAP;
   const int max_blocks = (max_seq_len + BLK - 1) / BLK;
   if (block_table_stride < max_blocks) return MLA_EINVAL;
-  hipStream_t s = as_stream(stream);
   const int H = cf.num_heads;
   const int n_q = batch * q_len;
 
@@ -338,12 +343,18 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
   ctx->last_n_split = t32 ? n_wg : n_split;
   ctx->last_waves = waves;
 
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  const bool fused = cw && cw->T > 0 && ctx->bf16;
+  if (cw && cw->T > 0 && !fused) {
+    ProfScope ps(ctx, MLA_K_CACHE_WRITE, s);
+    e = ctx->fp8 ? launch_cache_write_fp8(*cw, s) : launch_cache_write(ctx->bf16, *cw, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
   {
     QAbsorbArgs qa{q, ctx->W_uk, ctx->W_ukT, ctx->rope, seq_lens, q_len, n_q, H, max_seq_len, cf.max_position, ctx->qscale,
                    ctx->qcat};
-    ProfScope ps(ctx, MLA_K_Q_ABSORB, s);
-    e = launch_q_absorb(ctx->bf16, qa, s);
+    ProfScope ps(ctx, fused ? MLA_K_PREP : MLA_K_Q_ABSORB, s);
+    e = fused ? launch_decode_prep(qa, *cw, ctx->fp8, s) : launch_q_absorb(ctx->bf16, qa, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {
@@ -365,6 +376,43 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
     e = launch_combine(ctx->bf16, ca, s);
   }
   return hip_status(e);
+}
+
+// the arguments of a cache write, checked as mla_cache_write checks them
+mla_status cache_write_args(const mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
+                            int64_t k_pe_row_stride, const int32_t* positions, const int32_t* slot_mapping,
+                            int32_t num_tokens, void* kv_cache, int32_t num_blocks, CacheWriteArgs* a) {
+  if (!ctx || num_tokens < 0) return MLA_EINVAL;
+  if (num_tokens > 0 && (!c_kv || !k_pe || !positions || !slot_mapping || !kv_cache || num_blocks <= 0))
+    return MLA_EINVAL;
+  if (num_tokens > 0 && (c_kv_row_stride < DC || k_pe_row_stride < DR)) return MLA_EINVAL;
+  *a = CacheWriteArgs{c_kv, c_kv_row_stride, k_pe, k_pe_row_stride, positions, slot_mapping, num_tokens,
+                      kv_cache, int64_t(num_blocks) * BLK, ctx->gamma, ctx->rope, ctx->cfg.max_position,
+                      double(ctx->cfg.rms_eps)};
+  return MLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+                      int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                      const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream) {
+  return decode_impl(ctx, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride, seq_lens,
+                     max_seq_len, out, as_stream(stream), nullptr);
+}
+
+mla_status mla_decode_step(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
+                           int64_t k_pe_row_stride, const int32_t* positions, const int32_t* slot_mapping,
+                           int32_t num_tokens, const void* q, int32_t batch, int32_t q_len, void* kv_cache,
+                           int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                           const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream) {
+  CacheWriteArgs cw;
+  const mla_status st = cache_write_args(ctx, c_kv, c_kv_row_stride, k_pe, k_pe_row_stride, positions, slot_mapping,
+                                         num_tokens, kv_cache, num_blocks, &cw);
+  if (st != MLA_OK) return st;
+  return decode_impl(ctx, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride, seq_lens,
+                     max_seq_len, out, as_stream(stream), &cw);
 }
 
 namespace {

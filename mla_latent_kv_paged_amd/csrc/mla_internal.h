@@ -147,6 +147,9 @@ hipError_t launch_absorb(bool bf16, const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_cache_write(bool bf16, const CacheWriteArgs& a, hipStream_t s);
 hipError_t launch_cache_write_fp8(const CacheWriteArgs& a, hipStream_t s);  // bf16 inputs, fp8 rows
 hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s);
+// one launch: the cache write cw (bf16 inputs; bf16 rows, or FP8 rows when fp8) beside the bf16 query
+// absorption a
+hipError_t launch_decode_prep(const QAbsorbArgs& a, const CacheWriteArgs& cw, bool fp8, hipStream_t s);
 // waves: waves per workgroup of the bf16 decode kernel (ignored in fp32 mode)
 hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);

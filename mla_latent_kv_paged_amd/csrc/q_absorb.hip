@@ -12,7 +12,7 @@
 // small to fill the chip; its W_uk^T slice is staged in LDS with one batch of loads.
 // fp32 storage: one workgroup per (head, 16 query rows) on the vector ALUs, W_uk[h] streamed once
 // per workgroup, each thread owning two latent columns.  Both accumulate in fp32.
-#include "mla_internal.h"
+#include "cache_write_impl.h"
 
 namespace mla {
 
@@ -94,11 +94,9 @@ __global__ __launch_bounds__(256) void q_absorb_kernel(QAbsorbArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a, int c_split) {
-  __shared__ u32x4_t wlds[256 * 16];  // up to 256 channels of W_uk^T (64 KiB)
-  const int h = blockIdx.x;
-  const int rb = blockIdx.y;  // 64 query rows
-  const int cp = blockIdx.z;  // part of the 512 channels (one of c_split)
+// workgroup (head h, 64 query rows rb, channel part cp of c_split); wlds: 64 KiB of LDS
+__device__ __forceinline__ void q_absorb_bf16_block(const QAbsorbArgs& a, int c_split, int h, int rb, int cp,
+                                                    u32x4_t* wlds) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
@@ -206,13 +204,55 @@ __global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a, int c
   }
 }
 
+__global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a, int c_split) {
+  __shared__ u32x4_t wlds[256 * 16];  // up to 256 channels of W_uk^T (64 KiB)
+  q_absorb_bf16_block(a, c_split, blockIdx.x, blockIdx.y, blockIdx.z, wlds);
+}
+
+// The decode step's first launch: the two independent steps before the decode kernel in one grid.
+// Workgroups 0 .. ncw - 1 write the new tokens' cache rows (four tokens each, FP8 rows when fp8);
+// the rest are the query absorption's (head, 64 rows, channel part), in its own order.
+__global__ __launch_bounds__(256) void decode_prep_kernel(QAbsorbArgs a, int c_split, CacheWriteArgs cw, int ncw,
+                                                          int fp8) {
+  __shared__ u32x4_t wlds[256 * 16];
+  const int bid = int(blockIdx.x);
+  if (bid < ncw) {
+    const int j = bid * 4 + int(threadIdx.x >> 6);
+    if (fp8)
+      cache_write_fp8_token(cw, j, threadIdx.x & 63);
+    else
+      cache_write_token<uint16_t>(cw, j, threadIdx.x & 63);
+    return;
+  }
+  const int q = bid - ncw;
+  const int rbs = (a.n_q + 63) / 64;
+  q_absorb_bf16_block(a, c_split, q % a.H, (q / a.H) % rbs, q / (a.H * rbs), wlds);
+}
+
+namespace {
+// channels split over c_split workgroups only as far as needed for about 512 workgroups; at most
+// 256 channels per workgroup (its W_uk^T slice fits 64 KiB of LDS)
+int q_absorb_c_split(const QAbsorbArgs& a) {
+  const int rbs = (a.n_q + 63) / 64;
+  int c_split = 2;
+  while (c_split < 8 && int64_t(a.H) * rbs * c_split < 512) c_split *= 2;
+  return c_split;
+}
+}  // namespace
+
+hipError_t launch_decode_prep(const QAbsorbArgs& a, const CacheWriteArgs& cw, bool fp8, hipStream_t s) {
+  const int c_split = q_absorb_c_split(a);
+  const int64_t ncw = cw.T > 0 ? (int64_t(cw.T) + 3) / 4 : 0;
+  const int64_t grid = ncw + int64_t(a.H) * ((a.n_q + 63) / 64) * c_split;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  decode_prep_kernel<<<int(grid), 256, 0, s>>>(a, c_split, cw, int(ncw), fp8 ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s) {
   if (bf16) {
-    // channels split over c_split workgroups only as far as needed for about 512 workgroups
-    const int rbs = (a.n_q + 63) / 64;
-    int c_split = 2;  // at most 256 channels per workgroup (its W_uk^T slice fits 64 KiB of LDS)
-    while (c_split < 8 && int64_t(a.H) * rbs * c_split < 512) c_split *= 2;
-    dim3 grid(a.H, rbs, c_split);
+    const int c_split = q_absorb_c_split(a);
+    dim3 grid(a.H, (a.n_q + 63) / 64, c_split);
     q_absorb_bf16_kernel<<<grid, 256, 0, s>>>(a, c_split);
   } else {
     dim3 grid(a.H, (a.n_q + 15) / 16);
