@@ -12,6 +12,8 @@
 // small to fill the chip; its W_uk^T slice is staged in LDS with one batch of loads.
 // fp32 storage: one workgroup per (head, 16 query rows) on the vector ALUs, W_uk[h] streamed once
 // per workgroup, each thread owning two latent columns.  Both accumulate in fp32.
+// The decode step's first launch (decode_prep_kernel) adds the new tokens' cache-write workgroups
+// to the bf16 grid: the two steps are independent and latency-bound at decode sizes.
 #include "cache_write_impl.h"
 
 namespace mla {
