@@ -137,6 +137,12 @@ int choose_split_blocks(const mla_ctx* c, int units, int max_blocks, int waves) 
 
 }  // namespace
 
+namespace {
+mla_status cache_write_args(const mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
+                            int64_t k_pe_row_stride, const int32_t* positions, const int32_t* slot_mapping,
+                            int32_t num_tokens, void* kv_cache, int32_t num_blocks, CacheWriteArgs* a);
+}  // namespace
+
 extern "C" {
 
 const char* mla_status_string(int32_t status) {
@@ -275,14 +281,11 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
 mla_status mla_cache_write(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
                            int64_t k_pe_row_stride, const int32_t* positions, const int32_t* slot_mapping,
                            int32_t num_tokens, void* kv_cache, int32_t num_blocks, void* stream) {
-  if (!ctx || num_tokens < 0) return MLA_EINVAL;
-  if (num_tokens == 0) return MLA_OK;
-  if (!c_kv || !k_pe || !positions || !slot_mapping || !kv_cache || num_blocks <= 0) return MLA_EINVAL;
-  if (c_kv_row_stride < DC || k_pe_row_stride < DR) return MLA_EINVAL;
+  CacheWriteArgs a;
+  const mla_status st = cache_write_args(ctx, c_kv, c_kv_row_stride, k_pe, k_pe_row_stride, positions, slot_mapping,
+                                         num_tokens, kv_cache, num_blocks, &a);
+  if (st != MLA_OK || num_tokens == 0) return st;
   hipStream_t s = as_stream(stream);
-  CacheWriteArgs a{c_kv, c_kv_row_stride, k_pe, k_pe_row_stride, positions, slot_mapping, num_tokens,
-                   kv_cache, int64_t(num_blocks) * BLK, ctx->gamma, ctx->rope, ctx->cfg.max_position,
-                   double(ctx->cfg.rms_eps)};
   ProfScope ps(ctx, MLA_K_CACHE_WRITE, s);
   return hip_status(ctx->fp8 ? launch_cache_write_fp8(a, s) : launch_cache_write(ctx->bf16, a, s));
 }
