@@ -6,7 +6,7 @@ TEST INFRASTRUCTURE ONLY, like mla_oracle.py: only the tests, ``__graft_entry__.
 What it follows.  The learning-book page on MLA in vLLM ([P-vllm] ch. 07 "模型架构特异：MLA / Mamba /
 MoE 在 vLLM 源码层") lists an FP8 KV cache for MLA among the engine's options, and the same page
 (§2.3) fixes the cache shape (n_blocks, block, 1, latent_d + rope_d); the pages give no scale
-convention and no byte layout.  The reading taken here (listed in the design doc):
+convention and no byte layout.  The reading taken here:
 
 * Number format: OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
   no infinities; S.1111.111 is NaN; the largest finite value is 1.75 * 2^8 = 448; exponent field 0

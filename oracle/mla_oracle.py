@@ -32,7 +32,7 @@ Sources (cited by page title and section; no line numbers):
     layer, a block table maps logical to physical blocks.
   - §2.3 cache的存储大小对比: MLA cache bytes = 2 * seq_len * (kv_lora_rank + qk_rope_head_dim).
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * RoPE: interleaved consecutive pairs (x[2i], x[2i+1]) rotated by p * theta^(-2i/d_rope)
   (the RoFormer formulation); the pages never define the pairing.
