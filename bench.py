@@ -39,6 +39,8 @@ TRAFFIC = {"lite_b64": ("decode_bf16_lite_b64_s4096_traffic.json", "decode_bf16.
            "wide": ("decode_bf16_mt32_wide_h128_b128_traffic.json", "decode_bf16_mt32.hip"),
            "ragged": ("decode_bf16_mt32_ragged_b256_q4_traffic.json", "decode_bf16_mt32.hip")}
 TRAFFIC_FP8 = {"lite_b64": ("decode_fp8_lite_b64_s4096_traffic.json", "decode_fp8.hip")}
+# the chunked prefill's attention kernel at the default prefill sizes (4 sequences x 4,096 tokens)
+TRAFFIC_PF = ("prefill_attn_b4_s4096_traffic.json", "prefill.hip")
 
 
 def parse():
@@ -115,6 +117,22 @@ def kernel_source_sha(src):
     for f in (src, "mla_internal.h"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
+
+
+def prefill_traffic(args):
+    """HBM traffic of the prefill attention kernel from its committed rocprofv3 --pmc summary (default
+    sizes only), if it was taken on the current kernel source; else None."""
+    if args.pf_batch != 4 or args.pf_len != 4096:
+        return None
+    fname, src = TRAFFIC_PF
+    path = os.path.join(PROFILES, fname)
+    try:
+        rec = json.load(open(path))
+        if rec.get("kernel_source_sha256") != kernel_source_sha(src):
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except Exception:
+        return None
 
 
 def traffic_entry(args):
@@ -310,7 +328,8 @@ def prefill_main(args):
            "flops": {"attention": fa, "expansion": fe}, "kernels_us": kus,
            "roofline": {"bound": "mfma", "achieved": round(fa / (kus["attn"] * 1e-6) / 1e12, 2),
                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(fa / (kus["attn"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "frac": round(fa / (kus["attn"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        "traffic": prefill_traffic(args),
                         "kernel": "prefill_attn_kernel",
                         "expand_tflops": round(fe / (kus["expand"] * 1e-6) / 1e12, 2)}}
     if not args.no_cpu_baseline:
