@@ -253,21 +253,15 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       f32x16_t sc = f32x16_t{};
 #pragma unroll
       for (int k = 0; k < D; ++k) ring[k] = sp[16 * k];
+      // one scheduling region per K step (MFMA k and the read of operand k + D), so that the reads
+      // stay D steps ahead: left free, the scheduler moved each read next to its own MFMA
 #pragma unroll
       for (int k = 0; k < kChunks; ++k) {
         const u32x4_t xr = ring[k % D];
-        if (k + D < kChunks) ring[k % D] = sp[16 * (k + D)];
         sc = mfma32x32(xr, qreg[k], sc);
+        if (k + D < kChunks) ring[k % D] = sp[16 * (k + D)];
         if (x && k % SP == SP / 2) put(*x, k / SP);
-      }
-      if (!x) {
-        __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
-#pragma unroll
-        for (int k = 0; k < kChunks - D; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = sc[r];
