@@ -136,3 +136,32 @@ def test_prefill_status_codes():
             ctx8.prefill(q, dev_i32(cu), pool8, dev_i32(w.block_table), dev_i32(w.seq_lens), 48, 8)
     finally:
         ctx8.free()
+
+
+def test_prefill_full_size_sampled():
+    """The benchmark's configuration and launch (4 sequences, each a fresh chunk of 4,096 tokens, 16
+    heads, the same seed): sampled rows against the oracle.  A causal row depends only on the tokens
+    up to its own position, so the last 8 rows of each sequence are the oracle's prefill of an
+    8-token chunk over the whole context, and the first 8 rows its prefill of an 8-token context (the
+    first 8 tokens, the same cache rows)."""
+    B, S, R = 4, 4096, 8
+    w = W.custom(f"prefill_b{B}_s{S}", "bf16", 16, [S] * B, q_len=1, seed=1240)
+    _say("prefill full size", B, "x", S, "sampled rows", R, "first and last per sequence")
+    W_uk, W_uv = oracle_weights(w)
+    tok = w.all_tokens()
+    cache = O.cache_write(np.full((w.n_blocks, 16, 1, 576), np.nan), tok["c_kv"], tok["k_pe"], tok["positions"],
+                          tok["slot_mapping"], w.gamma().astype(np.float64), w.eps, w.theta, w.storage)
+    q = w.chunk_queries([S] * B)
+    cu_r = _cu([R] * B)
+    last_rows = np.concatenate([np.arange(b * S + S - R, b * S + S) for b in range(B)])
+    first_rows = np.concatenate([np.arange(b * S, b * S + R) for b in range(B)])
+    ref_last = O.prefill_naive(q[last_rows], cu_r, cache, w.block_table, w.seq_lens, W_uk, W_uv, w.scale, w.theta)
+    ref_first = O.prefill_naive(q[first_rows], cu_r, cache, w.block_table, np.full(B, R), W_uk, W_uv, w.scale,
+                                w.theta)
+    run = GpuRun(w)
+    try:
+        out = _run_prefill(run, [S] * B)
+        compare(out[torch.from_numpy(last_rows).cuda()], ref_last, "bf16", "prefill full size, last rows")
+        compare(out[torch.from_numpy(first_rows).cuda()], ref_first, "bf16", "prefill full size, first rows")
+    finally:
+        run.free()
