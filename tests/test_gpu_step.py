@@ -136,3 +136,21 @@ def test_decode_step_refuses_bad_arguments_before_writing():
         assert np.array_equal(_bits(p1), _bits(p2))
     finally:
         run.ctx.free()
+
+
+def test_decode_step_full_size_matches_two_calls():
+    """The benchmark's step at full size (lite_b64: 64 sequences x 4,096 cached + 1 new token, 16 heads,
+    bf16 pool of 20,000 blocks, the library's own launch): mla_decode_step against mla_cache_write +
+    mla_decode on copies of the pool, bit for bit.  (The decode itself is checked against the oracle at
+    this size in test_gpu_parity.py.)"""
+    w = W.lite_b64()
+    _say("decode_step full size: lite_b64")
+    run = StepRun(w, "bf16")
+    try:
+        p1, p2 = run.pool.clone(), run.pool.clone()
+        o1 = run.two_calls(p1)
+        o2 = run.step(p2)
+        assert torch.equal(p1.view(torch.int16), p2.view(torch.int16)), "cache rows differ"
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "outputs differ"
+    finally:
+        run.ctx.free()
