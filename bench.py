@@ -342,7 +342,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU sharding is a design "
-                                   "note only (the path has no cross-GPU step in this build)",
+                                   "note only (the library has no cross-GPU step)",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
     import numpy as np
