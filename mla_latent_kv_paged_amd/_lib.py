@@ -8,7 +8,6 @@ pointers.  There is no fallback: if libmla.so is missing or fails to load, the c
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -292,6 +291,3 @@ class MLAContext:
                "mla_profile_samples")
         return list(buf[:n.value])
 
-
-def default_scale():
-    return 1.0 / math.sqrt(192.0)

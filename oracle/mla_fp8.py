@@ -118,12 +118,12 @@ def pack_row(codes, rope_bf16, scales):
 
 
 def unpack_row(row):
-    """656-byte row -> (latent values [512] float64, rope values [64] float64)."""
-    row = np.asarray(row, dtype=np.uint8)
-    scales = row[DC + 2 * DR:].view("<f4").astype(np.float64)
-    lat = e4m3_decode(row[:DC]) * np.repeat(scales, GROUP)
-    rope = (row[DC:DC + 2 * DR].view("<u2").astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return lat, rope
+    """656-byte row(s) [..., 656] -> (latent values [..., 512] float64, rope values [..., 64] float64)."""
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    scales = row[..., DC + 2 * DR:].copy().view("<f4").astype(np.float64)          # [..., 4]
+    lat = e4m3_decode(row[..., :DC]) * np.repeat(scales, GROUP, axis=-1)
+    rope = (row[..., DC:DC + 2 * DR].copy().view("<u2").astype(np.uint32) << 16).view(np.float32)
+    return lat, rope.astype(np.float64)
 
 
 def cache_write_fp8(cache, c_kv, k_pe, positions, slot_mapping, gamma, eps, theta):
@@ -155,12 +155,5 @@ def cache_write_fp8(cache, c_kv, k_pe, positions, slot_mapping, gamma, eps, thet
 def dequantize_cache(cache):
     """Byte cache [n_blocks, block, 1, 656] -> float64 cache [n_blocks, block, 1, 576] of the values
     the decode sees (rows that were never written come out as whatever their bytes say)."""
-    cache = np.asarray(cache, dtype=np.uint8)
-    n_blocks, block_size = cache.shape[:2]
-    out = np.empty((n_blocks, block_size, 1, DC + DR), dtype=np.float64)
-    for b in range(n_blocks):
-        for t in range(block_size):
-            lat, rope = unpack_row(cache[b, t, 0])
-            out[b, t, 0, :DC] = lat
-            out[b, t, 0, DC:] = rope
-    return out
+    lat, rope = unpack_row(np.asarray(cache, dtype=np.uint8))
+    return np.concatenate([lat, rope], axis=-1)

@@ -185,6 +185,9 @@ def cache_write(cache, c_kv, k_pe, positions, slot_mapping, gamma, eps, theta, s
     if width != dc + k_pe.shape[1]:
         raise ValueError("cache row width must be kv_lora_rank + qk_rope_head_dim")
     rnd = round_to_bf16 if storage == "bf16" else round_to_f32
+    # every token's row at once: RMSNorm and RoPE act on each row on its own
+    rows = np.concatenate([rnd(rms_norm(c_kv, gamma, eps)),
+                           rnd(rope(k_pe, np.asarray(positions), theta))], axis=1)
     for j in range(c_kv.shape[0]):
         slot = int(slot_mapping[j])
         if slot < 0:
@@ -192,10 +195,7 @@ def cache_write(cache, c_kv, k_pe, positions, slot_mapping, gamma, eps, theta, s
         blk, off = divmod(slot, block_size)
         if blk >= n_blocks:
             raise IndexError("slot outside the cache pool")
-        c = rms_norm(c_kv[j], gamma, eps)
-        k = rope(k_pe[j], positions[j], theta)
-        out[blk, off, 0, :dc] = rnd(c)
-        out[blk, off, 0, dc:] = rnd(k)
+        out[blk, off, 0, :] = rows[j]
     return out
 
 
@@ -204,13 +204,13 @@ def cache_write(cache, c_kv, k_pe, positions, slot_mapping, gamma, eps, theta, s
 # ----------------------------------------------------------------------------------------------
 
 def gather_sequence(cache, block_table_row, ctx, dc):
-    """Return the logical latent rows C [ctx, dc] and rope keys R [ctx, dr] of one sequence."""
+    """Return the logical latent rows C [ctx, dc] and rope keys R [ctx, dr] of one sequence:
+    token t is row t % block_size of physical block block_table_row[t // block_size]."""
     cache = np.asarray(cache, dtype=np.float64)
     block_size = cache.shape[1]
-    rows = np.empty((ctx, cache.shape[3]), dtype=np.float64)
-    for t in range(ctx):
-        blk = int(block_table_row[t // block_size])
-        rows[t] = cache[blk, t % block_size, 0, :]
+    t = np.arange(ctx)
+    blk = np.asarray(block_table_row)[t // block_size].astype(np.int64)
+    rows = cache[blk, t % block_size, 0, :]
     return rows[:, :dc], rows[:, dc:]
 
 
@@ -418,7 +418,3 @@ def mla_cache_bytes(seq_len, kv_lora_rank, qk_rope_head_dim, elem_bytes=2):
     """Cache bytes of one MLA layer for seq_len tokens."""
     return seq_len * latent_bytes_per_token(kv_lora_rank, qk_rope_head_dim, elem_bytes)
 
-
-def default_scale(qk_nope_head_dim, qk_rope_head_dim):
-    """Softmax scale 1/sqrt(dn + dr)."""
-    return 1.0 / math.sqrt(qk_nope_head_dim + qk_rope_head_dim)

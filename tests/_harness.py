@@ -96,20 +96,58 @@ def oracle_full(w):
     return cache, out
 
 
-def oracle_sequence(w, b, W_uk=None, W_uv=None):
+def oracle_sequence(w, b, W_uk=None, W_uv=None, q=None):
     """Oracle output rows of sequence b alone, computed on an identity-paged local pool
-    (paging relabel invariance makes the physical placement irrelevant)."""
+    (paging relabel invariance makes the physical placement irrelevant).  q: w.queries(), if the
+    caller already holds it."""
     if W_uk is None:
         W_uk, W_uv = oracle_weights(w)
+    if q is None:
+        q = w.queries()
     ctx = int(w.seq_lens[b])
     nb = (ctx + 15) // 16
     c, k = w.history(b)
     pool = np.full((nb, 16, 1, 576), np.nan)
     cache = O.cache_write(pool, c, k, np.arange(ctx), np.arange(ctx), w.gamma().astype(np.float64), w.eps,
                           w.theta, w.storage)
-    q = w.queries()[b * w.q_len:(b + 1) * w.q_len]
-    return O.decode_absorbed(q, cache, np.arange(nb)[None, :], np.array([ctx]), w.q_len, W_uk, W_uv, w.scale,
-                             w.theta)
+    return O.decode_absorbed(q[b * w.q_len:(b + 1) * w.q_len], cache, np.arange(nb)[None, :], np.array([ctx]),
+                             w.q_len, W_uk, W_uv, w.scale, w.theta)
+
+
+def _oracle_rows_task(args):
+    """Worker of oracle_all_sequences: the oracle rows of a list of sequences (one BLAS thread)."""
+    w, seqs = args
+    try:
+        from threadpoolctl import threadpool_limits
+        lim = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        lim = None
+    W_uk, W_uv = oracle_weights(w)
+    q = w.queries()
+    res = [(b, oracle_sequence(w, b, W_uk, W_uv, q)) for b in seqs]
+    if lim is not None:
+        lim.unregister()
+    return res
+
+
+def oracle_all_sequences(w, seqs=None, workers=None):
+    """oracle_sequence for every sequence (or those in seqs), spread over worker processes started
+    fresh (spawn: they import NumPy and the oracle only, never the GPU).  Returns [B*q_len, H, dv]
+    float64 rows; rows of sequences not asked for are NaN."""
+    import concurrent.futures
+    import multiprocessing
+    import os
+    seqs = list(range(w.batch) if seqs is None else seqs)
+    n = max(1, min(workers or 16, len(os.sched_getaffinity(0)), len(seqs)))
+    # longest first, dealt round robin, so that the workers finish together
+    order = sorted(seqs, key=lambda b: -int(w.seq_lens[b]))
+    parts = [order[i::n] for i in range(n)]
+    out = np.full((w.n_q, w.num_heads, w.v_head_dim), np.nan)
+    with concurrent.futures.ProcessPoolExecutor(n, mp_context=multiprocessing.get_context("spawn")) as ex:
+        for res in ex.map(_oracle_rows_task, [(w, p) for p in parts]):
+            for b, rows in res:
+                out[b * w.q_len:(b + 1) * w.q_len] = rows
+    return out
 
 
 def compare(out_gpu, ref, storage, label=""):

@@ -121,3 +121,67 @@ def test_row_round_trip_and_bf16_consistency():
     for s in slots[slots >= 0]:
         untouched[s // 16, s % 16] = False
     assert np.all(out8[untouched] == 0)
+
+
+def _hand_row():
+    """A 656-byte row written byte by byte from the format fields and the row layout (latent codes at
+    bytes 0..511, bf16 rope values little-endian at 512..639, fp32 group scales little-endian at
+    640..655), with the values each byte stands for."""
+    row = np.zeros(656, dtype=np.uint8)
+    lat = np.zeros(512)
+    # E4M3 codes: sign | exponent (bias 7) | mantissa
+    row[0], lat[0] = 0x38, 1.0               # 0 0111 000: 2^0
+    row[1], lat[1] = 0x7E, 448.0             # 0 1111 110: 1.75 * 2^8, the largest finite
+    row[2], lat[2] = 0xC0, -2.0              # 1 1000 000
+    row[127], lat[127] = 0x01, 2.0 ** -9     # 0 0000 001: the smallest subnormal
+    row[128], lat[128] = 0x38, 1.0 * 0.5     # group 1, scale 0.5
+    row[256], lat[256] = 0x7E, 448.0 * 2.0 ** -10   # group 2, scale 2^-10
+    row[511], lat[511] = 0xB0, -0.5 * 3.0    # 1 0110 000 = -0.5; group 3, scale 3
+    rope = np.zeros(64)
+    row[512], row[513], rope[0] = 0x80, 0x3F, 1.0    # bf16 0x3F80
+    row[514], row[515], rope[1] = 0x00, 0xC0, -2.0   # bf16 0xC000
+    row[516], row[517], rope[2] = 0x00, 0x3F, 0.5    # bf16 0x3F00
+    scales = np.array([1.0, 0.5, 2.0 ** -10, 3.0])
+    row[640:644] = (0x00, 0x00, 0x80, 0x3F)   # fp32 0x3F800000
+    row[644:648] = (0x00, 0x00, 0x00, 0x3F)   # fp32 0x3F000000
+    row[648:652] = (0x00, 0x00, 0x80, 0x3A)   # fp32 0x3A800000
+    row[652:656] = (0x00, 0x00, 0x40, 0x40)   # fp32 0x40400000
+    return row, lat, rope, scales
+
+
+def test_row_layout_against_hand_built_bytes():
+    """pack_row and unpack_row against a row whose bytes are written out by hand (not by either
+    function): a layout slip made in both (offsets, byte order, scale groups) fails here."""
+    row, lat, rope, scales = _hand_row()
+    codes = row[:512].copy()
+    assert np.array_equal(F.pack_row(codes, rope, scales), row)
+    got_lat, got_rope = F.unpack_row(row)
+    assert np.array_equal(got_lat, lat)
+    assert np.array_equal(got_rope, rope)
+    # a cache of two such rows decodes to the same values in each slot
+    cache = np.zeros((1, 16, 1, 656), dtype=np.uint8)
+    cache[0, 3, 0] = row
+    deq = F.dequantize_cache(cache)
+    assert np.array_equal(deq[0, 3, 0, :512], lat) and np.array_equal(deq[0, 3, 0, 512:], rope)
+    assert np.all(deq[0, 0, 0] == 0)
+
+
+def test_quantiser_codes_by_hand():
+    """quantize_latent on values whose codes and scales are worked out by hand from the format:
+    exact values, ties to the even code (normal and subnormal), a zero group, and group scales of
+    1, 1/2 and 3 (amax / 448 exact in fp32)."""
+    c = np.zeros(512)
+    expect = np.zeros(512, dtype=np.uint8)
+    vals = [(448.0, 0x7E), (1.0625, 0x38), (1.1875, 0x3A), (2.5 * 2.0 ** -9, 0x02), (-0.5, 0xB0), (240.0, 0x77),
+            (7 * 2.0 ** -9, 0x07), (2.0 ** -6, 0x08)]
+    for i, (v, code) in enumerate(vals):          # group 0: amax 448 -> scale 1
+        c[i], expect[i] = v, code
+    c[128], expect[128] = 224.0, 0x7E              # group 1: amax 224 -> scale 0.5
+    c[129], expect[129] = 0.5, 0x38
+    c[130], expect[130] = -1.0, 0xC0
+    # group 2 stays zero: scale 1, codes 0
+    c[384], expect[384] = 1344.0, 0x7E             # group 3: amax 1344 -> scale 3
+    c[385], expect[385] = -6.0, 0xC0
+    codes, scales = F.quantize_latent(c)
+    assert np.array_equal(codes, expect)
+    assert np.array_equal(scales, [1.0, 0.5, 1.0, 3.0])
