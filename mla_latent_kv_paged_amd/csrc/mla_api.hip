@@ -293,12 +293,31 @@ mla_status mla_cache_write(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
 }  // extern "C"
 
 namespace {
-// mla_decode; with cw, the cache write cw first (mla_decode_step): in the query absorption's launch
-// for bf16 storage, else as its own launch before it
-mla_status decode_impl(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+// The launch shape of one decode: kernel choice, split or partition, and the partial rows it writes.
+struct DecodePlan {
+  int t32 = 0;      // 32-row kernel: tiles per workgroup (0: a 16-row or the fp32 kernel)
+  int n_rt = 0;     // row tiles per sequence (of 16 rows, or of 32 for the 32-row kernel)
+  int waves = 0;
+  int groups = 0;   // workgroups per (sequence, split): row tiles, or tile groups of the 32-row kernel
+  int sb = 0, n_split = 0, n_wg = 0;
+  int64_t part_rows = 0;  // partial rows written: by split, or by piece (32-row kernel)
+  int64_t streams = 0;    // 32-row kernel: (sequence, tile group) pairs, one piece_tbl entry each
+};
+
+// The decode's scratch memory: [q_lat | q_pe'] rows, partial rows, their (m, l) and scales, and the
+// piece table of the 32-row kernel.
+struct DecodeWs {
+  void* qcat;
+  float* part_acc;  // fp32 partial rows; the bf16 kernels store fp16 rows in the same memory
+  float2* part_ml;
+  float* part_scale;
+  int2* piece_tbl;
+};
+
+// Check a decode's host-visible arguments against the context's caps and choose its launch shape.
+mla_status decode_plan(const mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
                        int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
-                       const int32_t* seq_lens, int32_t max_seq_len, void* out, hipStream_t s,
-                       const CacheWriteArgs* cw) {
+                       const int32_t* seq_lens, int32_t max_seq_len, const void* out, DecodePlan* pl) {
   if (!ctx || !q || !kv_cache || !block_table || !seq_lens || !out) return MLA_EINVAL;
   if (batch < 1 || q_len < 1 || num_blocks <= 0 || max_seq_len < q_len) return MLA_EINVAL;
   const mla_config& cf = ctx->cfg;
@@ -310,41 +329,90 @@ mla_status decode_impl(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len
   const int H = cf.num_heads;
   const int n_q = batch * q_len;
 
+  DecodePlan p;
   const int n_rt16 = (H / 16) * q_len;  // row tiles of 16 per sequence (rows ordered query, head)
   // bf16 kernels by rows per sequence: a multiple of 32 -> 32-row tiles, T of them per workgroup
   // (each block read once per workgroup); otherwise the one-tile kernel, 16-row tiles in the grid
   const int n_rt32 = (H * q_len) % 32 == 0 ? H * q_len / 32 : 0;
   // (FP8 cache rows: the 16-row FP8 kernel for every shape)
-  const int t32 = (ctx->bf16 && !ctx->fp8 && n_rt32 > 0) ? ((n_rt32 % 4 == 0) ? 4 : (n_rt32 % 2 == 0) ? 2 : 1) : 0;
-  const int n_rt = t32 ? n_rt32 : n_rt16;
-  const int waves = !ctx->bf16 ? 1
-                    : t32         ? t32
-                    : ctx->forced_waves > 0 ? ctx->forced_waves
-                    : ctx->fp8    ? 4
-                                  : 2;
-  const int groups = t32 ? n_rt / t32 : n_rt;  // workgroups per (sequence, split)
-  int sb = 0, n_split = 0, n_wg = 0;
-  if (t32) {
+  p.t32 = (ctx->bf16 && !ctx->fp8 && n_rt32 > 0) ? ((n_rt32 % 4 == 0) ? 4 : (n_rt32 % 2 == 0) ? 2 : 1) : 0;
+  p.n_rt = p.t32 ? n_rt32 : n_rt16;
+  p.waves = !ctx->bf16 ? 1
+            : p.t32     ? p.t32
+            : ctx->forced_waves > 0 ? ctx->forced_waves
+            : ctx->fp8  ? 4
+                        : 2;
+  p.groups = p.t32 ? p.n_rt / p.t32 : p.n_rt;
+  if (p.t32) {
     // balanced partition over one workgroup per resident slot (T = 4 fills a CU; T <= 2, two),
     // and enough workgroups that no range exceeds the block ids one workgroup stages in LDS
-    n_wg = ctx->cu_count * (t32 == 4 ? 1 : 2);
-    if (ctx->forced_split_blocks > 0) n_wg = ctx->forced_split_blocks;  // tuning: workgroup count
-    const int64_t steps_max = int64_t(batch) * groups * ((max_blocks + 1) / 2 + kPieceCost);
-    n_wg = int(std::max<int64_t>(n_wg, (steps_max + kMt32MaxSteps - 1) / kMt32MaxSteps));
-    if (n_wg > ctx->max_wg32) return MLA_ECAP;
+    p.n_wg = ctx->cu_count * (p.t32 == 4 ? 1 : 2);
+    if (ctx->forced_split_blocks > 0) p.n_wg = ctx->forced_split_blocks;  // tuning: workgroup count
+    const int64_t steps_max = int64_t(batch) * p.groups * ((max_blocks + 1) / 2 + kPieceCost);
+    p.n_wg = int(std::max<int64_t>(p.n_wg, (steps_max + kMt32MaxSteps - 1) / kMt32MaxSteps));
+    if (p.n_wg > ctx->max_wg32) return MLA_ECAP;
+    // piece ids run up to (workgroups - 1) + (streams - 1); a piece holds 32 T rows
+    p.streams = int64_t(batch) * p.groups;
+    p.part_rows = (int64_t(p.n_wg) + p.streams) * 32 * p.t32;
   } else {
-    const int blocks_per_wave_cap = 128 * waves;  // block ids held in two registers
-    sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
-                                      : choose_split_blocks(ctx, batch * groups, max_blocks, waves);
+    p.sb = ctx->forced_split_blocks > 0 ? ctx->forced_split_blocks
+                                        : choose_split_blocks(ctx, batch * p.groups, max_blocks, p.waves);
     const int min_sb = (max_blocks + ctx->max_split - 1) / ctx->max_split;  // workspace bound
-    if (sb < min_sb) sb = min_sb;
-    if (sb > blocks_per_wave_cap) sb = blocks_per_wave_cap;
-    if (sb > max_blocks) sb = max_blocks;
-    n_split = (max_blocks + sb - 1) / sb;
+    if (p.sb < min_sb) p.sb = min_sb;
+    // the 16-row bf16 and FP8 kernels hold a wave's block ids in two registers: at most 128 blocks
+    // per wave (max_split is sized so that min_sb never exceeds this at two or more waves); the
+    // fp32 kernel reads its ids as it goes and has no such limit
+    if (ctx->bf16 && p.sb > 128 * p.waves) p.sb = 128 * p.waves;
+    if (p.sb > max_blocks) p.sb = max_blocks;
+    p.n_split = (max_blocks + p.sb - 1) / p.sb;
+    if (p.n_split > ctx->max_split) return MLA_ECAP;  // never past the partial workspace
+    p.part_rows = int64_t(n_q) * H * p.n_split;
   }
-  ctx->last_split_blocks = t32 ? 0 : sb;
-  ctx->last_n_split = t32 ? n_wg : n_split;
-  ctx->last_waves = waves;
+  *pl = p;
+  return MLA_OK;
+}
+
+// Bytes of scratch one decode of plan pl uses when its buffers are carved from one region (each
+// buffer 256-byte aligned), and the carving itself when base is not null.
+size_t decode_ws_carve(const mla_ctx* ctx, const DecodePlan& pl, int64_t n_q, char* base, DecodeWs* ws) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t esz = ctx->bf16 ? 2 : 4;
+  const size_t H = size_t(ctx->cfg.num_heads);
+  size_t off = 0;
+  const size_t q_off = off;
+  off += up(size_t(n_q) * H * ROW * esz);
+  const size_t acc_off = off;
+  off += up(size_t(pl.part_rows) * DC * esz);  // fp16 rows (bf16 kernels) or fp32 rows
+  const size_t ml_off = off;
+  off += up(size_t(pl.part_rows) * sizeof(float2));
+  const size_t sc_off = off;
+  off += up(size_t(pl.part_rows) * sizeof(float));
+  const size_t pt_off = off;
+  off += up(size_t(pl.streams + 1) * sizeof(int2));
+  if (base && ws) {
+    ws->qcat = base + q_off;
+    ws->part_acc = reinterpret_cast<float*>(base + acc_off);
+    ws->part_ml = reinterpret_cast<float2*>(base + ml_off);
+    ws->part_scale = reinterpret_cast<float*>(base + sc_off);
+    ws->piece_tbl = reinterpret_cast<int2*>(base + pt_off);
+  }
+  return off;
+}
+
+// mla_decode on the workspace ws with the launch shape pl; with cw, the cache write cw first
+// (mla_decode_step): in the query absorption's launch for bf16 storage, else as its own launch
+// before it
+mla_status decode_launch(mla_ctx* ctx, const DecodePlan& pl, const DecodeWs& ws, const void* q, int32_t batch,
+                         int32_t q_len, const void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                         int32_t block_table_stride, const int32_t* seq_lens, int32_t max_seq_len, void* out,
+                         hipStream_t s, const CacheWriteArgs* cw) {
+  const mla_config& cf = ctx->cfg;
+  const int H = cf.num_heads;
+  const int n_q = batch * q_len;
+  const int t32 = pl.t32;
+  ctx->last_split_blocks = t32 ? 0 : pl.sb;
+  ctx->last_n_split = t32 ? pl.n_wg : pl.n_split;
+  ctx->last_waves = pl.waves;
 
   hipError_t e = hipSuccess;
   const bool fused = cw && cw->T > 0 && ctx->bf16;
@@ -355,30 +423,46 @@ mla_status decode_impl(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len
   if (e != hipSuccess) return hip_status(e);
   {
     QAbsorbArgs qa{q, ctx->W_uk, ctx->W_ukT, ctx->rope, seq_lens, q_len, n_q, H, max_seq_len, cf.max_position, ctx->qscale,
-                   ctx->qcat};
+                   ws.qcat};
     ProfScope ps(ctx, fused ? MLA_K_PREP : MLA_K_Q_ABSORB, s);
     e = fused ? launch_decode_prep(qa, *cw, ctx->fp8, s) : launch_q_absorb(ctx->bf16, qa, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {
-    DecodeArgs da{batch,  kv_cache,       ctx->zero_block, num_blocks,    block_table, block_table_stride,
-                  seq_lens, max_seq_len,  q_len,           H,             ctx->qcat,   ctx->part_acc,
-                  reinterpret_cast<uint16_t*>(ctx->part_acc), ctx->part_ml, ctx->part_scale, sb,       n_split,         n_rt,          t32 ? n_wg : batch * n_split * groups,
-                  ctx->piece_tbl};
+    DecodeArgs da{batch,   kv_cache,    ctx->zero_block, num_blocks,  block_table,
+                  block_table_stride,   seq_lens,        max_seq_len, q_len,
+                  H,       ws.qcat,     ws.part_acc,     reinterpret_cast<uint16_t*>(ws.part_acc),
+                  ws.part_ml,           ws.part_scale,   pl.sb,       pl.n_split,
+                  pl.n_rt, t32 ? pl.n_wg : batch * pl.n_split * pl.groups,  ws.piece_tbl};
     ProfScope ps(ctx, MLA_K_DECODE, s);
-    e = t32 ? launch_decode_mt32(da, t32, s) : ctx->fp8 ? launch_decode_fp8(da, waves, s) : launch_decode(ctx->bf16, da, waves, s);
+    e = t32 ? launch_decode_mt32(da, t32, s)
+            : ctx->fp8 ? launch_decode_fp8(da, pl.waves, s) : launch_decode(ctx->bf16, da, pl.waves, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {
     // output channels split over 4 workgroups only when the (head, 16 rows) grid is small
     const int v_parts = int64_t(H) * ((n_q + 15) / 16) >= 2 * ctx->cu_count ? 1 : 4;
-    CombineArgs ca{ctx->part_acc, reinterpret_cast<const uint16_t*>(ctx->part_acc), ctx->part_ml, ctx->part_scale, seq_lens, max_seq_len, q_len, n_q, H, sb, n_split,
-                   ctx->W_uv, ctx->W_uvT, out, t32 ? ctx->piece_tbl : nullptr, 32 * t32,
-                   t32 ? n_rt / t32 : 0, v_parts};
+    CombineArgs ca{ws.part_acc, reinterpret_cast<const uint16_t*>(ws.part_acc), ws.part_ml, ws.part_scale, seq_lens,
+                   max_seq_len, q_len, n_q, H, pl.sb, pl.n_split, ctx->W_uv, ctx->W_uvT, out,
+                   t32 ? ws.piece_tbl : nullptr, 32 * t32, t32 ? pl.n_rt / t32 : 0, v_parts};
     ProfScope ps(ctx, MLA_K_COMBINE, s);
     e = launch_combine(ctx->bf16, ca, s);
   }
   return hip_status(e);
+}
+
+// mla_decode (and mla_decode_step with cw) on the context's own workspace
+mla_status decode_impl(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                       const int32_t* seq_lens, int32_t max_seq_len, void* out, hipStream_t s,
+                       const CacheWriteArgs* cw) {
+  DecodePlan pl;
+  const mla_status st = decode_plan(ctx, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride,
+                                    seq_lens, max_seq_len, out, &pl);
+  if (st != MLA_OK) return st;
+  const DecodeWs ws{ctx->qcat, ctx->part_acc, ctx->part_ml, ctx->part_scale, ctx->piece_tbl};
+  return decode_launch(ctx, pl, ws, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride, seq_lens,
+                       max_seq_len, out, s, cw);
 }
 
 // the arguments of a cache write, checked as mla_cache_write checks them
