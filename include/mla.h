@@ -165,6 +165,26 @@ mla_status mla_decode(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len,
                       const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
 
 /*
+ * mla_decode_noalloc -- mla_decode for callers that cannot allocate device memory during the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, semantics, launch shape and kernels as mla_decode, so the output is bit for bit the
+ * same; the decode's scratch (the [q_lat | q_pe'] rows, the split or piece partials, their
+ * (max, sum) pairs and scales, the piece table) lives in a static device region of 64 MiB that the
+ * library holds on every GPU it runs on until the process ends, instead of the context's workspace.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *  - A decode whose scratch would exceed 64 MiB returns MLA_ECAP (for example, 16 heads: a batch of
+ *    64 at 4,097 tokens uses about 5.4 MB; 128 heads x 128 sequences do not fit).
+ *  - Every call on one GPU shares that GPU's region and leaves its contents behind: calls that
+ *    overlap on one GPU (other streams, other contexts, other threads) race and must be serialised
+ *    by the caller.  Nothing in the region needs clearing between calls.
+ *  - MLA_EHIP if the region's address could not be looked up when the context was made.
+ * Returns what mla_decode returns otherwise.
+ */
+mla_status mla_decode_noalloc(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+                              int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                              const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
+
+/*
  * mla_decode_step -- one decode step of the layer ([P-vllm] §2.2 wrapper forward: the new tokens'
  * cache write by slot_mapping, then attention): exactly mla_cache_write(ctx, c_kv, ..., num_tokens,
  * kv_cache, num_blocks) followed by mla_decode(ctx, q, ..., kv_cache, num_blocks, ...), with the

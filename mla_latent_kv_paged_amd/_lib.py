@@ -19,7 +19,8 @@ MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
 K_PF_EXPAND, K_PF_ATTN, K_PREP = 4, 5, 6
 
-EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_decode_step", "mla_free", "mla_status_string",
+EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_decode_step", "mla_decode_noalloc",
+           "mla_free", "mla_status_string",
            "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",
            "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size")
 
@@ -58,6 +59,8 @@ def load(path=None):
     lib.mla_cache_write.restype = i32
     lib.mla_decode.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
     lib.mla_decode.restype = i32
+    lib.mla_decode_noalloc.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
+    lib.mla_decode_noalloc.restype = i32
     lib.mla_decode_step.argtypes = [vp, vp, i64, vp, i64, vp, vp, i32, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
     lib.mla_decode_step.restype = i32
     lib.mla_prefill.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, vp, vp]
@@ -225,6 +228,27 @@ class MLAContext:
                                  _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(max_seq_len),
                                  _ptr(out), _stream_ptr(stream))
         _check(st, "mla_decode")
+        return out
+
+    def decode_noalloc(self, q, kv_cache, block_table, seq_lens, max_seq_len, out, q_len=1, stream=None):
+        """mla_decode_noalloc: mla_decode on the library's static scratch region; allocates nothing, so
+        `out` must be given (device [batch*q_len, H, 128] of the storage dtype)."""
+        torch = _torch()
+        H = self.num_heads
+        batch = int(seq_lens.shape[0])
+        _need(q, "q", self.tdtype, shape=(batch * q_len, H, 192))
+        _need(kv_cache, "kv_cache", self.cache_dtype)
+        if kv_cache.dim() != 4 or tuple(kv_cache.shape[1:]) != (16, 1, self.cache_row):
+            raise ValueError(f"kv_cache must be [n_blocks, 16, 1, {self.cache_row}]")
+        _need(block_table, "block_table", torch.int32)
+        _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+        if block_table.dim() != 2 or block_table.shape[0] != batch:
+            raise ValueError("block_table must be [batch, stride]")
+        _need(out, "out", self.tdtype, shape=(batch * q_len, H, 128))
+        st = self.lib.mla_decode_noalloc(self.handle, _ptr(q), batch, q_len, _ptr(kv_cache), int(kv_cache.shape[0]),
+                                         _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+                                         int(max_seq_len), _ptr(out), _stream_ptr(stream))
+        _check(st, "mla_decode_noalloc")
         return out
 
     def prefill_workspace_size(self, batch, total_q, max_seq_len):

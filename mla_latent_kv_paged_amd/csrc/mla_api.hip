@@ -5,12 +5,40 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "mla_internal.h"
 
 using namespace mla;
+
+// Decode scratch of mla_decode_noalloc: one static region per GPU, held by the loaded library until
+// the process ends.  Host code never passes its name to a kernel (on the host the name is only a
+// stand-in): the region's device address is looked up once per device, with that device current,
+// and used from then on.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of the scratch region (the current device must be `dev`).
+hipError_t scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
 
 namespace {
 
@@ -51,6 +79,7 @@ struct mla_ctx {
   int32_t forced_split_blocks = 0;
   int32_t forced_waves = 0;
   int32_t last_split_blocks = 0, last_n_split = 0, last_waves = 0;
+  void* scratch = nullptr;  // this device's static scratch region (mla_decode_noalloc)
   Prof prof;
 };
 
@@ -181,6 +210,8 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
     ctx_release(c);
     return MLA_EHIP;
   }
+  // the static scratch region of this device (mla_decode_noalloc reports a failed lookup)
+  if (scratch_address(c->device, &c->scratch) != hipSuccess) c->scratch = nullptr;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, c->device) == hipSuccess && prop.multiProcessorCount > 0)
     c->cu_count = prop.multiProcessorCount;
@@ -500,6 +531,22 @@ mla_status mla_decode_step(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
   if (st != MLA_OK) return st;
   return decode_impl(ctx, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride, seq_lens,
                      max_seq_len, out, as_stream(stream), &cw);
+}
+
+mla_status mla_decode_noalloc(mla_ctx* ctx, const void* q, int32_t batch, int32_t q_len, const void* kv_cache,
+                              int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                              const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream) {
+  DecodePlan pl;
+  const mla_status st = decode_plan(ctx, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride,
+                                    seq_lens, max_seq_len, out, &pl);
+  if (st != MLA_OK) return st;
+  if (!ctx->scratch) return MLA_EHIP;  // the scratch lookup failed when the context was made
+  const int64_t n_q = int64_t(batch) * q_len;
+  if (decode_ws_carve(ctx, pl, n_q, nullptr, nullptr) > kScratchBytes) return MLA_ECAP;
+  DecodeWs ws;
+  decode_ws_carve(ctx, pl, n_q, static_cast<char*>(ctx->scratch), &ws);
+  return decode_launch(ctx, pl, ws, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride, seq_lens,
+                       max_seq_len, out, as_stream(stream), nullptr);
 }
 
 namespace {
