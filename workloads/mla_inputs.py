@@ -38,7 +38,8 @@ BLOCK_SIZE = 16
 ROW = KV_LORA_RANK + QK_ROPE_HEAD_DIM
 
 # tags for independent seed streams
-_T_WEIGHT, _T_GAMMA, _T_Q, _T_STRUCT, _T_HIST, _T_POOL, _T_QCHUNK = range(7)
+_T_WEIGHT, _T_GAMMA, _T_Q, _T_STRUCT, _T_HIST, _T_POOL, _T_QCHUNK, _T_LAYER, _T_HIDDEN = range(9)
+HIDDEN_DIM = 2048  # DeepSeek-V2-Lite hidden size
 
 
 def f32_to_bf16_bits(x):
@@ -76,6 +77,7 @@ class Workload:
     qk_nope_head_dim: int = QK_NOPE_HEAD_DIM
     v_head_dim: int = V_HEAD_DIM
     block_size: int = BLOCK_SIZE
+    hidden_dim: int = HIDDEN_DIM
 
     # ---------------------------------------------------------------- derived sizes
     @property
@@ -134,11 +136,46 @@ class Workload:
             (int(np.sum(chunks)), self.num_heads, self.qk_nope_head_dim + self.qk_rope_head_dim), dtype=np.float32)
         return self._store(q)[0]
 
-    def history(self, b):
+    def hidden(self, layer=0):
+        """[B*q_len, D] hidden states of the new tokens entering layer `layer` ~ N(0, 1)."""
+        h = _rng(self.seed, _T_HIDDEN, layer).standard_normal((self.n_q, self.hidden_dim), dtype=np.float32)
+        return self._store(h)[0]
+
+    def layer_weights(self, layer=0, input_gamma_noise=0.0):
+        """Projection weights of one attention layer, each ~ N(0, 1/fan_in) (float32 storage values):
+        q_proj [H*(dn+dr), D], kv_a_proj [dc+dr, D], o_proj [D, H*dv]; input_norm_gamma [D] (1, or
+        1 + noise * N(0,1)); kv_b_proj [H*(dn+dv), dc] (layer 0: the workload's kv_b_proj) and the
+        kv_a_layernorm gamma [dc] (layer 0: the workload's gamma)."""
+        H, D = self.num_heads, self.hidden_dim
+        dq = self.qk_nope_head_dim + self.qk_rope_head_dim
+        dkv = self.kv_lora_rank + self.qk_rope_head_dim
+
+        def draw(k, shape, fan_in):
+            w = _rng(self.seed, _T_LAYER, layer, k).standard_normal(shape, dtype=np.float32)
+            return self._store(w * np.float32(1.0 / math.sqrt(fan_in)))[0]
+
+        g = np.ones(D, dtype=np.float32)
+        if input_gamma_noise:
+            g += np.float32(input_gamma_noise) * _rng(self.seed, _T_LAYER, layer, 3).standard_normal(
+                D, dtype=np.float32)
+        if layer == 0:
+            kvb, kvg = self.kv_b_proj(), self.gamma()
+        else:
+            kvb = draw(4, (H * (self.qk_nope_head_dim + self.v_head_dim), self.kv_lora_rank), self.kv_lora_rank)
+            kvg = np.ones(self.kv_lora_rank, dtype=np.float32)
+            if self.gamma_noise:
+                kvg += np.float32(self.gamma_noise) * _rng(self.seed, _T_LAYER, layer, 5).standard_normal(
+                    self.kv_lora_rank, dtype=np.float32)
+            kvg = self._store(kvg)[0]
+        return dict(q_proj=draw(0, (H * dq, D), D), kv_a_proj=draw(1, (dkv, D), D),
+                    o_proj=draw(2, (D, H * self.v_head_dim), H * self.v_head_dim),
+                    input_norm_gamma=self._store(g)[0], kv_b_proj=kvb, kv_norm_gamma=kvg)
+
+    def history(self, b, layer=0):
         """Raw (un-normed c_kv, un-rotated k_pe) for every context token of sequence b,
-        positions 0..ctx_b-1: ([ctx, dc], [ctx, dr]) float32 storage values."""
+        positions 0..ctx_b-1: ([ctx, dc], [ctx, dr]) float32 storage values (one stream per layer)."""
         ctx = int(self.seq_lens[b])
-        g = _rng(self.seed, _T_HIST, b)
+        g = _rng(self.seed, _T_HIST, b) if layer == 0 else _rng(self.seed, _T_HIST, b, layer)
         c = g.standard_normal((ctx, self.kv_lora_rank), dtype=np.float32)
         k = g.standard_normal((ctx, self.qk_rope_head_dim), dtype=np.float32)
         return self._store(c)[0], self._store(k)[0]
