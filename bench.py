@@ -67,8 +67,10 @@ def parse():
     ap.add_argument("--pf-batch", type=int, default=4, help="prefill mode: sequences")
     ap.add_argument("--pf-len", type=int, default=4096, help="prefill mode: tokens per sequence, all new (fresh "
                     "prefill: the chunk is the whole context)")
+    ap.add_argument("--layers", type=int, default=1, help="layer mode: attention layers in the model step (each "
+                    "with its own weights and cache)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only", "prefill",
-                                                        "prefill-only"],
+                                                        "prefill-only", "layer", "layer-only"],
                     help="copy-calibration: run a plain 256 MiB device copy (for counter scaling); "
                          "decode-only: run just the decode loop (for profilers)")
     return ap.parse_args()
@@ -338,6 +340,126 @@ def prefill_main(args):
     print(json.dumps(res), flush=True)
 
 
+def layer_main(args):
+    """Decode step from hidden states through `--layers` attention layers (mla_layer_decode_step: input
+    RMSNorm, q_proj and kv_a_proj, the cache write of the new tokens, the absorbed attention, o_proj and
+    the residual), each layer with its own seeded weights and its own cache.  Layer 0's history rows
+    come from the workload's generator; the other layers' from a seeded device generator, written
+    through mla_cache_write (the values only need to be realistic rows: parity is the tests')."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_paged_amd import (MLAContext, K_LAYER_QKV, K_PREP, K_DECODE, K_COMBINE, K_LAYER_O)
+    w = make_workload(args)
+    if w.storage != "bf16":
+        raise SystemExit("layer mode needs a bf16 workload")
+    L = args.layers
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+    def dev_i(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+    max_ctx = int(w.seq_lens.max())
+    hist_pos, hist_slot = [], []
+    for b in range(w.batch):
+        hist = int(w.seq_lens[b]) - w.q_len
+        hist_pos.append(np.arange(hist))
+        hist_slot.append(w.slots(b, 0, hist))
+    hpos, hslot = dev_i(np.concatenate(hist_pos)), dev_i(np.concatenate(hist_slot))
+    new = w.all_tokens(new_only=True)
+    npos, nslot = dev_i(new["positions"]), dev_i(new["slot_mapping"])
+    bt, sl = dev_i(w.block_table), dev_i(w.seq_lens)
+    t0 = time.perf_counter()
+    layers = []
+    weight_bytes = 0
+    for li in range(L):
+        lw = w.layer_weights(li)
+        ctx = MLAContext(dev(lw["kv_b_proj"]), None, num_heads=w.num_heads, dtype="bf16", rms_eps=w.eps,
+                         rope_theta=w.theta, max_q_tokens=w.n_q, max_batch=w.batch, max_position=max_ctx,
+                         max_seq_len=max_ctx)
+        ctx.layer_weights(dev(lw["q_proj"]), dev(lw["kv_a_proj"]), dev(lw["o_proj"]), dev(lw["input_norm_gamma"]))
+        weight_bytes += 2 * sum(int(np.prod(lw[k].shape)) for k in ("q_proj", "kv_a_proj", "o_proj", "kv_b_proj"))
+        pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if li == 0:
+            hist = w.all_tokens(history_only=True)
+            ctx.cache_write(dev(hist["c_kv"]), dev(hist["k_pe"]), hpos, hslot, pool)
+        else:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(1240 + li)
+            T = int(hpos.shape[0])
+            c = torch.randn((T, 512), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+            k = torch.randn((T, 64), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+            ctx.cache_write(c, k, hpos, hslot, pool)
+            del c, k
+        layers.append((ctx, pool))
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    # one layer: three copies of its pool rotate between steps (no step re-reads the previous one's cache
+    # out of the Infinity Cache); several layers: each reads its own cache once per step anyway
+    pools1 = [layers[0][1]] + ([layers[0][1].clone() for _ in range(max(0, args.rotate - 1))] if L == 1 else [])
+    hidden0 = dev(w.hidden())
+    bufs = [torch.empty_like(hidden0), torch.empty_like(hidden0)]
+
+    def step(i):
+        h = hidden0
+        for li, (ctx, pool) in enumerate(layers):
+            p = pools1[i % len(pools1)] if L == 1 else pool
+            ctx.layer_decode_step(h, npos, nslot, p, bt, sl, max_ctx, q_len=w.q_len, out=bufs[li % 2])
+            h = bufs[li % 2]
+
+    if args.mode == "layer-only":
+        for i in range(args.warmup + args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "layer-only", "layers": L, "launches": args.warmup + args.steps,
+                          "workload": w.name}), flush=True)
+        return
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    for ctx, _ in layers:
+        ctx.profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kus = {}
+    for name, kid in (("qkv_proj", K_LAYER_QKV), ("prep", K_PREP), ("decode", K_DECODE), ("combine", K_COMBINE),
+                      ("o_proj", K_LAYER_O)):
+        tot = n = 0
+        for ctx, _ in layers:
+            t_, n_ = ctx.profile_read(kid)
+            tot += t_
+            n += n_
+        kus[name] = round(1e3 * tot / max(n, 1), 2)
+    for ctx, _ in layers:
+        ctx.profile_enable(False)
+    latent = w.latent_bytes() * L
+    res = {"metric": f"MLA decode step from hidden states, {L} attention layer(s), µs/step + GB/s (latent cache + "
+                     f"weights), V2-Lite {w.name}",
+           "value": round(ms * 1e3, 2), "unit": "µs/step", "mode": "layer", "layers": L, "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+           "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) hidden states and activations, N(0,1/fan_in) weights)",
+           "config": dict(describe(w), hidden_dim=2048, layers=L),
+           "kernels_us_per_layer": kus,
+           "us_per_layer": round(ms * 1e3 / L, 2),
+           "latent_gbps": round(latent / (ms * 1e-3) / 1e9, 1),
+           "latent_plus_weights_gbps": round((latent + weight_bytes) / (ms * 1e-3) / 1e9, 1),
+           "weight_bytes_per_step": weight_bytes, "latent_bytes_per_step": latent,
+           "setup_s": round(setup_s, 1)}
+    for ctx, _ in layers:
+        ctx.free()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -352,6 +474,9 @@ def main():
         return
     if args.mode in ("prefill", "prefill-only"):
         prefill_main(args)
+        return
+    if args.mode in ("layer", "layer-only"):
+        layer_main(args)
         return
     from mla_latent_kv_paged_amd import MLAContext, K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE, K_PREP
 

@@ -202,6 +202,64 @@ mla_status mla_decode_step(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
                            const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
 
 /*
+ * mla_layer_weights -- attach one layer's projections to a context, for mla_layer_decode_step: the
+ * weight path q_proj, kv_a_proj_with_mqa, kv_b_proj, o_proj of [P-mini] 版本 1 (kv_b_proj and the
+ * kv_a_layernorm gamma are the context's own, from mla_absorb_weights), and the input_layernorm of
+ * the decoder layer ([P-vllm] DeepseekV3DecoderLayer listing).  bf16 contexts (MLA_BF16 and
+ * MLA_BF16_FP8) only.
+ *
+ *  hidden_dim        D, the hidden size: a positive multiple of 1,024 (DeepSeek-V2-Lite: 2,048).
+ *  q_proj_w          device bf16 [H*(dn+dr), D]: per head [nope | rope] query rows (no query
+ *                    low-rank step, the V2-Lite shape).
+ *  kv_a_proj_w       device bf16 [dc + dr, D]: compressed_kv rows then k_pe rows.
+ *  o_proj_w          device bf16 [D, H*dv]: columns head-major (head h owns h*dv .. h*dv + dv - 1).
+ *  input_norm_gamma  device bf16 [D] or NULL (all ones); used with MLA_LAYER_INPUT_NORM.
+ *  flags             MLA_LAYER_INPUT_NORM: RMSNorm the hidden states first (with the context's
+ *                    rms_eps); MLA_LAYER_RESIDUAL: add the hidden states to the output.  Both: the
+ *                    attention half of the decoder layer; neither: the bare attention module of
+ *                    [P-vllm] §2.2.
+ *  stream            the call synchronises it once before returning.
+ * The context keeps its own copies (the q_proj and kv_a_proj rows multiplied by input_norm_gamma
+ * and rounded to bf16 once); the caller's buffers may be freed after the call.  It also sizes the
+ * step's workspace from the context's max_q_tokens.  A second call replaces the first.
+ * Returns MLA_EINVAL (null ctx or weights, unknown flags), MLA_EUNSUPPORTED (fp32 context, hidden_dim
+ * not a positive multiple of 1,024), MLA_ENOMEM, MLA_EHIP.
+ */
+enum { MLA_LAYER_INPUT_NORM = 1, MLA_LAYER_RESIDUAL = 2 };
+mla_status mla_layer_weights(mla_ctx* ctx, int32_t hidden_dim, const void* q_proj_w, const void* kv_a_proj_w,
+                             const void* o_proj_w, const void* input_norm_gamma, int32_t flags, void* stream);
+
+/*
+ * mla_layer_decode_step -- one decode step of one attention layer from hidden states ([P-vllm] §2.2
+ * wrapper forward: down-projection, decoupled RoPE, cache write by slot_mapping, attention; the
+ * DeepseekV3DecoderLayer listing for input_layernorm and the residual; [P-mini] 版本 1 for the
+ * kv_a_proj_with_mqa split [:dc] | [dc:] and o_proj).  For the N = batch * q_len new tokens
+ * (row n = b*q_len + i):
+ *   x      = RMSNorm(hidden[n]) * input_norm_gamma          (MLA_LAYER_INPUT_NORM; else hidden[n])
+ *   q[n]   = x . q_proj^T                                    ([H, dn + dr])
+ *   [c | k] = x . kv_a_proj^T,  split at dc
+ *   mla_cache_write(c, k, positions[n], slot_mapping[n])     (kv_a_layernorm, RoPE, scatter)
+ *   a[n]   = mla_decode(q)[n]                                ([H, dv], the absorbed attention)
+ *   out[n] = a[n] . o_proj^T (+ hidden[n] with MLA_LAYER_RESIDUAL)
+ * Intermediate values: q is rounded to bf16 (the query mla_decode takes), c and k stay fp32 until the
+ * cache row is evaluated in fp64 and rounded once, a is rounded to bf16; out is bf16 (nearest even).
+ *
+ *  hidden                    device bf16 [N, D]
+ *  positions, slot_mapping   device int32 [N]: RoPE position and cache slot of each new token (as
+ *                            mla_cache_write; position ctx_b - q_len + i for the decode to be causal)
+ *  batch, q_len, kv_cache, num_blocks, block_table, block_table_stride, seq_lens, max_seq_len
+ *                            as mla_decode (seq_lens include the new tokens)
+ *  out                       device bf16 [N, D]; may be the same buffer as hidden
+ * Asynchronous on `stream`, no allocation; the context's workspace is used, so calls on one context
+ * must be serialised.  Returns MLA_EINVAL (no layer weights attached, null pointers), and what
+ * mla_decode_step returns for the rest.
+ */
+mla_status mla_layer_decode_step(mla_ctx* ctx, const void* hidden, const int32_t* positions,
+                                 const int32_t* slot_mapping, int32_t batch, int32_t q_len, void* kv_cache,
+                                 int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                                 const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream);
+
+/*
  * mla_prefill -- chunked prefill over the latent cache, naive form: K and V are expanded from the
  * cached latent once per chunk and the new tokens attend to them causally, MHA-style.  The pages'
  * naive MLA ([P-mini] MLA 的数学结构 and 版本 1: K_nope = C W_uk^T, V = C W_uv^T per head, K_pe
@@ -273,7 +331,9 @@ enum {
   MLA_K_PF_EXPAND = 4, /* mla_prefill: K/V expansion */
   MLA_K_PF_ATTN = 5,   /* mla_prefill: causal attention (queries prepared in it) */
   MLA_K_PREP = 6,      /* mla_decode_step: cache write and query absorption in one launch */
-  MLA_K_COUNT = 7
+  MLA_K_LAYER_QKV = 7, /* mla_layer_decode_step: input norm, q_proj and kv_a_proj */
+  MLA_K_LAYER_O = 8,   /* mla_layer_decode_step: o_proj and the residual */
+  MLA_K_COUNT = 9
 };
 mla_status mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* Synchronises the recorded events and returns the summed milliseconds and launch count of

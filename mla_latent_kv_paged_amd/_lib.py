@@ -18,11 +18,14 @@ FP8_ROW_BYTES = 656  # FP8 cache row: 512 e4m3 codes | 64 bf16 rope values | 4 f
 MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ENOMEM, MLA_EHIP, MLA_ECAP = 0, -1, -2, -3, -4, -5
 K_CACHE_WRITE, K_Q_ABSORB, K_DECODE, K_COMBINE = 0, 1, 2, 3
 K_PF_EXPAND, K_PF_ATTN, K_PREP = 4, 5, 6
+K_LAYER_QKV, K_LAYER_O = 7, 8
+LAYER_INPUT_NORM, LAYER_RESIDUAL = 1, 2
 
 EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_decode_step", "mla_decode_noalloc",
            "mla_free", "mla_status_string",
            "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",
-           "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size")
+           "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size", "mla_layer_weights",
+           "mla_layer_decode_step")
 
 
 class MLAConfig(ctypes.Structure):
@@ -67,6 +70,10 @@ def load(path=None):
     lib.mla_prefill.restype = i32
     lib.mla_prefill_workspace_size.argtypes = [vp, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_prefill_workspace_size.restype = i32
+    lib.mla_layer_weights.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp]
+    lib.mla_layer_weights.restype = i32
+    lib.mla_layer_decode_step.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
+    lib.mla_layer_decode_step.restype = i32
     lib.mla_free.argtypes = [vp]
     lib.mla_free.restype = None
     lib.mla_status_string.argtypes = [i32]
@@ -249,6 +256,49 @@ class MLAContext:
                                          _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
                                          int(max_seq_len), _ptr(out), _stream_ptr(stream))
         _check(st, "mla_decode_noalloc")
+        return out
+
+    def layer_weights(self, q_proj, kv_a_proj, o_proj, input_norm_gamma=None, *, input_norm=True, residual=True,
+                      stream=None):
+        """mla_layer_weights: attach one layer's projections (bf16 device tensors q_proj [H*192, D],
+        kv_a_proj [576, D], o_proj [D, H*128], input_norm_gamma [D] or None)."""
+        H = self.num_heads
+        D = int(q_proj.shape[1]) if q_proj is not None and q_proj.dim() == 2 else 0
+        _need(q_proj, "q_proj", self.tdtype, shape=(H * 192, D))
+        _need(kv_a_proj, "kv_a_proj", self.tdtype, shape=(576, D))
+        _need(o_proj, "o_proj", self.tdtype, shape=(D, H * 128))
+        if input_norm_gamma is not None:
+            _need(input_norm_gamma, "input_norm_gamma", self.tdtype, shape=(D,))
+        flags = (LAYER_INPUT_NORM if input_norm else 0) | (LAYER_RESIDUAL if residual else 0)
+        _check(self.lib.mla_layer_weights(self.handle, D, _ptr(q_proj), _ptr(kv_a_proj), _ptr(o_proj),
+                                          _ptr(input_norm_gamma), flags, _stream_ptr(stream)), "mla_layer_weights")
+        self.hidden_dim = D
+
+    def layer_decode_step(self, hidden, positions, slot_mapping, kv_cache, block_table, seq_lens, max_seq_len,
+                          q_len=1, out=None, stream=None):
+        """mla_layer_decode_step: hidden [batch*q_len, D] -> out [batch*q_len, D] (out may be hidden)."""
+        torch = _torch()
+        batch = int(seq_lens.shape[0])
+        n = batch * q_len
+        D = getattr(self, "hidden_dim", 0)
+        _need(hidden, "hidden", self.tdtype, shape=(n, D))
+        _need(positions, "positions", torch.int32, shape=(n,))
+        _need(slot_mapping, "slot_mapping", torch.int32, shape=(n,))
+        _need(kv_cache, "kv_cache", self.cache_dtype)
+        if kv_cache.dim() != 4 or tuple(kv_cache.shape[1:]) != (16, 1, self.cache_row):
+            raise ValueError(f"kv_cache must be [n_blocks, 16, 1, {self.cache_row}]")
+        _need(block_table, "block_table", torch.int32)
+        _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+        if block_table.dim() != 2 or block_table.shape[0] != batch:
+            raise ValueError("block_table must be [batch, stride]")
+        if out is None:
+            out = torch.empty((n, D), dtype=self.tdtype, device=hidden.device)
+        _need(out, "out", self.tdtype, shape=(n, D))
+        st = self.lib.mla_layer_decode_step(self.handle, _ptr(hidden), _ptr(positions), _ptr(slot_mapping), batch,
+                                            q_len, _ptr(kv_cache), int(kv_cache.shape[0]), _ptr(block_table),
+                                            int(block_table.shape[1]), _ptr(seq_lens), int(max_seq_len), _ptr(out),
+                                            _stream_ptr(stream))
+        _check(st, "mla_layer_decode_step")
         return out
 
     def prefill_workspace_size(self, batch, total_q, max_seq_len):

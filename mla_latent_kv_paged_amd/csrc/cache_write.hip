@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
 }
 
 __global__ __launch_bounds__(256) void cache_write_fp8_kernel(CacheWriteArgs a) {
-  cache_write_fp8_token(a, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+  cache_write_fp8_token<uint16_t>(a, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
 hipError_t launch_cache_write_fp8(const CacheWriteArgs& a, hipStream_t s) {

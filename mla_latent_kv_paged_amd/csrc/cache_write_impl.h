@@ -11,14 +11,15 @@ __device__ __forceinline__ double load_f64(const float* p, int64_t i) { return d
 __device__ __forceinline__ void store_round(uint16_t* p, int64_t i, double v) { p[i] = f64_to_bf16(v); }
 __device__ __forceinline__ void store_round(float* p, int64_t i, double v) { p[i] = float(v); }
 
-// token j of a cache write, by one wavefront (lane = lane id)
-template <typename T>
+// token j of a cache write, by one wavefront (lane = lane id): inputs of type Tin (the storage
+// dtype, or fp32 rows of the layer step's projection), cache rows of type T
+template <typename T, typename Tin = T>
 __device__ __forceinline__ void cache_write_token(const CacheWriteArgs& a, int j, int lane) {
 #pragma clang fp contract(off)
   if (j >= a.T) return;
   // every load of the token is issued before any of them is inspected (one memory round trip)
-  const T* c = static_cast<const T*>(a.c_kv) + int64_t(j) * a.c_stride;
-  const T* k = static_cast<const T*>(a.k_pe) + int64_t(j) * a.k_stride;
+  const Tin* c = static_cast<const Tin*>(a.c_kv) + int64_t(j) * a.c_stride;
+  const Tin* k = static_cast<const Tin*>(a.k_pe) + int64_t(j) * a.k_stride;
   const int slot = a.slots[j];
   const int pos = a.positions[j];
   double x[8];
@@ -88,11 +89,13 @@ __device__ __forceinline__ uint32_t e4m3_code(double x) {
 // normed latent y and the rotated rope pair; then per group of 128 channels (16 lanes) the scale
 // s = fp32(amax / 448), stepped up one fp32 value if amax / s would exceed 448 (1 for an all-zero
 // group), and codes e4m3(y / s) with the quotient in fp64.  The rope values are rounded to bf16.
+// Inputs of type Tin: bf16, or fp32 rows of the layer step's projection.
+template <typename Tin = uint16_t>
 __device__ __forceinline__ void cache_write_fp8_token(const CacheWriteArgs& a, int j, int lane) {
 #pragma clang fp contract(off)
   if (j >= a.T) return;
-  const uint16_t* c = static_cast<const uint16_t*>(a.c_kv) + int64_t(j) * a.c_stride;
-  const uint16_t* k = static_cast<const uint16_t*>(a.k_pe) + int64_t(j) * a.k_stride;
+  const Tin* c = static_cast<const Tin*>(a.c_kv) + int64_t(j) * a.c_stride;
+  const Tin* k = static_cast<const Tin*>(a.k_pe) + int64_t(j) * a.k_stride;
   const int slot = a.slots[j];
   const int pos = a.positions[j];
   double x[8];

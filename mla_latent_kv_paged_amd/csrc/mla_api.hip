@@ -80,6 +80,14 @@ struct mla_ctx {
   int32_t forced_waves = 0;
   int32_t last_split_blocks = 0, last_n_split = 0, last_waves = 0;
   void* scratch = nullptr;  // this device's static scratch region (mla_decode_noalloc)
+  // layer step (mla_layer_weights)
+  int32_t hidden_dim = 0;     // 0: no layer attached
+  int32_t layer_flags = 0;
+  void* W1 = nullptr;         // [H*QW + ROW, D] bf16: q_proj rows, then kv_a_proj rows (times gamma_in)
+  void* Wo = nullptr;         // [D, H*DV] bf16
+  void* l_q = nullptr;        // [max_q_tokens, H, QW] bf16 queries
+  float* l_ckv = nullptr;     // [max_q_tokens, ROW] fp32 [c_kv | k_pe] rows
+  void* l_attn = nullptr;     // [max_q_tokens, H, DV] bf16 attention output
   Prof prof;
 };
 
@@ -101,6 +109,11 @@ void ctx_release(mla_ctx* c) {
   hipFree(c->part_ml);
   hipFree(c->part_scale);
   hipFree(c->piece_tbl);
+  hipFree(c->W1);
+  hipFree(c->Wo);
+  hipFree(c->l_q);
+  hipFree(c->l_ckv);
+  hipFree(c->l_attn);
   if (c->prof.created)
     for (int k = 0; k < MLA_K_COUNT; ++k)
       for (int i = 0; i < kProfRing; ++i) {
@@ -547,6 +560,113 @@ mla_status mla_decode_noalloc(mla_ctx* ctx, const void* q, int32_t batch, int32_
   decode_ws_carve(ctx, pl, n_q, static_cast<char*>(ctx->scratch), &ws);
   return decode_launch(ctx, pl, ws, q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride, seq_lens,
                        max_seq_len, out, as_stream(stream), nullptr);
+}
+
+mla_status mla_layer_weights(mla_ctx* ctx, int32_t hidden_dim, const void* q_proj_w, const void* kv_a_proj_w,
+                             const void* o_proj_w, const void* input_norm_gamma, int32_t flags, void* stream) {
+  if (!ctx || !q_proj_w || !kv_a_proj_w || !o_proj_w) return MLA_EINVAL;
+  if (flags & ~(MLA_LAYER_INPUT_NORM | MLA_LAYER_RESIDUAL)) return MLA_EINVAL;
+  if (!ctx->bf16 || hidden_dim <= 0 || hidden_dim % 1024 != 0) return MLA_EUNSUPPORTED;
+  const int H = ctx->cfg.num_heads;
+  const int64_t n1 = int64_t(H) * QW + ROW;
+  const size_t mq = size_t(ctx->cfg.max_q_tokens);
+  // a second call replaces the first
+  hipFree(ctx->W1);
+  hipFree(ctx->Wo);
+  hipFree(ctx->l_q);
+  hipFree(ctx->l_ckv);
+  hipFree(ctx->l_attn);
+  ctx->W1 = ctx->Wo = ctx->l_q = ctx->l_attn = nullptr;
+  ctx->l_ckv = nullptr;
+  ctx->hidden_dim = 0;
+  hipError_t e = hipSuccess;
+  auto alloc = [&](void** p, size_t n) {
+    if (e == hipSuccess) e = hipMalloc(p, n);
+  };
+  alloc(&ctx->W1, size_t(n1) * hidden_dim * 2);
+  alloc(&ctx->Wo, size_t(hidden_dim) * H * DV * 2);
+  alloc(&ctx->l_q, mq * H * QW * 2);
+  alloc(reinterpret_cast<void**>(&ctx->l_ckv), mq * ROW * sizeof(float));
+  alloc(&ctx->l_attn, mq * H * DV * 2);
+  hipStream_t s = as_stream(stream);
+  const void* g = (flags & MLA_LAYER_INPUT_NORM) ? input_norm_gamma : nullptr;
+  if (e == hipSuccess) e = launch_layer_pack(q_proj_w, g, ctx->W1, int64_t(H) * QW, hidden_dim, s);
+  if (e == hipSuccess)
+    e = launch_layer_pack(kv_a_proj_w, g, static_cast<uint16_t*>(ctx->W1) + int64_t(H) * QW * hidden_dim, ROW,
+                          hidden_dim, s);
+  if (e == hipSuccess) e = launch_layer_pack(o_proj_w, nullptr, ctx->Wo, hidden_dim, H * DV, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    hipFree(ctx->W1);
+    hipFree(ctx->Wo);
+    hipFree(ctx->l_q);
+    hipFree(ctx->l_ckv);
+    hipFree(ctx->l_attn);
+    ctx->W1 = ctx->Wo = ctx->l_q = ctx->l_attn = nullptr;
+    ctx->l_ckv = nullptr;
+    return hip_status(e);
+  }
+  ctx->hidden_dim = hidden_dim;
+  ctx->layer_flags = flags;
+  return MLA_OK;
+}
+
+mla_status mla_layer_decode_step(mla_ctx* ctx, const void* hidden, const int32_t* positions,
+                                 const int32_t* slot_mapping, int32_t batch, int32_t q_len, void* kv_cache,
+                                 int32_t num_blocks, const int32_t* block_table, int32_t block_table_stride,
+                                 const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream) {
+  if (!ctx || !ctx->hidden_dim || !hidden || !positions || !slot_mapping || !out) return MLA_EINVAL;
+  DecodePlan pl;
+  mla_status st = decode_plan(ctx, ctx->l_q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride,
+                              seq_lens, max_seq_len, ctx->l_attn, &pl);
+  if (st != MLA_OK) return st;
+  const int H = ctx->cfg.num_heads;
+  const int n_q = batch * q_len;
+  const int D = ctx->hidden_dim;
+  CacheWriteArgs cw;
+  st = cache_write_args(ctx, ctx->l_ckv, ROW, ctx->l_ckv + DC, ROW, positions, slot_mapping, n_q, kv_cache,
+                        num_blocks, &cw);
+  if (st != MLA_OK) return st;
+  cw.in_f32 = 1;
+  hipStream_t s = as_stream(stream);
+  hipError_t e;
+  {
+    ProjArgs pa{};
+    pa.X = static_cast<const uint16_t*>(hidden);
+    pa.x_stride = D;
+    pa.W = static_cast<const uint16_t*>(ctx->W1);
+    pa.M = n_q;
+    pa.N = H * QW + ROW;
+    pa.K = D;
+    pa.norm = (ctx->layer_flags & MLA_LAYER_INPUT_NORM) ? 1 : 0;
+    pa.eps = ctx->cfg.rms_eps;
+    pa.mode = 0;
+    pa.n_split = H * QW;
+    pa.y0 = static_cast<uint16_t*>(ctx->l_q);
+    pa.y1 = ctx->l_ckv;
+    ProfScope ps(ctx, MLA_K_LAYER_QKV, s);
+    e = launch_proj_gemm(pa, s);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  const DecodeWs ws{ctx->qcat, ctx->part_acc, ctx->part_ml, ctx->part_scale, ctx->piece_tbl};
+  st = decode_launch(ctx, pl, ws, ctx->l_q, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride,
+                     seq_lens, max_seq_len, ctx->l_attn, s, &cw);
+  if (st != MLA_OK) return st;
+  {
+    ProjArgs pa{};
+    pa.X = static_cast<const uint16_t*>(ctx->l_attn);
+    pa.x_stride = int64_t(H) * DV;
+    pa.W = static_cast<const uint16_t*>(ctx->Wo);
+    pa.M = n_q;
+    pa.N = D;
+    pa.K = H * DV;
+    pa.mode = 1;
+    pa.R = (ctx->layer_flags & MLA_LAYER_RESIDUAL) ? static_cast<const uint16_t*>(hidden) : nullptr;
+    pa.out = static_cast<uint16_t*>(out);
+    ProfScope ps(ctx, MLA_K_LAYER_O, s);
+    e = launch_proj_gemm(pa, s);
+  }
+  return hip_status(e);
 }
 
 namespace {

@@ -46,6 +46,7 @@ struct CacheWriteArgs {
   const double2* rope;   // [(max_position+1) * NPAIR] (cos, sin)
   int32_t max_position;
   double eps;
+  int32_t in_f32;        // 1: c_kv / k_pe are fp32 rows (the layer step's projection), else the storage dtype
 };
 
 struct QAbsorbArgs {
@@ -141,6 +142,26 @@ struct CombineArgs {
   int32_t v_parts;        // bf16: output channels split over this many workgroups (1 or 4)
 };
 
+// The layer step's projections: Y[M, N] = X[M, K] W[N, K]^T (bf16 in, fp32 accumulation), K a
+// multiple of 1,024, N a multiple of 16.
+struct ProjArgs {
+  const uint16_t* X;      // [M, K] rows of stride x_stride
+  int64_t x_stride;
+  const uint16_t* W;      // [N, K]
+  int32_t M, N, K;
+  int32_t norm;           // 1: row m scaled by 1 / sqrt(mean(X[m]^2) + eps) (the input RMSNorm)
+  float eps;
+  int32_t mode;           // 0: query / kv_a projection; 1: output projection
+  // mode 0: outputs n < n_split to y0 [M, n_split] in bf16 (the queries), the rest to y1 [M, N - n_split]
+  // in fp32 (the [c_kv | k_pe] rows the cache write reads)
+  int32_t n_split;
+  uint16_t* y0;
+  float* y1;
+  // mode 1: out [M, N] in bf16 = Y (+ R, the residual stream, when R is not null)
+  const uint16_t* R;
+  uint16_t* out;
+};
+
 // ------------------------------------------------------------------------------ launchers
 
 hipError_t launch_absorb(bool bf16, const AbsorbArgs& a, hipStream_t s);
@@ -168,6 +189,9 @@ constexpr int kMt32MaxSteps = 1024;
 constexpr int kPieceCost = 6;
 hipError_t launch_decode_mt32(const DecodeArgs& a, int T, hipStream_t s);
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s);
+// dst [rows, K] = src [rows, K] * gamma [K] (bf16, rounded once), or a copy when gamma is null
+hipError_t launch_layer_pack(const void* src, const void* gamma, void* dst, int64_t rows, int K, hipStream_t s);
+hipError_t launch_proj_gemm(const ProjArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------------------ device helpers
 

