@@ -208,7 +208,7 @@ mla_status mla_decode_step(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
  * the decoder layer ([P-vllm] DeepseekV3DecoderLayer listing).  bf16 contexts (MLA_BF16 and
  * MLA_BF16_FP8) only.
  *
- *  hidden_dim        D, the hidden size: a positive multiple of 1,024 (DeepSeek-V2-Lite: 2,048).
+ *  hidden_dim        D, the hidden size: a positive multiple of 512 (DeepSeek-V2-Lite: 2,048).
  *  q_proj_w          device bf16 [H*(dn+dr), D]: per head [nope | rope] query rows (no query
  *                    low-rank step, the V2-Lite shape).
  *  kv_a_proj_w       device bf16 [dc + dr, D]: compressed_kv rows then k_pe rows.
@@ -223,7 +223,7 @@ mla_status mla_decode_step(mla_ctx* ctx, const void* c_kv, int64_t c_kv_row_stri
  * and rounded to bf16 once); the caller's buffers may be freed after the call.  It also sizes the
  * step's workspace from the context's max_q_tokens.  A second call replaces the first.
  * Returns MLA_EINVAL (null ctx or weights, unknown flags), MLA_EUNSUPPORTED (fp32 context, hidden_dim
- * not a positive multiple of 1,024), MLA_ENOMEM, MLA_EHIP.
+ * not a positive multiple of 512), MLA_ENOMEM, MLA_EHIP.
  */
 enum { MLA_LAYER_INPUT_NORM = 1, MLA_LAYER_RESIDUAL = 2 };
 mla_status mla_layer_weights(mla_ctx* ctx, int32_t hidden_dim, const void* q_proj_w, const void* kv_a_proj_w,

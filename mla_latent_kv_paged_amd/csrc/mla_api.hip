@@ -88,6 +88,8 @@ struct mla_ctx {
   void* l_q = nullptr;        // [max_q_tokens, H, QW] bf16 queries
   float* l_ckv = nullptr;     // [max_q_tokens, ROW] fp32 [c_kv | k_pe] rows
   void* l_attn = nullptr;     // [max_q_tokens, H, DV] bf16 attention output
+  float* l_part = nullptr;    // projection partial tiles (ProjArgs::part), sized for both projections
+  float* l_ss = nullptr;      // their per-token sums of squares
   Prof prof;
 };
 
@@ -114,6 +116,8 @@ void ctx_release(mla_ctx* c) {
   hipFree(c->l_q);
   hipFree(c->l_ckv);
   hipFree(c->l_attn);
+  hipFree(c->l_part);
+  hipFree(c->l_ss);
   if (c->prof.created)
     for (int k = 0; k < MLA_K_COUNT; ++k)
       for (int i = 0; i < kProfRing; ++i) {
@@ -566,19 +570,29 @@ mla_status mla_layer_weights(mla_ctx* ctx, int32_t hidden_dim, const void* q_pro
                              const void* o_proj_w, const void* input_norm_gamma, int32_t flags, void* stream) {
   if (!ctx || !q_proj_w || !kv_a_proj_w || !o_proj_w) return MLA_EINVAL;
   if (flags & ~(MLA_LAYER_INPUT_NORM | MLA_LAYER_RESIDUAL)) return MLA_EINVAL;
-  if (!ctx->bf16 || hidden_dim <= 0 || hidden_dim % 1024 != 0) return MLA_EUNSUPPORTED;
+  if (!ctx->bf16 || hidden_dim <= 0 || hidden_dim % kProjChunk != 0) return MLA_EUNSUPPORTED;
   const int H = ctx->cfg.num_heads;
   const int64_t n1 = int64_t(H) * QW + ROW;
   const size_t mq = size_t(ctx->cfg.max_q_tokens);
-  // a second call replaces the first
-  hipFree(ctx->W1);
-  hipFree(ctx->Wo);
-  hipFree(ctx->l_q);
-  hipFree(ctx->l_ckv);
-  hipFree(ctx->l_attn);
-  ctx->W1 = ctx->Wo = ctx->l_q = ctx->l_attn = nullptr;
-  ctx->l_ckv = nullptr;
-  ctx->hidden_dim = 0;
+  auto release = [&]() {
+    hipFree(ctx->W1);
+    hipFree(ctx->Wo);
+    hipFree(ctx->l_q);
+    hipFree(ctx->l_ckv);
+    hipFree(ctx->l_attn);
+    hipFree(ctx->l_part);
+    hipFree(ctx->l_ss);
+    ctx->W1 = ctx->Wo = ctx->l_q = ctx->l_attn = nullptr;
+    ctx->l_ckv = ctx->l_part = ctx->l_ss = nullptr;
+    ctx->hidden_dim = 0;
+  };
+  release();  // a second call replaces the first
+  // projection workspace: both projections' output tiles of 64 and K chunks, for m tiles of 64 tokens
+  const size_t m_tiles = (mq + 63) / 64;
+  const size_t tiles_qkv = size_t(n1 / 64) * (hidden_dim / kProjChunk);
+  const size_t tiles_o = size_t(hidden_dim / 64) * (H * DV / kProjChunk);
+  const size_t tiles = std::max(tiles_qkv, tiles_o);
+  const size_t chunks = std::max<size_t>(hidden_dim, size_t(H) * DV) / kProjChunk;
   hipError_t e = hipSuccess;
   auto alloc = [&](void** p, size_t n) {
     if (e == hipSuccess) e = hipMalloc(p, n);
@@ -588,6 +602,8 @@ mla_status mla_layer_weights(mla_ctx* ctx, int32_t hidden_dim, const void* q_pro
   alloc(&ctx->l_q, mq * H * QW * 2);
   alloc(reinterpret_cast<void**>(&ctx->l_ckv), mq * ROW * sizeof(float));
   alloc(&ctx->l_attn, mq * H * DV * 2);
+  alloc(reinterpret_cast<void**>(&ctx->l_part), m_tiles * tiles * 64 * 64 * sizeof(float));
+  alloc(reinterpret_cast<void**>(&ctx->l_ss), m_tiles * chunks * 64 * sizeof(float));
   hipStream_t s = as_stream(stream);
   const void* g = (flags & MLA_LAYER_INPUT_NORM) ? input_norm_gamma : nullptr;
   if (e == hipSuccess) e = launch_layer_pack(q_proj_w, g, ctx->W1, int64_t(H) * QW, hidden_dim, s);
@@ -597,13 +613,7 @@ mla_status mla_layer_weights(mla_ctx* ctx, int32_t hidden_dim, const void* q_pro
   if (e == hipSuccess) e = launch_layer_pack(o_proj_w, nullptr, ctx->Wo, hidden_dim, H * DV, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
-    hipFree(ctx->W1);
-    hipFree(ctx->Wo);
-    hipFree(ctx->l_q);
-    hipFree(ctx->l_ckv);
-    hipFree(ctx->l_attn);
-    ctx->W1 = ctx->Wo = ctx->l_q = ctx->l_attn = nullptr;
-    ctx->l_ckv = nullptr;
+    release();
     return hip_status(e);
   }
   ctx->hidden_dim = hidden_dim;
@@ -644,6 +654,8 @@ mla_status mla_layer_decode_step(mla_ctx* ctx, const void* hidden, const int32_t
     pa.n_split = H * QW;
     pa.y0 = static_cast<uint16_t*>(ctx->l_q);
     pa.y1 = ctx->l_ckv;
+    pa.part = ctx->l_part;
+    pa.ss_part = ctx->l_ss;
     ProfScope ps(ctx, MLA_K_LAYER_QKV, s);
     e = launch_proj_gemm(pa, s);
   }
@@ -663,6 +675,8 @@ mla_status mla_layer_decode_step(mla_ctx* ctx, const void* hidden, const int32_t
     pa.mode = 1;
     pa.R = (ctx->layer_flags & MLA_LAYER_RESIDUAL) ? static_cast<const uint16_t*>(hidden) : nullptr;
     pa.out = static_cast<uint16_t*>(out);
+    pa.part = ctx->l_part;
+    pa.ss_part = ctx->l_ss;
     ProfScope ps(ctx, MLA_K_LAYER_O, s);
     e = launch_proj_gemm(pa, s);
   }

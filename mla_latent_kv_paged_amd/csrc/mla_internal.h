@@ -143,7 +143,9 @@ struct CombineArgs {
 };
 
 // The layer step's projections: Y[M, N] = X[M, K] W[N, K]^T (bf16 in, fp32 accumulation), K a
-// multiple of 1,024, N a multiple of 16.
+// multiple of kProjChunk, N a multiple of 64.  K is split into chunks of kProjChunk over workgroups;
+// launch_proj_gemm launches the GEMM and the kernel that adds the chunks and applies the epilogue.
+constexpr int kProjChunk = 512;
 struct ProjArgs {
   const uint16_t* X;      // [M, K] rows of stride x_stride
   int64_t x_stride;
@@ -160,6 +162,10 @@ struct ProjArgs {
   // mode 1: out [M, N] in bf16 = Y (+ R, the residual stream, when R is not null)
   const uint16_t* R;
   uint16_t* out;
+  // workspace: fp32 partial tiles [m tiles][N / 64][K / kProjChunk][64 x 64] and the chunks' per-token
+  // sums of squares [m tiles][K / kProjChunk][64]
+  float* part;
+  float* ss_part;
 };
 
 // ------------------------------------------------------------------------------ launchers

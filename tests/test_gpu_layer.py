@@ -292,9 +292,9 @@ def test_layer_status_codes():
         with pytest.raises(MLAError) as e:          # no layer attached
             ctx.layer_decode_step(h, i2, i2, pool, bt, sl, 40)
         assert e.value.status == -1
-        bad = torch.zeros((16 * 192, 1536), dtype=torch.bfloat16, device="cuda")
+        bad = torch.zeros((16 * 192, 1280), dtype=torch.bfloat16, device="cuda")
         p = bad.data_ptr()
-        assert ctx.lib.mla_layer_weights(ctx.handle, 1536, p, p, p, None, 3, None) == -2  # D not a multiple of 1,024
+        assert ctx.lib.mla_layer_weights(ctx.handle, 1280, p, p, p, None, 3, None) == -2  # D not a multiple of 512
         assert ctx.lib.mla_layer_weights(ctx.handle, 2048, p, p, p, None, 8, None) == -1  # unknown flag
         assert ctx.lib.mla_layer_weights(ctx.handle, 2048, None, p, p, None, 3, None) == -1  # null weights
     finally:
