@@ -70,9 +70,11 @@ def parse():
     ap.add_argument("--layers", type=int, default=1, help="layer mode: attention layers in the model step (each "
                     "with its own weights and cache)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only", "prefill",
-                                                        "prefill-only", "layer", "layer-only"],
+                                                        "prefill-only", "layer", "layer-only", "ceiling"],
                     help="copy-calibration: run a plain 256 MiB device copy (for counter scaling); "
-                         "decode-only: run just the decode loop (for profilers)")
+                         "decode-only: run just the decode loop (for profilers); ceiling: the decode kernel "
+                         "beside a plain streaming read of the same byte count and the decode's block gather "
+                         "alone (no math)")
     return ap.parse_args()
 
 
@@ -340,6 +342,59 @@ def prefill_main(args):
     print(json.dumps(res), flush=True)
 
 
+def ceiling_main(args, w, ctx, pools, q, bt, sl, max_ctx, out):
+    """The decode kernel beside two ceilings for its latent-cache stream, each launch on its own events
+    over rotated pools (every launch reads bytes the previous one did not): a plain streaming read of the
+    same number of bytes, and the decode's HBM -> LDS block gather with no math."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_paged_amd import _lib as L, K_DECODE
+    latent = w.latent_bytes()
+    sink = torch.empty((1 << 20) // 4, dtype=torch.int32, device="cuda")
+    flat = [p.view(-1).view(torch.uint8)[:latent] for p in pools]
+
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return np.array([a_.elapsed_time(b_) for a_, b_ in ev]) * 1e3
+
+    def read(i):
+        L.ceiling_read(flat[i % len(flat)], sink)
+
+    def gather(i):
+        ctx.ceiling_gather(pools[i % len(pools)], bt, sl, max_ctx, sink, q_len=w.q_len)
+
+    def decode(i):
+        ctx.decode(q, pools[i % len(pools)], bt, sl, max_ctx, q_len=w.q_len, out=out)
+
+    for fn in (read, gather, decode):
+        timed(fn, args.warmup)
+    res = {"mode": "ceiling", "workload": w.name, "latent_bytes": latent, "launches": args.steps,
+           "rotated_pools": len(pools)}
+    for name, fn in (("stream_read", read), ("gather_dma", gather), ("decode_events", decode)):
+        t = timed(fn, args.steps)
+        res[name] = {"us_p10": round(float(np.percentile(t, 10)), 2), "us_median": round(float(np.median(t)), 2),
+                     "us_p90": round(float(np.percentile(t, 90)), 2),
+                     "tbps_median": round(latent / (float(np.median(t)) * 1e-6) / 1e12, 3)}
+    # the decode kernel alone, with the library's events around it (as the benchmark's roofline)
+    ctx.profile_enable(True)
+    for i in range(args.steps):
+        decode(i)
+    torch.cuda.synchronize()
+    d = np.array(ctx.profile_samples(K_DECODE)) * 1e3
+    ctx.profile_enable(False)
+    res["decode_kernel"] = {"us_median": round(float(np.median(d)), 2),
+                            "tbps_median": round(latent / (float(np.median(d)) * 1e-6) / 1e12, 3)}
+    res["decode_kernel_vs_gather"] = round(res["gather_dma"]["us_median"] / res["decode_kernel"]["us_median"], 4)
+    res["hbm_peak_tbps"] = HBM_PEAK_GBPS / 1e3
+    ctx.free()
+    print(json.dumps(res), flush=True)
+
+
 def layer_main(args):
     """Decode step from hidden states through `--layers` attention layers (mla_layer_decode_step: input
     RMSNorm, q_proj and kv_a_proj, the cache write of the new tokens, the absorbed attention, o_proj and
@@ -533,6 +588,10 @@ def main():
             ctx.decode(q, p, bt, sl, max_ctx, q_len=w.q_len, out=out)
         else:
             ctx.decode_step(nc, nk, npos, nslot, q, p, bt, sl, max_ctx, q_len=w.q_len, out=out)
+
+    if args.mode == "ceiling":
+        ceiling_main(args, w, ctx, pools, q, bt, sl, max_ctx, out)
+        return
 
     if args.mode == "decode-only":
         for i in range(args.warmup + args.steps):

@@ -345,6 +345,28 @@ mla_status mla_profile_read(mla_ctx* ctx, int32_t kernel_id, double* total_ms, i
  * with max > 0. */
 mla_status mla_profile_samples(mla_ctx* ctx, int32_t kernel_id, float* ms, int32_t max, int32_t* n);
 
+/* ------------------------------------------------------------------------------------------
+ * Measurement kernels (not part of the compute path): the practical ceilings of the decode's
+ * latent-cache stream on this device.
+ * ------------------------------------------------------------------------------------------ */
+
+/* A plain streaming read of `bytes` (a positive multiple of 16) contiguous device bytes at `src` by
+ * 1,024 workgroups of 256 threads, each reading a contiguous range 32 KiB at a time (eight 16-byte
+ * loads per thread in flight); each thread writes one word to `sink` (device, at least 1 MiB) so that
+ * the loads are kept.  Asynchronous on `stream`.
+ * MLA_EINVAL for a null pointer, a size that is not a positive multiple of 16, or a sink too small. */
+mla_status mla_ceiling_read(const void* src, int64_t bytes, void* sink, int64_t sink_bytes, void* stream);
+
+/* The data movement of mla_decode's 16-row bf16 decode kernel and nothing else, for the decode those
+ * arguments describe (same split, work units, unit order, waves, LDS ring and zero-block substitution):
+ * every visible latent-cache block is moved HBM -> LDS by global_load_lds_dwordx4 and read once from LDS;
+ * no MFMA, softmax or partial store.  `sink` (device, at least 512 bytes per workgroup: 128 KiB covers
+ * 256 workgroups) receives one word per thread.  bf16 contexts whose decode shape runs the 16-row
+ * kernel only (MLA_EUNSUPPORTED otherwise); MLA_EINVAL / MLA_ECAP as mla_decode for the rest. */
+mla_status mla_ceiling_gather(mla_ctx* ctx, int32_t batch, int32_t q_len, const void* kv_cache, int32_t num_blocks,
+                              const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+                              int32_t max_seq_len, void* sink, int64_t sink_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

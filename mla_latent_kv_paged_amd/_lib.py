@@ -25,7 +25,7 @@ EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_decode_st
            "mla_free", "mla_status_string",
            "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",
            "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size", "mla_layer_weights",
-           "mla_layer_decode_step")
+           "mla_layer_decode_step", "mla_ceiling_read", "mla_ceiling_gather")
 
 
 class MLAConfig(ctypes.Structure):
@@ -74,6 +74,10 @@ def load(path=None):
     lib.mla_layer_weights.restype = i32
     lib.mla_layer_decode_step.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
     lib.mla_layer_decode_step.restype = i32
+    lib.mla_ceiling_read.argtypes = [vp, i64, vp, i64, vp]
+    lib.mla_ceiling_read.restype = i32
+    lib.mla_ceiling_gather.argtypes = [vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, i64, vp]
+    lib.mla_ceiling_gather.restype = i32
     lib.mla_free.argtypes = [vp]
     lib.mla_free.restype = None
     lib.mla_status_string.argtypes = [i32]
@@ -91,6 +95,13 @@ def load(path=None):
     if path is None:
         _lib = lib
     return lib
+
+
+def ceiling_read(src, sink, stream=None):
+    """mla_ceiling_read: a plain streaming read of every byte of the device tensor src."""
+    nbytes = int(src.numel() * src.element_size())
+    _check(load().mla_ceiling_read(_ptr(src), nbytes, _ptr(sink), int(sink.numel() * sink.element_size()),
+                                   _stream_ptr(stream)), "mla_ceiling_read")
 
 
 def status_string(status):
@@ -337,6 +348,15 @@ class MLAContext:
                                   _ptr(out), _stream_ptr(stream))
         _check(st, "mla_prefill")
         return out
+
+    # -- measurement kernels (not part of the compute path)
+    def ceiling_gather(self, kv_cache, block_table, seq_lens, max_seq_len, sink, q_len=1, stream=None):
+        """mla_ceiling_gather: the 16-row decode kernel's HBM->LDS block stream alone, for this decode."""
+        batch = int(seq_lens.shape[0])
+        _check(self.lib.mla_ceiling_gather(self.handle, batch, q_len, _ptr(kv_cache), int(kv_cache.shape[0]),
+                                           _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+                                           int(max_seq_len), _ptr(sink), int(sink.numel() * sink.element_size()),
+                                           _stream_ptr(stream)), "mla_ceiling_gather")
 
     # -- helpers
     def set_decode_tuning(self, split_blocks=0, waves=0):

@@ -63,13 +63,19 @@ __device__ __forceinline__ void wait_blocks(int n) {
 
 }  // namespace
 
+// NW waves per workgroup (2 or 4), NS ring stages per wave.  With four waves the query tile is moved
+// into the last stage of the last wave's ring (read into registers before that stage first takes a
+// block), which keeps the workgroup within the 160 KiB of LDS at two stages per wave.
 template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
-  static_assert(NW == 2, "the query tile is moved by two waves");
+  static_assert(NW == 2 || NW == 4, "two or four waves");
   static_assert(NS >= 2 && NS <= 4, "a wave keeps at most 3 blocks in flight (vmcnt range)");
-  static_assert(NW * NS * kBlockBytes >= 32 * 64 * 16 + 16 * 1024, "the merge reuses the rings");
+  static_assert(NW * NS * kBlockBytes >= NW * 32 * 64 * 16 + 16 * 1024, "the merge reuses the rings");
+  constexpr bool kQInRing = NW > 2;
+  constexpr int kTilesPerWave = 32 / NW;  // channel tiles each wave finishes in the merge
+  constexpr int kRowsPerWave = 16 / NW;   // partial rows each wave stores
   __shared__ __attribute__((aligned(16))) char ring_mem[NW * NS * kBlockBytes];
-  __shared__ __attribute__((aligned(16))) char q_mem[kBlockBytes];
+  __shared__ __attribute__((aligned(16))) char q_mem[kQInRing ? 16 : kBlockBytes];
   __shared__ float m_lds[NW][16];
   __shared__ float l_lds[NW][16];
   __shared__ float x_lds[NW][16];
@@ -111,12 +117,17 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   const int nid = in_row > 0 ? (in_row + NW - 1) / NW : 0;
   const int phys_lo = lane < nid ? bt[kb0 + w + NW * lane] : 0;
   const int phys_hi = lane + 64 < nid ? bt[kb0 + w + NW * (lane + 64)] : 0;
-  {  // query tile -> LDS: wave w moves rows 8w..8w+7
-    const char* src = static_cast<const char*>(a.qcat) + (int64_t(row) * a.H + h0 + 8 * w + lrow) * (ROW * 2) +
+  lds_char_t* const qbuf = kQInRing ? (lds_char_t*)ring_mem + (NW * NS - 1) * kBlockBytes : (lds_char_t*)q_mem;
+  {  // query tile -> LDS: rows 8 (w % 2) .. + 7; two waves move all 9 chunks of 128 bytes of their
+     // rows, four waves split them 5 + 4
+    const int rh = w % 2;
+    const int gq0 = NW == 2 ? 0 : (w < 2 ? 0 : 5), gq1 = NW == 2 ? 9 : (w < 2 ? 5 : 9);
+    const char* src = static_cast<const char*>(a.qcat) + (int64_t(row) * a.H + h0 + 8 * rh + lrow) * (ROW * 2) +
                       16 * lgr;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_char_t*)q_mem)));
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(qbuf)));
 #pragma unroll
-    for (int gq = 0; gq < 9; ++gq) dma16(src + 128 * gq, dst + 1024 * (9 * w + gq));
+    for (int gq = 0; gq < 9; ++gq)
+      if (gq >= gq0 && gq < gq1) dma16(src + 128 * gq, dst + 1024 * (9 * rh + gq));
   }
   // the ids are complete here: the compiler's wait for them must not land inside the transfer
   // pipeline below (it cannot tell them from the transfers and would wait for all of them)
@@ -173,10 +184,12 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   // query tile in registers, in the B-operand layout of the score MFMA: granule 4k + g of row r16
   u32x4_t qreg[18];
   {
-    const lds_u32x4_t* qp = (const lds_u32x4_t*)((lds_char_t*)q_mem + sc_off);
+    const lds_u32x4_t* qp = (const lds_u32x4_t*)(qbuf + sc_off);
 #pragma unroll
     for (int k = 0; k < 18; ++k) qreg[k] = qp[32 * k];
   }
+  // the query tile's LDS is the last wave's last stage: every wave has read it before it takes a block
+  if constexpr (kQInRing) lds_barrier();
 
   f32x4_t acc[32];
 #pragma unroll
@@ -291,35 +304,27 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) acc[jj] *= sw;
 
-  // Each wave finishes half of the channel tiles: wave w keeps tiles 16w..16w+15, hands the other
-  // half to its partner through LDS ([tile][lane] x 16 B: consecutive lanes, consecutive words)
-  // and writes its half of the partial.
-  static_assert(NW == 2, "two-wave merge");
-  f32x4_t* slots = reinterpret_cast<f32x4_t*>(ring_mem);  // region r = tiles 16r..16r+15
-  if (w == 0) {
+  // Each wave finishes kTilesPerWave of the 32 channel tiles (wave w: tiles kTilesPerWave w ..): every
+  // wave writes its scaled accumulator to LDS ([wave][tile][lane] x 16 B: consecutive lanes,
+  // consecutive words), and each tile is summed over the waves in wave order (deterministic).
+  f32x4_t* slots = reinterpret_cast<f32x4_t*>(ring_mem);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) slots[(16 + t) * 64 + lane] = acc[16 + t];
-  } else {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) slots[t * 64 + lane] = acc[t];
-  }
+  for (int t = 0; t < 32; ++t) slots[(w * 32 + t) * 64 + lane] = acc[t];
   __syncthreads();
-  // this wave's half of the merged accumulator; fixed order for every tile: wave 0's term first
-  f32x4_t fin[16];
-  if (w == 0) {
+  f32x4_t fin[kTilesPerWave];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) fin[t] = acc[t] + slots[t * 64 + lane];
-  } else {
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    fin[t] = slots[(0 * 32 + kTilesPerWave * w + t) * 64 + lane];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) fin[t] = slots[(16 + t) * 64 + lane] + acc[16 + t];
+    for (int ww = 1; ww < NW; ++ww) fin[t] += slots[(ww * 32 + kTilesPerWave * w + t) * 64 + lane];
   }
   // The partial is stored normalised, o = acc / l, in fp16 (a convex combination of cache
   // values), divided by a power of two when the row's largest |o| would not fit fp16.  The row
-  // spans both waves (lanes r16 + 16 g of each): max over the lane's values, its row's four
-  // lanes, then the two waves through LDS.
+  // spans every wave (lanes r16 + 16 g of each): max over the lane's values, its row's four
+  // lanes, then the waves through LDS.
   float mx = 0.f;
 #pragma unroll
-  for (int t = 0; t < 16; ++t)
+  for (int t = 0; t < kTilesPerWave; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(fin[t][e]));
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -327,11 +332,14 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   if (g == 0) x_lds[w][r16] = mx;
   __syncthreads();
   const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
-  const float down = fp16_fit_scale(fmaxf(x_lds[0][r16], x_lds[1][r16]) * inv);
+  float xmax = x_lds[0][r16];
+#pragma unroll
+  for (int ww = 1; ww < NW; ++ww) xmax = fmaxf(xmax, x_lds[ww][r16]);
+  const float down = fp16_fit_scale(xmax * inv);
   const float sc = inv * down;
   // through an LDS tile (16 rows x 1 KB after the exchange slots; granule G of row r at slot
   // G ^ r) so that each store instruction writes one whole 1 KB row
-  lds_char_t* const otile = (lds_char_t*)ring_mem + 32 * 64 * 16;
+  lds_char_t* const otile = (lds_char_t*)ring_mem + NW * 32 * 64 * 16;
   auto put = [&](int jj, f32x4_t v) {  // channels 16 jj + 4 g .. + 3 of row r16: granule 2 jj + g / 2
     v *= sc;
     const int G = 2 * jj + (g >> 1);
@@ -339,11 +347,11 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
         u32x2_t{cvt_pk_f16(v[0], v[1]), cvt_pk_f16(v[2], v[3])};
   };
 #pragma unroll
-  for (int t = 0; t < 16; ++t) put(16 * w + t, fin[t]);
+  for (int t = 0; t < kTilesPerWave; ++t) put(kTilesPerWave * w + t, fin[t]);
   __syncthreads();
   const int64_t pidx = (int64_t(row) * a.H + h0 + r16) * a.n_split + j;  // this lane's row (r16)
 #pragma unroll
-  for (int r = 8 * w; r < 8 * w + 8; ++r) {  // wave w stores rows 8w..8w+7
+  for (int r = kRowsPerWave * w; r < kRowsPerWave * w + kRowsPerWave; ++r) {  // wave w's rows
     const int64_t pr = (int64_t(row) * a.H + h0 + r) * a.n_split + j;
     *reinterpret_cast<u32x4_t*>(a.part_o16 + pr * DC + 8 * lane) =
         *(const lds_u32x4_t*)(otile + r * 1024 + 16 * (lane ^ r));
@@ -358,6 +366,9 @@ hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t 
   switch (waves) {
     case 2:
       decode_bf16_kernel<2, 3><<<grid, 128, 0, s>>>(a);
+      break;
+    case 4:
+      decode_bf16_kernel<4, 2><<<grid, 256, 0, s>>>(a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -754,11 +754,47 @@ void mla_free(mla_ctx* ctx) {
   ctx_release(ctx);
 }
 
+mla_status mla_ceiling_read(const void* src, int64_t bytes, void* sink, int64_t sink_bytes, void* stream) {
+  constexpr int kGrid = 1024;
+  if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || sink_bytes < int64_t(kGrid) * 256 * 4) return MLA_EINVAL;
+  return hip_status(launch_stream_read(src, bytes, static_cast<uint32_t*>(sink), kGrid, as_stream(stream)));
+}
+
+mla_status mla_ceiling_gather(mla_ctx* ctx, int32_t batch, int32_t q_len, const void* kv_cache, int32_t num_blocks,
+                              const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+                              int32_t max_seq_len, void* sink, int64_t sink_bytes, void* stream) {
+  if (!sink) return MLA_EINVAL;
+  DecodePlan pl;
+  // the decode's own plan (its q and out pointers are not read: the sink stands in for both)
+  const mla_status st = decode_plan(ctx, sink, batch, q_len, kv_cache, num_blocks, block_table, block_table_stride,
+                                    seq_lens, max_seq_len, sink, &pl);
+  if (st != MLA_OK) return st;
+  if (!ctx->bf16 || ctx->fp8 || pl.t32 != 0 || pl.waves != 2) return MLA_EUNSUPPORTED;
+  const int units = batch * pl.n_split * pl.groups;
+  const int64_t grid = (int64_t(units) + 7) / 8 * 8;
+  if (sink_bytes < grid * 128 * 4) return MLA_EINVAL;
+  DecodeArgs da{};
+  da.batch = batch;
+  da.cache = kv_cache;
+  da.zero_block = ctx->zero_block;
+  da.num_blocks = num_blocks;
+  da.block_table = block_table;
+  da.bt_stride = block_table_stride;
+  da.seq_lens = seq_lens;
+  da.max_seq_len = max_seq_len;
+  da.q_len = q_len;
+  da.H = ctx->cfg.num_heads;
+  da.split_blocks = pl.sb;
+  da.n_split = pl.n_split;
+  da.n_rt = pl.n_rt;
+  da.units = units;
+  return hip_status(launch_gather_dma(da, static_cast<uint32_t*>(sink), as_stream(stream)));
+}
+
 mla_status mla_set_decode_tuning(mla_ctx* ctx, int32_t split_blocks, int32_t waves_per_group) {
   if (!ctx || split_blocks < 0) return MLA_EINVAL;
-  // 2 for every 16-row kernel; 4 for the FP8 one only
-  if (waves_per_group != 0 && waves_per_group != 2 && !(waves_per_group == 4 && ctx->fp8))
-    return MLA_EINVAL;
+  // 2 or 4 for the 16-row kernels (bf16 and FP8 rows)
+  if (waves_per_group != 0 && waves_per_group != 2 && waves_per_group != 4) return MLA_EINVAL;
   ctx->forced_split_blocks = split_blocks;
   ctx->forced_waves = waves_per_group;
   return MLA_OK;

@@ -198,6 +198,9 @@ hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s);
 // dst [rows, K] = src [rows, K] * gamma [K] (bf16, rounded once), or a copy when gamma is null
 hipError_t launch_layer_pack(const void* src, const void* gamma, void* dst, int64_t rows, int K, hipStream_t s);
 hipError_t launch_proj_gemm(const ProjArgs& a, hipStream_t s);
+// measurement kernels (ceiling.hip)
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+hipError_t launch_gather_dma(const DecodeArgs& a, uint32_t* sink, hipStream_t s);
 
 // ------------------------------------------------------------------------------ device helpers
 

@@ -245,12 +245,15 @@ def test_score_climb(heads, q_len):
     ctx = MLAContext(dev(kvb, "bf16"), None, num_heads=heads, dtype="bf16", rms_eps=w.eps, rope_theta=w.theta,
                      max_q_tokens=w.n_q, max_batch=w.batch, max_position=mx + 16, max_seq_len=mx + 16)
     try:
-        for sb in (0, 1, 160):  # library choice; fewest 32-row workgroups; longest 16-row splits
-            ctx.set_decode_tuning(sb, 0)
+        # library choice; fewest 32-row workgroups; longest 16-row splits, at two and four waves
+        for sb, waves in ((0, 0), (1, 0), (160, 0), (160, 4), (3, 4)):
+            if waves and (heads * q_len) % 32 == 0:
+                continue  # the wave count applies to the 16-row kernel
+            ctx.set_decode_tuning(sb, waves)
             out = ctx.decode(dev(q, "bf16"), dev(pool, "bf16"), dev_i32(w.block_table), dev_i32(w.seq_lens), mx,
                              q_len=w.q_len)
             torch.cuda.synchronize()
-            compare(out, ref, "bf16", f"score climb H={heads} q_len={q_len} tuning={sb}")
+            compare(out, ref, "bf16", f"score climb H={heads} q_len={q_len} tuning={sb} waves={waves}")
     finally:
         ctx.free()
 
@@ -269,6 +272,27 @@ def test_split_sweep_and_determinism(storage, heads, q_len):
             compare(out, ref, storage, f"split_blocks={sb}")
             again = run.decode(split_blocks=sb)
             assert torch.equal(out, again), f"non-deterministic at split_blocks={sb}"
+    finally:
+        run.free()
+
+
+@pytest.mark.parametrize("waves", [2, 4])
+def test_16row_kernel_waves_split_sweep(waves):
+    """The 16-row bf16 kernel (16 heads, one query token) at two and four waves per workgroup: split sizes
+    from one block to past the longest context (a wave with no block, odd block counts per wave), each run
+    twice (bitwise equal), against the oracle; contexts of 1 to 1,500 tokens."""
+    w = W.custom("w16", "bf16", 16, [1, 15, 16, 17, 200, 513, 1000, 1500], q_len=1, seed=33)
+    _say("16-row kernel", "waves", waves)
+    _, ref = oracle_full(w)
+    run = GpuRun(w)
+    try:
+        for sb in (1, 2, 3, 5, 8, 13, 33, 96, 0):
+            out = run.decode(split_blocks=sb, waves=waves)
+            shape = run.ctx.last_decode_shape()
+            assert shape["waves"] == waves, shape
+            compare(out, ref, "bf16", f"waves={waves} split_blocks={sb}")
+            again = run.decode(split_blocks=sb, waves=waves)
+            assert torch.equal(out, again), f"non-deterministic at waves={waves} split_blocks={sb}"
     finally:
         run.free()
 
