@@ -307,3 +307,68 @@ def test_layer_status_codes():
                                            None) == -2  # fp32 context: unsupported
     finally:
         ctx32.free()
+
+
+def test_model_step_27_layers_every_layer():
+    """A decode step through 27 attention layers (one context, set of weights and cache per layer, layer l's
+    output the input of layer l + 1), as bench.py --mode layer --layers 27 runs it, at 16 heads, three
+    sequences.  Every layer's output and new cache rows against the oracle's layer step on the GPU's own
+    input to that layer (the bf16 rounding of each layer's output is then not carried into the next
+    comparison); the end-to-end result against the oracle's 27-layer model step within the bound those
+    roundings allow."""
+    L_ = 27
+    w = W.custom("model27", "bf16", 16, [130, 37, 300], q_len=1, seed=405)
+    _say("27-layer model step")
+    runs, lws = [], []
+    try:
+        for li in range(L_):
+            lw = w.layer_weights(li)
+            run = LayerRun(w, lw)
+            if li:  # layers other than 0 draw their own history
+                for b in range(w.batch):
+                    c, k = w.history(b, li)
+                    hist = int(w.seq_lens[b]) - 1
+                    run.ctx.cache_write(dev(c[:hist], "bf16"), dev(k[:hist], "bf16"), dev_i32(np.arange(hist)),
+                                        dev_i32(w.slots(b, 0, hist)), run.pool)
+            runs.append(run)
+            lws.append(lw)
+        h = w.hidden()
+        ins, outs, pools = [], [], []
+        for run in runs:
+            ins.append(h)
+            h = run.step(h)
+            outs.append(h)
+            pools.append(run.pool.to(torch.float32).cpu().numpy().astype(np.float64))
+    finally:
+        for run in runs:
+            run.free()
+    new = w.all_tokens(new_only=True)
+    caches0 = []
+    for li in range(L_):
+        hist = {k: [] for k in ("c_kv", "k_pe", "positions", "slot_mapping")}
+        for b in range(w.batch):
+            c, k = w.history(b, li)
+            n = int(w.seq_lens[b]) - 1
+            hist["c_kv"].append(c[:n]); hist["k_pe"].append(k[:n])
+            hist["positions"].append(np.arange(n)); hist["slot_mapping"].append(w.slots(b, 0, n))
+        cache = O.cache_write(np.full((w.n_blocks, 16, 1, 576), np.nan), np.concatenate(hist["c_kv"]),
+                              np.concatenate(hist["k_pe"]), np.concatenate(hist["positions"]),
+                              np.concatenate(hist["slot_mapping"]), lws[li]["kv_norm_gamma"].astype(np.float64), w.eps,
+                              w.theta, "bf16")
+        caches0.append(cache)
+        ref, cache_after = L.layer_decode_step(ins[li], new["positions"], new["slot_mapping"], cache, w.block_table,
+                                               w.seq_lens, 1, _weights(w, lws[li]))
+        _compare_out(outs[li], ref, True, f"layer {li}")
+        _check_rows(pools[li], cache_after, new["slot_mapping"], f"layer {li}")
+    # end to end: the oracle's model step keeps the residual stream in fp64, the GPU stores it in bf16 after
+    # every layer.  The per-layer checks above are the parity; end to end, each layer's error carries into the
+    # next through the residual, so elementwise the errors add up to at most L times one layer's bound, and in
+    # relative L2 the output roundings (at most 2^-9 of a value each, independent) grow like a random walk,
+    # sqrt(L) 2^-9 on top of the single-step bound
+    ref27, _ = L.model_decode_step(w.hidden(), new["positions"], new["slot_mapping"], caches0, w.block_table,
+                                   w.seq_lens, 1, [_weights(w, lw) for lw in lws])
+    err = np.abs(outs[-1] - ref27)
+    rel = float(np.linalg.norm(outs[-1] - ref27) / np.linalg.norm(ref27))
+    _say(f"27 layers end to end: max abs {err.max():.3e}, rel L2 {rel:.3e}")
+    assert np.all(err <= L_ * (2e-2 + 0.5 * _spacing(ref27)))
+    assert rel <= 5e-3 + np.sqrt(L_) * 2.0 ** -9
