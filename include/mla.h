@@ -267,8 +267,9 @@ mla_status mla_layer_decode_step(mla_ctx* ctx, const void* hidden, const int32_t
  * [P-vllm] §2.3 and the block table of [P-hybrid] §2.1:
  *   out[i, h] = softmax_{t <= p_i}(scale (q_nope . K_nope[t, h] + RoPE(q_pe, p_i) . k_pe_t)) V[t, h]
  * Sequence b's n_b = cu_q_lens[b+1] - cu_q_lens[b] new tokens sit at positions ctx_b - n_b ..
- * ctx_b - 1 and must already be in the cache (mla_cache_write), as for mla_decode.  bf16 storage
- * (MLA_BF16) only.
+ * ctx_b - 1 and must already be in the cache (mla_cache_write), as for mla_decode.  bf16 contexts
+ * (MLA_BF16 and MLA_BF16_FP8) only; over FP8 rows the latent values are the dequantised ones,
+ * code x group scale, as in mla_decode.
  *
  *  q           device bf16 [total_q, H, dn + dr], un-rotated queries, rows in sequence order
  *  cu_q_lens   device int32 [batch + 1], prefix sums of the chunk lengths (cu_q_lens[0] = 0,
@@ -281,7 +282,7 @@ mla_status mla_layer_decode_step(mla_ctx* ctx, const void* hidden, const int32_t
  * trusted like mla_decode's; a chunk whose prefix sums are inconsistent is skipped (its rows are not
  * written).  Returns MLA_EINVAL (null pointer, batch < 1, total_q < 1, max_q_len < 1,
  * max_seq_len < max_q_len, num_blocks <= 0, stride smaller than ceil(max_seq_len/16), workspace too
- * small), MLA_EUNSUPPORTED (a storage dtype other than MLA_BF16), MLA_ECAP (max_seq_len - 1 >
+ * small), MLA_EUNSUPPORTED (an MLA_F32 context), MLA_ECAP (max_seq_len - 1 >
  * max_position), MLA_EHIP.
  */
 mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, int32_t batch, int32_t total_q,

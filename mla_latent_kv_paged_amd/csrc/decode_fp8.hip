@@ -56,14 +56,6 @@ __device__ __forceinline__ void wait_blocks8(int n) {  // at most n blocks (11 t
     wait_vmcnt<33>();
 }
 
-// e4m3 codes -> bf16, exactly (every e4m3 value is a bf16 value); byte k of w -> element k
-template <bool HI>
-__device__ __forceinline__ uint32_t cvt2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
-}
-__device__ __forceinline__ u32x4_t codes8(u32x2_t c) {
-  return u32x4_t{cvt2<false>(c[0]), cvt2<true>(c[0]), cvt2<false>(c[1]), cvt2<true>(c[1])};
-}
 __device__ __forceinline__ s16x4_t codes4(uint32_t c) {
   return __builtin_bit_cast(s16x4_t, make_uint2(cvt2<false>(c), cvt2<true>(c)));
 }

@@ -703,7 +703,7 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
                        size_t workspace_bytes, void* out, void* stream) {
   if (!ctx || !q || !cu_q_lens || !kv_cache || !block_table || !seq_lens || !workspace || !out) return MLA_EINVAL;
   if (batch < 1 || total_q < 1 || max_q_len < 1 || num_blocks <= 0 || max_seq_len < max_q_len) return MLA_EINVAL;
-  if (!ctx->bf16 || ctx->fp8) return MLA_EUNSUPPORTED;
+  if (!ctx->bf16) return MLA_EUNSUPPORTED;
   const mla_config& cf = ctx->cfg;
   if (max_seq_len - 1 > cf.max_position) return MLA_ECAP;
   const int max_blocks = (max_seq_len + BLK - 1) / BLK;
@@ -738,7 +738,7 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
   hipError_t e;
   {
     ProfScope ps(ctx, MLA_K_PF_EXPAND, s);
-    e = launch_prefill_expand(pa, s);
+    e = launch_prefill_expand(pa, ctx->fp8, s);
   }
   if (e != hipSuccess) return hip_status(e);
   {

@@ -100,7 +100,7 @@ struct PrefillArgs {
   const int32_t* cu_q_lens;    // [batch + 1]
   int32_t total_q;
   int32_t max_q_len;           // an upper bound of every chunk length (sizes the grids)
-  const void* cache;           // bf16 [num_blocks, BLK, 1, ROW]
+  const void* cache;           // bf16 [num_blocks, BLK, 1, ROW], or FP8 rows [num_blocks, BLK, 1, kFp8Row]
   const void* zero_block;
   int32_t num_blocks;
   const int32_t* block_table;
@@ -182,7 +182,8 @@ hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 // FP8 cache rows (kFp8Row bytes), 16-row tiles; every H multiple of 16 and every q_len
 hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s);
-hipError_t launch_prefill_expand(PrefillArgs a, hipStream_t s);
+// fp8: the cache holds FP8 rows (kFp8Row bytes) instead of bf16 rows
+hipError_t launch_prefill_expand(PrefillArgs a, bool fp8, hipStream_t s);
 hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s);
 // bf16, 32-row tiles (H*q_len a multiple of 32), T in {1, 2, 4} tiles per workgroup; n_rt = tiles of
 // 32 rows per sequence (a multiple of T); units = workgroups, enough that every workgroup's share
@@ -266,6 +267,16 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   float f = __double2float_rz(x);
   if (double(f) != x && !__builtin_isnan(x)) f = __uint_as_float(__float_as_uint(f) | 1u);
   return f32_to_bf16(f);
+}
+
+// e4m3 codes -> bf16, exactly (every e4m3 value is a bf16 value), with the hardware converter at scale
+// 1; byte k of w -> element k
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
+}
+__device__ __forceinline__ u32x4_t codes8(u32x2_t c) {
+  return u32x4_t{cvt2<false>(c[0]), cvt2<true>(c[0]), cvt2<false>(c[1]), cvt2<true>(c[1])};
 }
 
 // Context length of sequence b as the kernels use it: clamped to [q_len, max_seq_len].

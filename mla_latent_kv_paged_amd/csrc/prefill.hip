@@ -81,8 +81,15 @@ __device__ __forceinline__ float add_pk_bf16(uint32_t x, float acc) {
 // ----------------------------------------------------------------------------------------- expand
 
 // 128 KiB of LDS: one workgroup, so one wave per SIMD, per CU; the compiler is told so, and may use
-// the whole register file for reading ahead
+// the whole register file for reading ahead.
+// FP8: the cache rows are the 656-byte FP8 rows (latent codes, bf16 rope values, four fp32 group scales;
+// mla_cache_write).  Every e4m3 value is a bf16 value, so the codes are the MFMA's B operand exactly, and
+// the K steps of each group of 128 channels accumulate apart; the group's tile is then added to the
+// output times that token's group scale (a lane holds one token: one scale per lane), in fp32.
+template <bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_expand_kernel(PrefillArgs a) {
+  constexpr int kRowBytes = FP8 ? kFp8Row : ROW * 2;  // one cache row
+  constexpr int kRopeOff = FP8 ? DC : DC * 2;          // its rope values (bf16)
   // W_uk[h] or W_uv[h]: 128 rows of 512 values; granule c (8 values) of row r at slot c ^ (r % 16)
   __shared__ __attribute__((aligned(16))) char wl[DN * DC * 2];
   static_assert(DN == DV, "one staging buffer for both parts");
@@ -130,19 +137,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(kSubPerWave <= 64, "one id per lane");
   const int ids = (lane < kSubPerWave && tw + 16 * lane < ctx) ? bt[tw / BLK + lane] : -1;
   asm volatile("" ::"v"(ids));  // complete before the row loads
-  auto load_b = [&](int st, u32x4_t (&bq)[16]) {
+  // the latent part of one token row: bf16, 16 K steps of 8 values per lane (16 bytes); FP8, 16 K steps
+  // of 8 codes (8 bytes) and the row's four group scales
+  struct Brow {
+    u32x4_t v[FP8 ? 1 : 16];
+    u32x2_t c[FP8 ? 16 : 1];
+    f32x4_t sc;
+  };
+  auto load_b = [&](int st, Brow& bq) {
     const int tb = tw + 16 * st;
     const int tok = tb + r16;
     const int phys = __builtin_amdgcn_readlane(ids, st);  // st <= kSubPerWave < 64: -1 past the range
     const bool ok = tok < ctx && unsigned(phys) < unsigned(a.num_blocks);
     // rows past the context or of an invalid block read the zero block: no divergent loads, which
     // would make the compiler wait for every load in flight
-    const char* crow = ok ? cache + (int64_t(phys) * BLK + tok % BLK) * (ROW * 2) : zero;
+    const char* crow = ok ? cache + (int64_t(phys) * BLK + tok % BLK) * kRowBytes : zero;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) bq[s] = *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * g);
+      for (int s = 0; s < 16; ++s) bq.c[s] = *reinterpret_cast<const u32x2_t*>(crow + 32 * s + 8 * g);
+      bq.sc = *reinterpret_cast<const f32x4_t*>(crow + DC + 2 * DR);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) bq.v[s] = *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * g);
+    }
     return phys;
   };
-  auto step = [&](int st, const u32x4_t (&cb)[16], int phys) {
+  auto step = [&](int st, const Brow& cb, int phys) {
     const int tb = tw + 16 * st;
     const int tok = tb + r16;
     f32x4_t acc[8];
@@ -155,12 +175,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int jt = 0; jt < 8; ++jt) d[jt] = *(const lds_u32x4_t*)(wa + jt * 16 * (DC * 2) + 16 * ((4 * s + g) ^ r16));
     };
     load_a(0, av[0]);
+    if constexpr (FP8) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      if (s + 1 < 16) load_a(s + 1, av[(s + 1) & 1]);
+      for (int G = 0; G < 4; ++G) {  // scale group G: K steps 4G .. 4G + 3
+        f32x4_t gacc[8];
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) acc[jt] = mfma32v(av[s & 1][jt], cb[s], acc[jt]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int jt = 0; jt < 8; ++jt) gacc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int s = 4 * G + q;
+          if (s + 1 < 16) load_a(s + 1, av[(s + 1) & 1]);
+          const u32x4_t bv = codes8(cb.c[s]);
+#pragma unroll
+          for (int jt = 0; jt < 8; ++jt) gacc[jt] = mfma32v(av[s & 1][jt], bv, gacc[jt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) acc[jt] += cb.sc[G] * gacc[jt];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        if (s + 1 < 16) load_a(s + 1, av[(s + 1) & 1]);
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) acc[jt] = mfma32v(av[s & 1][jt], cb.v[s], acc[jt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // D[dim][token]: lane (token r16, g) holds dims 16 jt + 4 g .. + 3
     if (tok < ctx) {
@@ -174,7 +214,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int rt = tb + (lane >> 2);
       if (rt < ctx) {
         const bool rok = unsigned(phys) < unsigned(a.num_blocks);
-        const char* src = (rok ? cache + (int64_t(phys) * BLK + rt % BLK) * (ROW * 2) + DC * 2 : zero) + 32 * (lane & 3);
+        const char* src = (rok ? cache + (int64_t(phys) * BLK + rt % BLK) * kRowBytes + kRopeOff : zero) + 32 * (lane & 3);
         const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src);
         const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(kvrow0 + int64_t(rt) * kKV + DN + 16 * (lane & 3));
@@ -187,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // groups of four sub-tiles; within a group the buffers alternate at compile time, and the
   // prefetch is unconditional (past the wave's range it reads the zero block: lane kSubPerWave's id
   // is -1), so that no branch guards a load
-  u32x4_t bq[2][16];
+  Brow bq[2];
   int ph[2];
   ph[0] = load_b(0, bq[0]);
   for (int G = 0; G < kSubPerWave / 4; ++G) {
@@ -201,11 +241,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-hipError_t launch_prefill_expand(PrefillArgs a, hipStream_t s) {
+hipError_t launch_prefill_expand(PrefillArgs a, bool fp8, hipStream_t s) {
   const int64_t units = int64_t(a.batch) * (a.t_pad / kExpandTokens) * a.H * 2;
   if (units > 0x7fffffff) return hipErrorInvalidValue;
   a.units = int32_t(units);
-  prefill_expand_kernel<<<a.units, 256, 0, s>>>(a);
+  if (fp8)
+    prefill_expand_kernel<true><<<a.units, 256, 0, s>>>(a);
+  else
+    prefill_expand_kernel<false><<<a.units, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -85,35 +85,35 @@ def e4m3_decode(codes):
 
 
 def group_scale(amax):
-    """fp32 scale of a group with largest magnitude amax (see the module docstring)."""
-    if amax == 0.0:
-        return 1.0
-    s = float(np.float32(amax / E4M3_MAX))
-    if amax > E4M3_MAX * s:          # 448 * s is exact in fp64
-        s = float(np.nextafter(np.float32(s), np.float32(np.inf)))
-    return s
+    """fp32 scale of a group with largest magnitude amax (see the module docstring); amax may be an
+    array of group maxima, one scale each."""
+    amax = np.asarray(amax, dtype=np.float64)
+    s = (amax / E4M3_MAX).astype(np.float32)
+    up = amax > E4M3_MAX * s.astype(np.float64)          # 448 * s is exact in fp64
+    s = np.where(up, np.nextafter(s, np.float32(np.inf)), s).astype(np.float64)
+    s = np.where(amax == 0.0, 1.0, s)
+    return float(s) if s.ndim == 0 else s
 
 
 def quantize_latent(c):
-    """c [512] float64 -> (codes uint8 [512], scales float64 [4] (fp32 values))."""
+    """c [..., 512] float64 -> (codes uint8 [..., 512], scales float64 [..., 4] (fp32 values)).
+    Each row is quantised on its own: rows are independent."""
     c = np.asarray(c, dtype=np.float64)
-    codes = np.empty(DC, dtype=np.uint8)
-    scales = np.empty(DC // GROUP, dtype=np.float64)
-    for g in range(DC // GROUP):
-        part = c[g * GROUP:(g + 1) * GROUP]
-        s = group_scale(float(np.max(np.abs(part))))
-        scales[g] = s
-        codes[g * GROUP:(g + 1) * GROUP] = e4m3_encode(part / s)
-    return codes, scales
+    groups = c.reshape(c.shape[:-1] + (DC // GROUP, GROUP))
+    scales = group_scale(np.max(np.abs(groups), axis=-1))
+    codes = e4m3_encode(groups / np.asarray(scales)[..., None])
+    return codes.reshape(c.shape), scales
 
 
 def pack_row(codes, rope_bf16, scales):
-    """One 656-byte cache row from the latent codes, the bf16 rope values and the 4 scales."""
-    row = np.zeros(ROW_BYTES, dtype=np.uint8)
-    row[:DC] = codes
-    bits = np.asarray(rope_bf16, dtype=np.float64).astype(np.float32).view(np.uint32) >> 16
-    row[DC:DC + 2 * DR] = bits.astype("<u2").view(np.uint8)
-    row[DC + 2 * DR:] = np.asarray(scales, dtype=np.float64).astype("<f4").view(np.uint8)
+    """656-byte cache row(s) [..., 656] from the latent codes [..., 512], the bf16 rope values [..., 64]
+    and the scales [..., 4]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    row = np.zeros(codes.shape[:-1] + (ROW_BYTES,), dtype=np.uint8)
+    row[..., :DC] = codes
+    bits = np.ascontiguousarray(np.asarray(rope_bf16, dtype=np.float64).astype(np.float32)).view(np.uint32) >> 16
+    row[..., DC:DC + 2 * DR] = np.ascontiguousarray(bits.astype("<u2")).view(np.uint8)
+    row[..., DC + 2 * DR:] = np.ascontiguousarray(np.asarray(scales, dtype=np.float64).astype("<f4")).view(np.uint8)
     return row
 
 
@@ -131,24 +131,31 @@ def cache_write_fp8(cache, c_kv, k_pe, positions, slot_mapping, gamma, eps, thet
 
     Per token: c = RMSNorm(c_kv) * gamma and k = RoPE(k_pe, pos) in fp64 (mla_oracle.rms_norm,
     mla_oracle.rope), then c is quantised by groups and k rounded to bf16.  Negative slots are
-    skipped; untouched slots keep their bytes."""
+    skipped; untouched slots keep their bytes; a slot written twice keeps the later token.  Tokens
+    are independent, so their rows are computed many at a time."""
     out = np.array(cache, dtype=np.uint8, copy=True)
     n_blocks, block_size, _, width = out.shape
     if width != ROW_BYTES:
         raise ValueError("fp8 cache rows are 656 bytes")
-    c_kv = np.asarray(c_kv, dtype=np.float64)
-    k_pe = np.asarray(k_pe, dtype=np.float64)
-    for j in range(c_kv.shape[0]):
-        slot = int(slot_mapping[j])
-        if slot < 0:
-            continue
-        blk, off = divmod(slot, block_size)
-        if blk >= n_blocks:
-            raise IndexError("slot outside the cache pool")
-        c = O.rms_norm(c_kv[j], gamma, eps)
-        k = O.rope(k_pe[j], positions[j], theta)
-        codes, scales = quantize_latent(c)
-        out[blk, off, 0, :] = pack_row(codes, O.round_to_bf16(k), scales)
+    c_kv = np.asarray(c_kv, dtype=np.float64).reshape(-1, DC)
+    k_pe = np.asarray(k_pe, dtype=np.float64).reshape(-1, DR)
+    slots = np.asarray(slot_mapping, dtype=np.int64).reshape(-1)
+    keep = slots >= 0
+    if np.any(slots[keep] // block_size >= n_blocks):
+        raise IndexError("slot outside the cache pool")
+    if not np.any(keep):
+        return out
+    idx = np.nonzero(keep)[0]
+    # a slot written twice keeps the later token: store only each slot's last writer
+    _, last = np.unique(slots[idx][::-1], return_index=True)
+    idx = idx[len(idx) - 1 - last]
+    pos = np.asarray(positions).reshape(-1)
+    flat = out.reshape(-1, ROW_BYTES)
+    for lo in range(0, len(idx), 8192):  # rows in batches, to bound the temporaries
+        j = idx[lo:lo + 8192]
+        codes, scales = quantize_latent(O.rms_norm(c_kv[j], gamma, eps))
+        k = O.round_to_bf16(O.rope(k_pe[j], pos[j], theta))
+        flat[slots[j]] = pack_row(codes, k, scales)
     return out
 
 

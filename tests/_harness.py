@@ -96,10 +96,13 @@ def oracle_full(w):
     return cache, out
 
 
-def oracle_sequence(w, b, W_uk=None, W_uv=None, q=None):
+def oracle_sequence(w, b, W_uk=None, W_uv=None, q=None, fp8=False):
     """Oracle output rows of sequence b alone, computed on an identity-paged local pool
     (paging relabel invariance makes the physical placement irrelevant).  q: w.queries(), if the
-    caller already holds it."""
+    caller already holds it.  fp8: the cache holds the oracle's FP8 rows (oracle/mla_fp8.py) and the
+    decode reads their dequantised values; returns (rows, the local pool's bytes [nb, 16, 1, 656],
+    rows past the context 0xFF)."""
+    from oracle import mla_fp8 as F
     if W_uk is None:
         W_uk, W_uv = oracle_weights(w)
     if q is None:
@@ -107,16 +110,22 @@ def oracle_sequence(w, b, W_uk=None, W_uv=None, q=None):
     ctx = int(w.seq_lens[b])
     nb = (ctx + 15) // 16
     c, k = w.history(b)
-    pool = np.full((nb, 16, 1, 576), np.nan)
-    cache = O.cache_write(pool, c, k, np.arange(ctx), np.arange(ctx), w.gamma().astype(np.float64), w.eps,
-                          w.theta, w.storage)
-    return O.decode_absorbed(q[b * w.q_len:(b + 1) * w.q_len], cache, np.arange(nb)[None, :], np.array([ctx]),
+    gamma = w.gamma().astype(np.float64)
+    if fp8:
+        local = F.cache_write_fp8(np.full((nb, 16, 1, F.ROW_BYTES), 0xFF, np.uint8), c, k, np.arange(ctx),
+                                  np.arange(ctx), gamma, w.eps, w.theta)
+        cache = F.dequantize_cache(local)
+    else:
+        cache = O.cache_write(np.full((nb, 16, 1, 576), np.nan), c, k, np.arange(ctx), np.arange(ctx), gamma,
+                              w.eps, w.theta, w.storage)
+    rows = O.decode_absorbed(q[b * w.q_len:(b + 1) * w.q_len], cache, np.arange(nb)[None, :], np.array([ctx]),
                              w.q_len, W_uk, W_uv, w.scale, w.theta)
+    return (rows, local) if fp8 else rows
 
 
 def _oracle_rows_task(args):
     """Worker of oracle_all_sequences: the oracle rows of a list of sequences (one BLAS thread)."""
-    w, seqs = args
+    w, seqs, fp8 = args
     try:
         from threadpoolctl import threadpool_limits
         lim = threadpool_limits(1)
@@ -124,16 +133,18 @@ def _oracle_rows_task(args):
         lim = None
     W_uk, W_uv = oracle_weights(w)
     q = w.queries()
-    res = [(b, oracle_sequence(w, b, W_uk, W_uv, q)) for b in seqs]
+    res = [(b, oracle_sequence(w, b, W_uk, W_uv, q, fp8)) for b in seqs]
     if lim is not None:
         lim.unregister()
     return res
 
 
-def oracle_all_sequences(w, seqs=None, workers=None):
+def oracle_all_sequences(w, seqs=None, workers=None, fp8=False):
     """oracle_sequence for every sequence (or those in seqs), spread over worker processes started
     fresh (spawn: they import NumPy and the oracle only, never the GPU).  Returns [B*q_len, H, dv]
-    float64 rows; rows of sequences not asked for are NaN."""
+    float64 rows; rows of sequences not asked for are NaN.  fp8: returns (rows, the FP8 byte pool
+    [n_blocks, 16, 1, 656] with each sequence's oracle rows at its block table's blocks, every other
+    byte 0xFF)."""
     import concurrent.futures
     import multiprocessing
     import os
@@ -143,11 +154,15 @@ def oracle_all_sequences(w, seqs=None, workers=None):
     order = sorted(seqs, key=lambda b: -int(w.seq_lens[b]))
     parts = [order[i::n] for i in range(n)]
     out = np.full((w.n_q, w.num_heads, w.v_head_dim), np.nan)
+    pool = np.full((w.n_blocks, 16, 1, 656), 0xFF, np.uint8) if fp8 else None
     with concurrent.futures.ProcessPoolExecutor(n, mp_context=multiprocessing.get_context("spawn")) as ex:
-        for res in ex.map(_oracle_rows_task, [(w, p) for p in parts]):
-            for b, rows in res:
-                out[b * w.q_len:(b + 1) * w.q_len] = rows
-    return out
+        for res in ex.map(_oracle_rows_task, [(w, p, fp8) for p in parts]):
+            for b, r in res:
+                if fp8:
+                    r, local = r
+                    pool[w.block_table[b, :len(local)]] = local
+                out[b * w.q_len:(b + 1) * w.q_len] = r
+    return (out, pool) if fp8 else out
 
 
 def compare(out_gpu, ref, storage, label=""):

@@ -7,8 +7,9 @@ fp64 oracle (oracle/mla_fp8.py for the cache format, oracle/mla_oracle.py for at
   code may differ by one step where the oracle's quotient lies within 1e-9 (relative) of the tie
   between the two codes, a scale by one fp32 step where amax / 448 lies that close to an fp32
   midpoint, and a rope value by one bf16 ulp; anything else fails.
-* Decode: the kernel's output against the oracle's absorbed decode over the same bytes decoded by
-  the oracle's format decoder, to the bf16 tolerance (max abs 2e-2, relative L2 5e-3)."""
+* Decode: the oracle's bytes are copied into the GPU's pool, and the kernel's output over them is
+  compared with the oracle's absorbed decode over the same bytes decoded by the oracle's format
+  decoder, to the bf16 tolerance (max abs 2e-2, relative L2 5e-3)."""
 
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ from oracle import mla_fp8 as F
 from oracle import mla_oracle as O
 from workloads import mla_inputs as W
 
-from ._harness import bf16_ulp_distance, compare, dev, dev_i32, oracle_weights
+from ._harness import bf16_ulp_distance, compare, dev, dev_i32, oracle_all_sequences, oracle_weights
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -38,7 +39,7 @@ def _say(*a):
 class Fp8Run:
     """Context in FP8-cache mode, a zeroed byte pool, every context token written by the kernel."""
 
-    def __init__(self, w):
+    def __init__(self, w, fill=0):
         from mla_latent_kv_paged_amd import MLAContext
         self.w = w
         self.max_ctx = int(w.seq_lens.max())
@@ -46,7 +47,7 @@ class Fp8Run:
                               num_heads=w.num_heads, dtype="fp8", rms_eps=w.eps, rope_theta=w.theta,
                               max_q_tokens=w.n_q, max_batch=w.batch, max_position=self.max_ctx + 16,
                               max_seq_len=self.max_ctx + 16)
-        self.pool = torch.zeros((w.n_blocks, 16, 1, F.ROW_BYTES), dtype=torch.uint8, device="cuda")
+        self.pool = torch.full((w.n_blocks, 16, 1, F.ROW_BYTES), fill, dtype=torch.uint8, device="cuda")
         self.tok = w.all_tokens()
         t = self.tok
         self.ctx.cache_write(dev(t["c_kv"], "bf16"), dev(t["k_pe"], "bf16"), dev_i32(t["positions"]),
@@ -66,6 +67,11 @@ class Fp8Run:
 
     def pool_bytes(self):
         return self.pool.cpu().numpy()
+
+    def load_pool(self, pool8):
+        """Replace the pool's bytes by the given ones (the oracle's)."""
+        self.pool.copy_(torch.from_numpy(np.ascontiguousarray(pool8)))
+        torch.cuda.synchronize()
 
     def free(self):
         self.ctx.free()
@@ -134,10 +140,10 @@ def test_fp8_cache_and_decode(name, make):
     ref_pool = _oracle_cache(w)
     run = Fp8Run(w)
     try:
-        got_pool = run.pool_bytes()
-        _check_fp8_cache(got_pool, ref_pool, w)
+        _check_fp8_cache(run.pool_bytes(), ref_pool, w)
+        run.load_pool(ref_pool)
         W_uk, W_uv = oracle_weights(w)
-        deq = F.dequantize_cache(got_pool)
+        deq = F.dequantize_cache(ref_pool)
         ref = O.decode_absorbed(w.queries(), deq, w.block_table, w.seq_lens, w.q_len, W_uk, W_uv, w.scale, w.theta)
         out = run.decode()
         compare(out, ref, "bf16", f"fp8 {name}")
@@ -215,28 +221,21 @@ def test_fp8_score_climb(heads, q_len):
 
 def test_fp8_full_size_every_sequence():
     """The benchmark's FP8 configuration and launch (lite_b64: 64 sequences x 4,097 tokens, 16 heads,
-    FP8 rows, the library's own split): every sequence against the oracle's absorbed decode over the
-    bytes the kernel wrote, dequantised by the oracle's format decoder, on an identity-paged local pool
-    of each sequence's blocks."""
+    FP8 rows, the library's own split).  The kernel's cache write of every token against the oracle's
+    bytes; then, over the oracle's bytes, every sequence against the oracle's absorbed decode (each
+    computed on an identity-paged local pool of that sequence's blocks)."""
     w = W.lite_b64()
     _say("fp8 full size: lite_b64, every sequence")
-    run = Fp8Run(w)
+    ref, ref_pool = oracle_all_sequences(w, fp8=True)
+    run = Fp8Run(w, fill=0xFF)
     try:
-        out = run.decode()
-        got = run.pool_bytes()
-        res = out.to(torch.float32).cpu().numpy().astype(np.float64)
+        _check_fp8_cache(run.pool_bytes(), ref_pool, w)
+        run.load_pool(ref_pool)
+        res = run.decode().to(torch.float32).cpu().numpy().astype(np.float64)
     finally:
         run.free()
-    W_uk, W_uv = oracle_weights(w)
-    q = w.queries()
-    ref = np.empty_like(res)
     for b in range(w.batch):
-        ctx = int(w.seq_lens[b])
-        nb = (ctx + 15) // 16
-        deq = F.dequantize_cache(got[w.block_table[b, :nb]])
         rows = slice(b * w.q_len, (b + 1) * w.q_len)
-        ref[rows] = O.decode_absorbed(q[rows], deq, np.arange(nb)[None, :], np.array([ctx]), w.q_len, W_uk, W_uv,
-                                      w.scale, w.theta)
         compare(res[rows], ref[rows], "bf16", f"fp8 full size, sequence {b}")
     max_abs, rel = compare(res, ref, "bf16", "fp8 full size, whole output")
     _say(f"fp8 full size: max abs {max_abs:.3e}, rel L2 {rel:.3e}")

@@ -59,15 +59,20 @@ class LayerRun:
         self.ctx.layer_weights(dev(lw["q_proj"], "bf16"), dev(lw["kv_a_proj"], "bf16"), dev(lw["o_proj"], "bf16"),
                                dev(lw["input_norm_gamma"], "bf16"), input_norm=input_norm, residual=residual)
         if cache == "fp8":
-            self.pool = torch.full((w.n_blocks, 16, 1, 656), 255, dtype=torch.uint8, device="cuda")
+            # the oracle's FP8 rows of the history (every other byte 0xFF)
+            hist = w.all_tokens(history_only=True)
+            self.pool8 = F.cache_write_fp8(np.full((w.n_blocks, 16, 1, 656), 0xFF, np.uint8), hist["c_kv"],
+                                           hist["k_pe"], hist["positions"], hist["slot_mapping"],
+                                           np.asarray(lw["kv_norm_gamma"], np.float64), w.eps, w.theta)
+            self.pool = torch.from_numpy(self.pool8).to("cuda")
         else:
             self.pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
-        for b in range(w.batch):
-            c, k = w.history(b)
-            hist = int(w.seq_lens[b]) - w.q_len
-            if hist > 0:
-                self.ctx.cache_write(dev(c[:hist], "bf16"), dev(k[:hist], "bf16"), dev_i32(np.arange(hist)),
-                                     dev_i32(w.slots(b, 0, hist)), self.pool)
+            for b in range(w.batch):
+                c, k = w.history(b)
+                hist = int(w.seq_lens[b]) - w.q_len
+                if hist > 0:
+                    self.ctx.cache_write(dev(c[:hist], "bf16"), dev(k[:hist], "bf16"), dev_i32(np.arange(hist)),
+                                         dev_i32(w.slots(b, 0, hist)), self.pool)
         new = w.all_tokens(new_only=True)
         self.pos, self.slots = new["positions"], new["slot_mapping"]
         self.bt, self.sl = dev_i32(w.block_table), dev_i32(w.seq_lens)
@@ -194,6 +199,10 @@ def test_layer_two_steps_in_a_row():
 
 
 def test_layer_step_fp8_cache():
+    """One layer step over an FP8 cache whose history rows are the oracle's bytes.  The oracle writes
+    the new tokens' rows from its own fp64 projection and decodes over the dequantised bytes; the
+    GPU's new rows come from its own projection, so a code may sit one e4m3 step away (one row of
+    each context).  The new rows the GPU wrote are checked against the oracle's to the e4m3 spacing."""
     w = W.custom("layer_fp8", "bf16", 16, [400, 90, 1200], q_len=1, seed=403)
     _say("layer step, fp8 cache")
     lw = w.layer_weights(0)
@@ -201,24 +210,26 @@ def test_layer_step_fp8_cache():
     run = LayerRun(w, lw, cache="fp8")
     try:
         got = run.step(hidden)
-        pool8 = run.pool.cpu().numpy()
+        got8 = run.pool.cpu().numpy()
     finally:
         run.free()
-    deq = F.dequantize_cache(pool8)
-    # decode-only against the bytes the GPU holds (history and new rows), and the new rows' latent
-    # codes against the oracle's FP8 write of the oracle's projection
     x = O.rms_norm(hidden.astype(np.float64), lw["input_norm_gamma"], w.eps)
     q = (x @ lw["q_proj"].astype(np.float64).T).reshape(w.n_q, 16, 192)
+    kv = x @ lw["kv_a_proj"].astype(np.float64).T
+    pool8 = F.cache_write_fp8(run.pool8, kv[:, :512], kv[:, 512:], run.pos, run.slots,
+                              np.asarray(lw["kv_norm_gamma"], np.float64), w.eps, w.theta)
+    want = F.dequantize_cache(pool8)
     W_uk, W_uv = O.absorb(lw["kv_b_proj"].astype(np.float64), 16, 128, 128)
-    a = O.decode_absorbed(q, deq, w.block_table, w.seq_lens, 1, W_uk, W_uv, w.scale, w.theta)
+    a = O.decode_absorbed(q, want, w.block_table, w.seq_lens, 1, W_uk, W_uv, w.scale, w.theta)
     ref = a.reshape(w.n_q, -1) @ lw["o_proj"].astype(np.float64).T + hidden
     _compare_out(got, ref, True, "fp8 layer step")
-    kv = x @ lw["kv_a_proj"].astype(np.float64).T
-    want = F.dequantize_cache(F.cache_write_fp8(np.zeros((w.n_blocks, 16, 1, 656), np.uint8), kv[:, :512], kv[:, 512:],
-                                                run.pos, run.slots, np.ones(512), w.eps, w.theta))
+    deq = F.dequantize_cache(got8)
     for s in run.slots:
         g, r = deq[s // 16, s % 16, 0], want[s // 16, s % 16, 0]
         assert np.linalg.norm(g - r) / np.linalg.norm(r) < 2 ** -4
+    hist = np.ones(got8.shape[:2], bool)
+    hist[run.slots // 16, run.slots % 16] = False
+    assert np.array_equal(got8[hist], run.pool8[hist]), "the step changed bytes outside its new rows"
 
 
 @pytest.mark.parametrize("seq_len", [1, 256, 1024])

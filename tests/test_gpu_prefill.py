@@ -1,5 +1,6 @@
 """GPU parity of the chunked prefill (mla_prefill) through the C ABI against the fp64 oracle's
-prefill_naive (oracle/mla_oracle.py), to the bf16 tolerance (max abs 2e-2, relative L2 5e-3).
+prefill_naive (oracle/mla_oracle.py), to the bf16 tolerance (max abs 2e-2, relative L2 5e-3), over
+bf16 rows and over FP8 rows (the oracle's bytes, dequantised by oracle/mla_fp8.py for the oracle).
 
 Each case writes every context token with mla_cache_write (the chunk's tokens included, as a serving
 engine does before attention), then runs one prefill whose chunk of sequence b is its last n_b
@@ -10,6 +11,7 @@ Unused pool slots are NaN, so a read of a token the kernels should not see poiso
 import numpy as np
 import pytest
 
+from oracle import mla_fp8 as F
 from oracle import mla_oracle as O
 from workloads import mla_inputs as W
 
@@ -111,9 +113,83 @@ def test_prefill_one_token_chunks_match_decode():
         run.free()
 
 
+class Fp8Prefill:
+    """An FP8-cache context whose pool holds the oracle's FP8 rows of every token (other bytes 0xFF:
+    NaN codes, rope values and scales), and the oracle's dequantised values of the same bytes."""
+
+    def __init__(self, w):
+        from mla_latent_kv_paged_amd import MLAContext
+        self.w = w
+        self.max_ctx = int(w.seq_lens.max())
+        self.ctx = MLAContext(dev(w.kv_b_proj(), "bf16"), dev(w.gamma(), "bf16") if w.gamma_noise else None,
+                              num_heads=w.num_heads, dtype="fp8", rms_eps=w.eps, rope_theta=w.theta,
+                              max_q_tokens=w.n_q, max_batch=w.batch, max_position=self.max_ctx + 16,
+                              max_seq_len=self.max_ctx + 16)
+        tok = w.all_tokens()
+        pool8 = F.cache_write_fp8(np.full((w.n_blocks, 16, 1, F.ROW_BYTES), 0xFF, np.uint8), tok["c_kv"],
+                                  tok["k_pe"], tok["positions"], tok["slot_mapping"], w.gamma().astype(np.float64),
+                                  w.eps, w.theta)
+        self.deq = F.dequantize_cache(pool8)
+        self.pool = torch.from_numpy(pool8).to("cuda")
+        self.bt, self.sl = dev_i32(w.block_table), dev_i32(w.seq_lens)
+
+    def oracle(self, chunks):
+        W_uk, W_uv = oracle_weights(self.w)
+        return O.prefill_naive(self.w.chunk_queries(chunks), _cu(chunks), self.deq, self.w.block_table,
+                               self.w.seq_lens, W_uk, W_uv, self.w.scale, self.w.theta)
+
+    def free(self):
+        self.ctx.free()
+
+
+FP8_PREFILL_CASES = [
+    ("mixed_h16", 16, [300, 77, 129], [64, 77, 1], 0.0),
+    ("ragged_h16", 16, [513, 1000, 40], [257, 333, 0], 0.0),
+    ("h128", 128, [150, 90], [100, 90], 0.0),
+    ("fresh_2048_gamma", 16, [2048], [2048], 0.1),
+]
+
+
+@pytest.mark.parametrize("name,heads,ctxs,chunks,gamma_noise", FP8_PREFILL_CASES,
+                         ids=[c[0] for c in FP8_PREFILL_CASES])
+def test_prefill_fp8_cache(name, heads, ctxs, chunks, gamma_noise):
+    """Chunked prefill over FP8 rows (the expansion reads codes x group scales) against the oracle's
+    prefill_naive over the same bytes dequantised by the oracle's format decoder."""
+    w = W.custom("pf8_" + name, "bf16", heads, ctxs, q_len=1, seed=190 + heads, gamma_noise=gamma_noise)
+    _say("fp8 prefill", name, "H", heads, "ctx", ctxs, "chunks", chunks)
+    run = Fp8Prefill(w)
+    try:
+        ref = run.oracle(chunks)
+        q = dev(w.chunk_queries(chunks), "bf16")
+        out = run.ctx.prefill(q, dev_i32(_cu(chunks)), run.pool, run.bt, run.sl, run.max_ctx, max(max(chunks), 1))
+        torch.cuda.synchronize()
+        compare(out, ref, "bf16", f"fp8 prefill {name}")
+    finally:
+        run.free()
+
+
+def test_prefill_fp8_one_token_chunks_match_decode():
+    """One-token chunks over FP8 rows: the prefill (expanded K/V) and mla_decode (absorbed, FP8 rows
+    read in the decode kernel) against the oracle and against each other."""
+    w = W.custom("pf8_dec", "bf16", 16, [700, 33, 258], q_len=1, seed=196)
+    _say("fp8 prefill one-token chunks vs decode")
+    run = Fp8Prefill(w)
+    try:
+        ref = run.oracle([1, 1, 1])
+        q = dev(w.chunk_queries([1, 1, 1]), "bf16")
+        pf = run.ctx.prefill(q, dev_i32(_cu([1, 1, 1])), run.pool, run.bt, run.sl, run.max_ctx, 1)
+        dc = run.ctx.decode(q, run.pool, run.bt, run.sl, run.max_ctx, q_len=1)
+        torch.cuda.synchronize()
+        compare(pf, ref, "bf16", "fp8 prefill one-token chunks")
+        compare(dc, ref, "bf16", "fp8 decode")
+        assert (pf.float() - dc.float()).abs().max().item() <= 4e-2
+    finally:
+        run.free()
+
+
 def test_prefill_status_codes():
     """Host-side validation through the C ABI: a workspace one byte short, a chunk bound above the
-    context bound, and an FP8-cache context (unsupported) are refused before any launch."""
+    context bound, and an fp32 context (unsupported) are refused before any launch."""
     from mla_latent_kv_paged_amd import MLAError, MLAContext
     w = W.custom("pf_err", "bf16", 16, [40], q_len=1, seed=97)
     run = GpuRun(w)
@@ -128,14 +204,15 @@ def test_prefill_status_codes():
             run.ctx.prefill(q, dev_i32(cu), run.pool, run.bt, run.sl, 4, 8)
     finally:
         run.free()
-    ctx8 = MLAContext(dev(w.kv_b_proj(), "bf16"), None, num_heads=16, dtype="fp8", max_q_tokens=8, max_batch=1,
-                      max_position=64, max_seq_len=64)
+    ctx32 = MLAContext(dev(w.kv_b_proj(), "f32"), None, num_heads=16, dtype="f32", max_q_tokens=8, max_batch=1,
+                       max_position=64, max_seq_len=64)
     try:
-        pool8 = torch.zeros((w.n_blocks, 16, 1, 656), dtype=torch.uint8, device="cuda")
+        pool32 = torch.zeros((w.n_blocks, 16, 1, 576), dtype=torch.float32, device="cuda")
+        q32 = dev(w.chunk_queries([8]), "f32")
         with pytest.raises(MLAError):
-            ctx8.prefill(q, dev_i32(cu), pool8, dev_i32(w.block_table), dev_i32(w.seq_lens), 48, 8)
+            ctx32.prefill(q32, dev_i32(cu), pool32, dev_i32(w.block_table), dev_i32(w.seq_lens), 48, 8)
     finally:
-        ctx8.free()
+        ctx32.free()
 
 
 def test_prefill_full_size_sampled():

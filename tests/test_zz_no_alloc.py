@@ -50,7 +50,7 @@ CASES = [  # (label, storage, heads, q_len, first seq_lens, second (smaller) seq
 def test_noalloc_matches_decode(label, storage, heads, q_len, first, second):
     w = W.custom(f"na_{label}", storage, heads, first, q_len=q_len, seed=301)
     _say("noalloc", label, "first", first, "second", second)
-    _, ref_oracle = oracle_full(w)
+    cache_oracle, ref_oracle = oracle_full(w)
     run = GpuRun(w)
     try:
         a, b = _both(run, w, run.q, run.bt, run.sl, run.max_ctx)
@@ -64,11 +64,10 @@ def test_noalloc_matches_decode(label, storage, heads, q_len, first, second):
         bt2 = run.bt[:nb].contiguous()
         a2, b2 = _both(run, w, q2, bt2, sl2, mx2)
         assert torch.equal(a2, b2), f"{label}: second call differs from mla_decode"
-        # oracle for the second call: the same cache, shorter contexts (the last q_len tokens of each
-        # shortened context are the queries' positions)
-        pool64 = run.pool_f64()
+        # oracle for the second call: the oracle's cache, shorter contexts (the last q_len tokens of
+        # each shortened context are the queries' positions)
         W_uk, W_uv = oracle_weights(w)
-        ref2 = O.decode_absorbed(w.queries()[:nb * q_len], pool64, w.block_table[:nb],
+        ref2 = O.decode_absorbed(w.queries()[:nb * q_len], cache_oracle, w.block_table[:nb],
                                  np.minimum(w.seq_lens[:nb], second), q_len, W_uk, W_uv, w.scale, w.theta)
         compare(b2, ref2, storage, f"{label} second call vs oracle")
     finally:
@@ -84,10 +83,13 @@ def test_noalloc_fp8_matches_decode():
                      rope_theta=w.theta, max_q_tokens=w.n_q, max_batch=w.batch, max_position=mx + 16,
                      max_seq_len=mx + 16)
     try:
-        pool = torch.full((w.n_blocks, 16, 1, 656), 255, dtype=torch.uint8, device="cuda")
+        # the oracle's FP8 rows (every other byte 0xFF: NaN codes, rope values and scales)
         tok = w.all_tokens()
-        ctx.cache_write(dev(tok["c_kv"], "bf16"), dev(tok["k_pe"], "bf16"), dev_i32(tok["positions"]),
-                        dev_i32(tok["slot_mapping"]), pool)
+        pool8 = F.cache_write_fp8(np.full((w.n_blocks, 16, 1, 656), 0xFF, np.uint8), tok["c_kv"], tok["k_pe"],
+                                  tok["positions"], tok["slot_mapping"], w.gamma().astype(np.float64), w.eps,
+                                  w.theta)
+        deq = F.dequantize_cache(pool8)
+        pool = torch.from_numpy(pool8).to("cuda")
         q, bt, sl = dev(w.queries(), "bf16"), dev_i32(w.block_table), dev_i32(w.seq_lens)
         for nb, mxx in ((4, mx), (2, 700)):
             sl_n = dev_i32(np.minimum(w.seq_lens[:nb], mxx))
@@ -96,7 +98,6 @@ def test_noalloc_fp8_matches_decode():
             ctx.decode_noalloc(q[:nb].contiguous(), pool, bt[:nb].contiguous(), sl_n, mxx, b)
             torch.cuda.synchronize()
             assert torch.equal(a, b), f"fp8: batch {nb} differs from mla_decode"
-            deq = F.dequantize_cache(pool.cpu().numpy())
             W_uk, W_uv = oracle_weights(w)
             ref = O.decode_absorbed(w.queries()[:nb], deq, w.block_table[:nb], np.minimum(w.seq_lens[:nb], mxx), 1,
                                     W_uk, W_uv, w.scale, w.theta)
