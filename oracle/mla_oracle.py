@@ -185,17 +185,21 @@ def cache_write(cache, c_kv, k_pe, positions, slot_mapping, gamma, eps, theta, s
     if width != dc + k_pe.shape[1]:
         raise ValueError("cache row width must be kv_lora_rank + qk_rope_head_dim")
     rnd = round_to_bf16 if storage == "bf16" else round_to_f32
-    # every token's row at once: RMSNorm and RoPE act on each row on its own
-    rows = np.concatenate([rnd(rms_norm(c_kv, gamma, eps)),
-                           rnd(rope(k_pe, np.asarray(positions), theta))], axis=1)
-    for j in range(c_kv.shape[0]):
-        slot = int(slot_mapping[j])
-        if slot < 0:
-            continue
-        blk, off = divmod(slot, block_size)
-        if blk >= n_blocks:
-            raise IndexError("slot outside the cache pool")
-        out[blk, off, 0, :] = rows[j]
+    slots = np.asarray(slot_mapping, dtype=np.int64).reshape(-1)
+    idx = np.nonzero(slots >= 0)[0]
+    if np.any(slots[idx] // block_size >= n_blocks):
+        raise IndexError("slot outside the cache pool")
+    # a slot written twice keeps the later token: store only each slot's last writer
+    _, last = np.unique(slots[idx][::-1], return_index=True)
+    idx = idx[len(idx) - 1 - last]
+    positions = np.asarray(positions).reshape(-1)
+    flat = out.reshape(-1, width)
+    # RMSNorm and RoPE act on each row on its own: many rows at a time, in batches that bound the
+    # temporaries
+    for lo in range(0, len(idx), 8192):
+        j = idx[lo:lo + 8192]
+        flat[slots[j]] = np.concatenate([rnd(rms_norm(c_kv[j], gamma, eps)), rnd(rope(k_pe[j], positions[j], theta))],
+                                        axis=1)
     return out
 
 

@@ -45,9 +45,11 @@ def _weights(w, lw):
 
 
 class LayerRun:
-    """A layer attached to a context on the GPU, the history of every sequence written by mla_cache_write."""
+    """A layer attached to a context on the GPU; its pool holds the oracle's history rows of every sequence
+    (bf16 rows, or FP8 bytes), every other slot NaN (0xFF bytes).  history: the oracle's bf16 history cache,
+    if the caller already holds it."""
 
-    def __init__(self, w, lw, input_norm=True, residual=True, cache="bf16", extra_ctx=0):
+    def __init__(self, w, lw, input_norm=True, residual=True, cache="bf16", extra_ctx=0, history=None):
         from mla_latent_kv_paged_amd import MLAContext
         self.w = w
         mx = int(w.seq_lens.max()) + extra_ctx
@@ -66,13 +68,8 @@ class LayerRun:
                                            np.asarray(lw["kv_norm_gamma"], np.float64), w.eps, w.theta)
             self.pool = torch.from_numpy(self.pool8).to("cuda")
         else:
-            self.pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
-            for b in range(w.batch):
-                c, k = w.history(b)
-                hist = int(w.seq_lens[b]) - w.q_len
-                if hist > 0:
-                    self.ctx.cache_write(dev(c[:hist], "bf16"), dev(k[:hist], "bf16"), dev_i32(np.arange(hist)),
-                                         dev_i32(w.slots(b, 0, hist)), self.pool)
+            self.hist = _oracle_history(w, lw) if history is None else history
+            self.pool = dev(self.hist, "bf16")  # the oracle rounded every row to bf16: exact
         new = w.all_tokens(new_only=True)
         self.pos, self.slots = new["positions"], new["slot_mapping"]
         self.bt, self.sl = dev_i32(w.block_table), dev_i32(w.seq_lens)
@@ -155,7 +152,7 @@ def test_layer_step_small(label, heads, q_len, seqs, input_norm, residual, noise
         pool = run.pool.to(torch.float32).cpu().numpy().astype(np.float64)
     finally:
         run.free()
-    ref, cache = L.layer_decode_step(hidden, run.pos, run.slots, _oracle_history(w, lw), w.block_table, w.seq_lens,
+    ref, cache = L.layer_decode_step(hidden, run.pos, run.slots, run.hist, w.block_table, w.seq_lens,
                                      q_len, _weights(w, lw), input_norm=input_norm, residual=residual)
     max_abs, rel = _compare_out(got, ref, residual, label)
     _say(label, f"max abs {max_abs:.3e}, rel L2 {rel:.3e}")
@@ -190,7 +187,7 @@ def test_layer_two_steps_in_a_row():
         pool = run.pool.to(torch.float32).cpu().numpy().astype(np.float64)
     finally:
         run.free()
-    cache = _oracle_history(w, lw)
+    cache = run.hist
     ref1, cache = L.layer_decode_step(h1, run.pos, run.slots, cache, w.block_table, w.seq_lens, 1, wts)
     ref2, cache = L.layer_decode_step(h2, pos2, slots2, cache, bt2, sl2, 1, wts)
     _compare_out(got1, ref1, True, "step 1")
@@ -245,7 +242,7 @@ def test_layer_step_batch1(seq_len):
         pool = run.pool.to(torch.float32).cpu().numpy().astype(np.float64)
     finally:
         run.free()
-    ref, cache = L.layer_decode_step(hidden, run.pos, run.slots, _oracle_history(w, lw), w.block_table, w.seq_lens, 1,
+    ref, cache = L.layer_decode_step(hidden, run.pos, run.slots, run.hist, w.block_table, w.seq_lens, 1,
                                      _weights(w, lw), residual=False)
     compare(got, ref, "bf16", f"batch 1 seq {seq_len}")
     _check_rows(pool, cache, run.slots, f"batch 1 seq {seq_len}")
@@ -254,8 +251,7 @@ def test_layer_step_batch1(seq_len):
 def test_layer_step_b64_s4096_every_sequence():
     """Batch 64 x 4,096 cached tokens (16 heads, D = 2,048), input RMSNorm without the residual (so that the
     comparison rests on the attention and its projections): every sequence against the oracle's layer step
-    on that sequence's blocks of the GPU's history cache (the history rows are mla_cache_write's, checked
-    elsewhere; this isolates the step)."""
+    on that sequence's blocks of the oracle's history cache (the GPU's pool holds the same rows)."""
     w = W.lite_b64()
     _say("layer step lite_b64, every sequence")
     lw = w.layer_weights(0)
@@ -263,14 +259,13 @@ def test_layer_step_b64_s4096_every_sequence():
     hidden = w.hidden()
     run = LayerRun(w, lw, residual=False)
     try:
-        hist_pool = run.pool.clone()
         got = run.step(hidden)
-        # each sequence's blocks, before and after the step
+        # each sequence's blocks: the oracle's history, and the GPU's pool after the step
         locs, news = [], []
         for b in range(w.batch):
             nb = (int(w.seq_lens[b]) + 15) // 16
+            locs.append(run.hist[w.block_table[b, :nb]])
             ids = torch.from_numpy(w.block_table[b, :nb].astype(np.int64)).cuda()
-            locs.append(hist_pool[ids].to(torch.float32).cpu().numpy().astype(np.float64))
             news.append(run.pool[ids].to(torch.float32).cpu().numpy().astype(np.float64))
     finally:
         run.free()
@@ -323,36 +318,15 @@ def test_layer_status_codes():
 def test_model_step_27_layers_every_layer():
     """A decode step through 27 attention layers (one context, set of weights and cache per layer, layer l's
     output the input of layer l + 1), as bench.py --mode layer --layers 27 runs it, at 16 heads, three
-    sequences.  Every layer's output and new cache rows against the oracle's layer step on the GPU's own
-    input to that layer (the bf16 rounding of each layer's output is then not carried into the next
-    comparison); the end-to-end result against the oracle's 27-layer model step within the bound those
-    roundings allow."""
+    sequences.  End to end: the GPU's chained result against the oracle's 27-layer model step, within the
+    bound the per-layer roundings allow.  Per layer: the oracle runs its own chain, rounding each layer's
+    input to bf16 (the GPU's hidden states are bf16); each GPU layer is then stepped again on the oracle's
+    rounded input to that layer, and its output and new cache rows are compared with the oracle's layer
+    step on the same input."""
     L_ = 27
     w = W.custom("model27", "bf16", 16, [130, 37, 300], q_len=1, seed=405)
     _say("27-layer model step")
-    runs, lws = [], []
-    try:
-        for li in range(L_):
-            lw = w.layer_weights(li)
-            run = LayerRun(w, lw)
-            if li:  # layers other than 0 draw their own history
-                for b in range(w.batch):
-                    c, k = w.history(b, li)
-                    hist = int(w.seq_lens[b]) - 1
-                    run.ctx.cache_write(dev(c[:hist], "bf16"), dev(k[:hist], "bf16"), dev_i32(np.arange(hist)),
-                                        dev_i32(w.slots(b, 0, hist)), run.pool)
-            runs.append(run)
-            lws.append(lw)
-        h = w.hidden()
-        ins, outs, pools = [], [], []
-        for run in runs:
-            ins.append(h)
-            h = run.step(h)
-            outs.append(h)
-            pools.append(run.pool.to(torch.float32).cpu().numpy().astype(np.float64))
-    finally:
-        for run in runs:
-            run.free()
+    lws = [w.layer_weights(li) for li in range(L_)]
     new = w.all_tokens(new_only=True)
     caches0 = []
     for li in range(L_):
@@ -362,24 +336,45 @@ def test_model_step_27_layers_every_layer():
             n = int(w.seq_lens[b]) - 1
             hist["c_kv"].append(c[:n]); hist["k_pe"].append(k[:n])
             hist["positions"].append(np.arange(n)); hist["slot_mapping"].append(w.slots(b, 0, n))
-        cache = O.cache_write(np.full((w.n_blocks, 16, 1, 576), np.nan), np.concatenate(hist["c_kv"]),
-                              np.concatenate(hist["k_pe"]), np.concatenate(hist["positions"]),
-                              np.concatenate(hist["slot_mapping"]), lws[li]["kv_norm_gamma"].astype(np.float64), w.eps,
-                              w.theta, "bf16")
-        caches0.append(cache)
-        ref, cache_after = L.layer_decode_step(ins[li], new["positions"], new["slot_mapping"], cache, w.block_table,
-                                               w.seq_lens, 1, _weights(w, lws[li]))
-        _compare_out(outs[li], ref, True, f"layer {li}")
-        _check_rows(pools[li], cache_after, new["slot_mapping"], f"layer {li}")
+        caches0.append(O.cache_write(np.full((w.n_blocks, 16, 1, 576), np.nan), np.concatenate(hist["c_kv"]),
+                                     np.concatenate(hist["k_pe"]), np.concatenate(hist["positions"]),
+                                     np.concatenate(hist["slot_mapping"]),
+                                     lws[li]["kv_norm_gamma"].astype(np.float64), w.eps, w.theta, "bf16"))
+    # the oracle's chain with bf16 inputs: the per-layer cases
+    ins_o, refs, caches1 = [], [], []
+    h = w.hidden().astype(np.float64)
+    for li in range(L_):
+        ins_o.append(O.round_to_bf16(h))
+        h, cache_after = L.layer_decode_step(ins_o[li], new["positions"], new["slot_mapping"], caches0[li],
+                                             w.block_table, w.seq_lens, 1, _weights(w, lws[li]))
+        refs.append(h)
+        caches1.append(cache_after)
+    runs = []
+    try:
+        for li in range(L_):  # every layer its own history (the oracle's rows)
+            runs.append(LayerRun(w, lws[li], history=caches0[li]))
+        h = w.hidden()
+        for run in runs:  # the chained step
+            h = run.step(h)
+        out_chain = h
+        outs, pools = [], []
+        for li, run in enumerate(runs):  # each layer again on the oracle's input (its new rows rewritten)
+            outs.append(run.step(ins_o[li]))
+            pools.append(run.pool.to(torch.float32).cpu().numpy().astype(np.float64))
+    finally:
+        for run in runs:
+            run.free()
+    for li in range(L_):
+        _compare_out(outs[li], refs[li], True, f"layer {li}")
+        _check_rows(pools[li], caches1[li], new["slot_mapping"], f"layer {li}")
     # end to end: the oracle's model step keeps the residual stream in fp64, the GPU stores it in bf16 after
-    # every layer.  The per-layer checks above are the parity; end to end, each layer's error carries into the
-    # next through the residual, so elementwise the errors add up to at most L times one layer's bound, and in
-    # relative L2 the output roundings (at most 2^-9 of a value each, independent) grow like a random walk,
-    # sqrt(L) 2^-9 on top of the single-step bound
+    # every layer.  Each layer's error carries into the next through the residual, so elementwise the errors
+    # add up to at most L times one layer's bound, and in relative L2 the output roundings (at most 2^-9 of a
+    # value each, independent) grow like a random walk, sqrt(L) 2^-9 on top of the single-step bound
     ref27, _ = L.model_decode_step(w.hidden(), new["positions"], new["slot_mapping"], caches0, w.block_table,
                                    w.seq_lens, 1, [_weights(w, lw) for lw in lws])
-    err = np.abs(outs[-1] - ref27)
-    rel = float(np.linalg.norm(outs[-1] - ref27) / np.linalg.norm(ref27))
+    err = np.abs(out_chain - ref27)
+    rel = float(np.linalg.norm(out_chain - ref27) / np.linalg.norm(ref27))
     _say(f"27 layers end to end: max abs {err.max():.3e}, rel L2 {rel:.3e}")
     assert np.all(err <= L_ * (2e-2 + 0.5 * _spacing(ref27)))
     assert rel <= 5e-3 + np.sqrt(L_) * 2.0 ** -9
