@@ -62,6 +62,8 @@ def parse():
                     help="step as mla_cache_write + mla_decode (two calls) instead of mla_decode_step, which "
                          "runs the cache write in the query absorption's launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unflushed", action="store_true",
+                    help="also time steps that all read the same pool (pass D: the pool may sit in the Infinity Cache)")
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences in the oracle's timed sample (capped at "
                     "the batch)")
     ap.add_argument("--pf-batch", type=int, default=4, help="prefill mode: sequences")
@@ -636,15 +638,18 @@ def main():
         ev[i][1].record()
     torch.cuda.synchronize()
     step_samples = np.array([a_.elapsed_time(b_) for a_, b_ in ev]) * 1e3
-    # pass D: un-flushed, every step on the same pool (the previous step's cache may still sit in
-    # the 256 MB Infinity Cache)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(args.steps):
-        step(i, pools[0])
-    e1.record()
-    torch.cuda.synchronize()
-    unflushed_us = e0.elapsed_time(e1) / args.steps * 1e3
+    # pass D (--unflushed only): every step on the same pool, so the previous step's cache may still sit
+    # in the 256 MB Infinity Cache.  Off by default, so that every decode launch of a default run (and of
+    # its profiler trace) reads a pool the previous steps did not
+    unflushed_us = None
+    if args.unflushed:
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            step(i, pools[0])
+        e1.record()
+        torch.cuda.synchronize()
+        unflushed_us = e0.elapsed_time(e1) / args.steps * 1e3
 
     def pct(x):
         return {"p10": round(float(np.percentile(x, 10)), 2), "median": round(float(np.median(x)), 2),
@@ -686,7 +691,7 @@ def main():
         "decode_us": round(decode_us, 2),
         "decode_us_dist": pct(dec_samples),
         "step_us_dist": pct(step_samples),
-        "unflushed_us_per_step": round(unflushed_us, 2),
+        "unflushed_us_per_step": None if unflushed_us is None else round(unflushed_us, 2),
         "decode_latent_gbps": round(achieved, 1),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "step_calls": "mla_cache_write + mla_decode" if args.separate_write else "mla_decode_step",

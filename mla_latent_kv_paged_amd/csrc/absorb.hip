@@ -37,9 +37,9 @@ hipError_t launch_absorb(bool bf16, const AbsorbArgs& a, hipStream_t s) {
   const int64_t total = int64_t(a.H) * (DN + DV) * DC;
   const int grid = int((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   if (bf16)
-    absorb_kernel<uint16_t><<<grid, 256, 0, s>>>(a);
+    launch(absorb_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, a);
   else
-    absorb_kernel<float><<<grid, 256, 0, s>>>(a);
+    launch(absorb_kernel<float>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(CacheWriteArgs a) 
 
 hipError_t launch_cache_write_fp8(const CacheWriteArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  cache_write_fp8_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a);
+  launch(cache_write_fp8_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -29,9 +29,9 @@ hipError_t launch_cache_write(bool bf16, const CacheWriteArgs& a, hipStream_t s)
   if (a.T <= 0) return hipSuccess;
   const int grid = (a.T + 3) / 4;
   if (bf16)
-    cache_write_kernel<uint16_t><<<grid, 256, 0, s>>>(a);
+    launch(cache_write_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, a);
   else
-    cache_write_kernel<float><<<grid, 256, 0, s>>>(a);
+    launch(cache_write_kernel<float>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

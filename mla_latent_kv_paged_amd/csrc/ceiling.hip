@@ -107,13 +107,13 @@ __global__ __launch_bounds__(128) void gather_dma_kernel(DecodeArgs a, uint32_t*
 }
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s) {
-  stream_read_kernel<<<grid, 256, 0, s>>>(static_cast<const u32x4_t*>(src), bytes / 16, sink);
+  launch(stream_read_kernel, dim3(grid), dim3(256), 0, s, static_cast<const u32x4_t*>(src), bytes / 16, sink);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_dma(const DecodeArgs& a, uint32_t* sink, hipStream_t s) {
   const int grid = ((a.units + 7) >> 3) << 3;
-  gather_dma_kernel<<<grid, 128, 0, s>>>(a, sink);
+  launch(gather_dma_kernel, dim3(grid), dim3(128), 0, s, a, sink);
   return hipGetLastError();
 }
 

@@ -239,10 +239,10 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s) {
   if (bf16) {
     dim3 grid(a.H, (a.n_q + 15) / 16, a.v_parts);
-    combine_bf16_kernel<<<grid, 256, 0, s>>>(a);
+    launch(combine_bf16_kernel, dim3(grid), dim3(256), 0, s, a);
   } else {
     dim3 grid(a.H, (a.n_q + 15) / 16);
-    combine_kernel<float><<<grid, 256, 0, s>>>(a);
+    launch(combine_kernel<float>, dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -365,10 +365,10 @@ hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t 
   const int grid = ((a.units + 7) >> 3) << 3;
   switch (waves) {
     case 2:
-      decode_bf16_kernel<2, 3><<<grid, 128, 0, s>>>(a);
+      launch(decode_bf16_kernel<2, 3>, dim3(grid), dim3(128), 0, s, a);
       break;
     case 4:
-      decode_bf16_kernel<4, 2><<<grid, 256, 0, s>>>(a);
+      launch(decode_bf16_kernel<4, 2>, dim3(grid), dim3(256), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

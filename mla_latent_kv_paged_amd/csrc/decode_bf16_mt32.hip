@@ -449,13 +449,13 @@ hipError_t launch_decode_mt32(const DecodeArgs& a, int T, hipStream_t s) {
   const int grid = a.units;  // one workgroup per resident slot, each with an equal share
   switch (T) {
     case 1:
-      decode_bf16_mt32_kernel<1, 2><<<grid, 64, 0, s>>>(a);
+      launch(decode_bf16_mt32_kernel<1, 2>, dim3(grid), dim3(64), 0, s, a);
       break;
     case 2:
-      decode_bf16_mt32_kernel<2, 2><<<grid, 128, 0, s>>>(a);
+      launch(decode_bf16_mt32_kernel<2, 2>, dim3(grid), dim3(128), 0, s, a);
       break;
     case 4:
-      decode_bf16_mt32_kernel<4, 4><<<grid, 256, 0, s>>>(a);
+      launch(decode_bf16_mt32_kernel<4, 4>, dim3(grid), dim3(256), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

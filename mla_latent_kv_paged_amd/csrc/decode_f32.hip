@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.batch, a.q_len * a.H);
-  decode_f32_kernel<<<grid, 256, 0, s>>>(a);
+  launch(decode_f32_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

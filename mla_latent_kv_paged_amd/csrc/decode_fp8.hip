@@ -354,10 +354,10 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s) {
   const int grid = ((a.units + 7) >> 3) << 3;
   switch (waves) {
     case 2:
-      decode_fp8_kernel<2, 4><<<grid, 128, 0, s>>>(a);
+      launch(decode_fp8_kernel<2, 4>, dim3(grid), dim3(128), 0, s, a);
       break;
     case 4:
-      decode_fp8_kernel<4, 3><<<grid, 256, 0, s>>>(a);
+      launch(decode_fp8_kernel<4, 3>, dim3(grid), dim3(256), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -40,8 +40,8 @@ __global__ __launch_bounds__(256) void layer_pack_kernel(const uint16_t* src, co
 hipError_t launch_layer_pack(const void* src, const void* gamma, void* dst, int64_t rows, int K, hipStream_t s) {
   const int64_t n = rows * K;
   const int64_t grid = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
-  layer_pack_kernel<<<int(grid), 256, 0, s>>>(static_cast<const uint16_t*>(src), static_cast<const uint16_t*>(gamma),
-                                              static_cast<uint16_t*>(dst), n, K);
+  launch(layer_pack_kernel, dim3(int(grid)), dim3(256), 0, s, static_cast<const uint16_t*>(src),
+         static_cast<const uint16_t*>(gamma), static_cast<uint16_t*>(dst), n, K);
   return hipGetLastError();
 }
 
@@ -281,14 +281,14 @@ hipError_t launch_proj_gemm(const ProjArgs& a, hipStream_t s) {
   if (a.N % 64 != 0 || a.K % kProjChunk != 0) return hipErrorInvalidValue;
   if (a.M <= 16) {
     if (a.K % (kProjWaves * 32 * kProjSteps) != 0) return hipErrorInvalidValue;
-    proj_gemm_small_kernel<<<a.N / 16, kProjWaves * 64, 0, s>>>(a);
+    launch(proj_gemm_small_kernel, dim3(a.N / 16), dim3(kProjWaves * 64), 0, s, a);
     return hipGetLastError();
   }
-  proj_gemm_kernel<4><<<dim3(a.N / 64, a.K / kProjChunk, (a.M + 63) / 64), 256, 0, s>>>(a);
+  launch(proj_gemm_kernel<4>, dim3(a.N / 64, a.K / kProjChunk, (a.M + 63) / 64), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t threads = int64_t(a.M) * (a.N / 4);
-  proj_reduce_kernel<<<int((threads + 255) / 256), 256, 0, s>>>(a);
+  launch(proj_reduce_kernel, dim3(int((threads + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

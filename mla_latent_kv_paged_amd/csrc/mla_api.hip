@@ -13,6 +13,10 @@
 
 using namespace mla;
 
+namespace mla {
+thread_local LaunchEvents* t_launch_events = nullptr;
+}  // namespace mla
+
 // Decode scratch of mla_decode_noalloc: one static region per GPU, held by the loaded library until
 // the process ends.  Host code never passes its name to a kernel (on the host the name is only a
 // stand-in): the region's device address is looked up once per device, with that device current,
@@ -136,21 +140,31 @@ void prof_harvest(mla_ctx* c, int k, int64_t slot_count) {
     c->prof.total_ms[k] += ms;
 }
 
+// One profiled region: its launches carry the region's event pair (launch() in mla_internal.h), so
+// the pair times the kernels themselves.  A region that launched nothing records both events here.
 struct ProfScope {
   mla_ctx* c;
   int k;
   hipStream_t s;
   bool on;
+  LaunchEvents le{};
+  LaunchEvents* prev = nullptr;
   ProfScope(mla_ctx* c_, int k_, hipStream_t s_) : c(c_), k(k_), s(s_), on(c_->prof.on) {
     if (!on) return;
     const int64_t n = c->prof.count[k];
     if (n >= kProfRing) prof_harvest(c, k, n - kProfRing);  // slot about to be reused
-    hipEventRecord(c->prof.ev[k][n % kProfRing][0], s);
+    le = LaunchEvents{c->prof.ev[k][n % kProfRing][0], c->prof.ev[k][n % kProfRing][1], false};
+    prev = t_launch_events;
+    t_launch_events = &le;
   }
   ~ProfScope() {
     if (!on) return;
+    t_launch_events = prev;
     const int64_t n = c->prof.count[k];
-    hipEventRecord(c->prof.ev[k][n % kProfRing][1], s);
+    if (!le.started) {
+      hipEventRecord(le.start, s);
+      hipEventRecord(le.stop, s);
+    }
     c->prof.count[k] = n + 1;
   }
 };

@@ -1,12 +1,42 @@
 // Internal declarations shared by the host API and the kernels of libmla (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "mla.h"
 
 namespace mla {
+
+// ------------------------------------------------------------------------------------ launches
+
+// Timing of the kernels of one profiled region (mla_profile_enable).  While set, launch() hands the
+// region's events to the dispatch itself (hipExtLaunchKernelGGL): the first launch's start and each
+// launch's end.  The elapsed time is then the span of the kernels' own execution, without the queue's
+// time between a marker and the dispatch that follows it.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+  bool started;
+};
+extern thread_local LaunchEvents* t_launch_events;
+
+// Every kernel of the library is launched through here (the arguments are converted to the
+// kernel's parameter types, as a triple-chevron launch does).
+template <typename... P>
+inline void launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                   typename std::common_type<P>::type... args) {
+  LaunchEvents* e = t_launch_events;
+  if (e == nullptr) {
+    kernel<<<grid, block, shmem, s>>>(args...);
+    return;
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e->started ? nullptr : e->start, e->stop, 0u, args...);
+  e->started = true;
+}
 
 // Fixed MLA dimensions (DeepSeek-V2 / V2-Lite shapes).
 constexpr int DC = 512;        // kv_lora_rank: latent width

@@ -246,9 +246,9 @@ hipError_t launch_prefill_expand(PrefillArgs a, bool fp8, hipStream_t s) {
   if (units > 0x7fffffff) return hipErrorInvalidValue;
   a.units = int32_t(units);
   if (fp8)
-    prefill_expand_kernel<true><<<a.units, 256, 0, s>>>(a);
+    launch(prefill_expand_kernel<true>, dim3(a.units), dim3(256), 0, s, a);
   else
-    prefill_expand_kernel<false><<<a.units, 256, 0, s>>>(a);
+    launch(prefill_expand_kernel<false>, dim3(a.units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -564,7 +564,7 @@ hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s) {
   const int64_t grid = 8 * nbx * ((a.max_q_len + kQTile - 1) / kQTile);
   if (grid > 0x7ffffff0) return hipErrorInvalidValue;
   a.units = int32_t(grid);
-  prefill_attn_kernel<<<int(grid), 256, 0, s>>>(a);  // 80 KiB of LDS: two workgroups per CU
+  launch(prefill_attn_kernel, dim3(int(grid)), dim3(256), 0, s, a);  // 80 KiB of LDS: two workgroups per CU
   return hipGetLastError();
 }
 

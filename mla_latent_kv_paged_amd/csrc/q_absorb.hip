@@ -255,7 +255,7 @@ hipError_t launch_decode_prep(const QAbsorbArgs& a, const CacheWriteArgs& cw, bo
   const int64_t ncw = cw.T > 0 ? (int64_t(cw.T) + 3) / 4 : 0;
   const int64_t grid = ncw + int64_t(a.H) * ((a.n_q + 63) / 64) * c_split;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  decode_prep_kernel<<<int(grid), 256, 0, s>>>(a, c_split, cw, int(ncw), fp8 ? 1 : 0);
+  launch(decode_prep_kernel, dim3(int(grid)), dim3(256), 0, s, a, c_split, cw, int(ncw), fp8 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -263,10 +263,10 @@ hipError_t launch_q_absorb(bool bf16, const QAbsorbArgs& a, hipStream_t s) {
   if (bf16) {
     const int c_split = q_absorb_c_split(a);
     dim3 grid(a.H, (a.n_q + 63) / 64, c_split);
-    q_absorb_bf16_kernel<<<grid, 256, 0, s>>>(a, c_split);
+    launch(q_absorb_bf16_kernel, dim3(grid), dim3(256), 0, s, a, c_split);
   } else {
     dim3 grid(a.H, (a.n_q + 15) / 16);
-    q_absorb_kernel<float><<<grid, 256, 0, s>>>(a);
+    launch(q_absorb_kernel<float>, dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
