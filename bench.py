@@ -72,11 +72,13 @@ def parse():
     ap.add_argument("--layers", type=int, default=1, help="layer mode: attention layers in the model step (each "
                     "with its own weights and cache)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "decode-only", "prefill",
-                                                        "prefill-only", "layer", "layer-only", "ceiling"],
+                                                        "prefill-only", "layer", "layer-only", "ceiling",
+                                                        "mfma-calibration"],
                     help="copy-calibration: run a plain 256 MiB device copy (for counter scaling); "
                          "decode-only: run just the decode loop (for profilers); ceiling: the decode kernel "
                          "beside a plain streaming read of the same byte count and the decode's block gather "
-                         "alone (no math)")
+                         "alone (no math); mfma-calibration: the matrix cores' issue rate (mla_ceiling_mfma), "
+                         "the reference for the MFMA-busy counter")
     return ap.parse_args()
 
 
@@ -115,6 +117,36 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"mode": "copy-calibration", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                       "copies": 5}), flush=True)
+
+
+def mfma_calibration(args):
+    """mla_ceiling_mfma for both shapes (independent chains of v_mfma_f32_16x16x32_bf16, or of
+    v_mfma_f32_32x32x16_bf16, four waves per SIMD, 1,000 rounds per launch), each launch timed by events;
+    their MFMA-busy and GPU-active counters (taken in a profiler pass of this mode) define a fully
+    issued matrix pipe for each shape."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_paged_amd import _lib as L
+    L.load()
+    sink = torch.empty((1 << 20) // 4, dtype=torch.int32, device="cuda")
+    iters = 1000
+    res = {"mode": "mfma-calibration", "iterations": iters}
+    for shape, name in ((0, "16x16x32_bf16"), (1, "32x32x16_bf16")):
+        for _ in range(max(1, args.warmup)):
+            L.ceiling_mfma(shape, iters, sink)
+        n = max(1, args.steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        flops = 0.0
+        for i in range(n):
+            ev[i][0].record()
+            flops = L.ceiling_mfma(shape, iters, sink)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        med = float(np.median(np.array([a_.elapsed_time(b_) for a_, b_ in ev]) * 1e3))
+        res[name] = {"launches": n, "flops_per_launch": flops, "us_median": round(med, 2),
+                     "tflops_median": round(flops / (med * 1e-6) / 1e12, 1),
+                     "fraction_of_bf16_peak": round(flops / (med * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    print(json.dumps(res), flush=True)
 
 
 def kernel_source_sha(src):
@@ -528,6 +560,9 @@ def main():
     import torch
     if args.mode == "copy-calibration":
         copy_calibration()
+        return
+    if args.mode == "mfma-calibration":
+        mfma_calibration(args)
         return
     if args.mode in ("prefill", "prefill-only"):
         prefill_main(args)

@@ -348,7 +348,7 @@ mla_status mla_profile_samples(mla_ctx* ctx, int32_t kernel_id, float* ms, int32
 
 /* ------------------------------------------------------------------------------------------
  * Measurement kernels (not part of the compute path): the practical ceilings of the decode's
- * latent-cache stream on this device.
+ * latent-cache stream and of the matrix cores on this device.
  * ------------------------------------------------------------------------------------------ */
 
 /* A plain streaming read of `bytes` (a positive multiple of 16) contiguous device bytes at `src` by
@@ -357,6 +357,16 @@ mla_status mla_profile_samples(mla_ctx* ctx, int32_t kernel_id, float* ms, int32
  * the loads are kept.  Asynchronous on `stream`.
  * MLA_EINVAL for a null pointer, a size that is not a positive multiple of 16, or a sink too small. */
 mla_status mla_ceiling_read(const void* src, int64_t bytes, void* sink, int64_t sink_bytes, void* stream);
+
+/* The matrix cores' issue rate for one MFMA shape: 1,024 workgroups of four waves (four waves per SIMD),
+ * each wave running `iterations` (1 .. 2^20) rounds of independent chains on register operands: shape 0,
+ * eight chains of v_mfma_f32_16x16x32_bf16 (the decode's score MFMA); shape 1, four chains of
+ * v_mfma_f32_32x32x16_bf16.  Either way a round is 8 x 2 x 16 x 16 x 32 flops per wave; *flops (if not NULL)
+ * receives the launch's count, 1,024 x 4 x iterations x 8 x 2 x 16 x 16 x 32.  `sink` (device, at least
+ * 1 MiB) receives one word per thread.  Asynchronous on `stream`.  MLA_EINVAL for a null sink, a sink too
+ * small, an unknown shape or an iteration count out of range. */
+mla_status mla_ceiling_mfma(int32_t shape, int32_t iterations, void* sink, int64_t sink_bytes, double* flops,
+                            void* stream);
 
 /* The data movement of mla_decode's 16-row bf16 decode kernel and nothing else, for the decode those
  * arguments describe (same split, work units, unit order, waves, LDS ring and zero-block substitution):

@@ -25,7 +25,7 @@ EXPORTS = ("mla_absorb_weights", "mla_cache_write", "mla_decode", "mla_decode_st
            "mla_free", "mla_status_string",
            "mla_set_decode_tuning", "mla_last_decode_shape", "mla_profile_enable", "mla_profile_read",
            "mla_profile_samples", "mla_prefill", "mla_prefill_workspace_size", "mla_layer_weights",
-           "mla_layer_decode_step", "mla_ceiling_read", "mla_ceiling_gather")
+           "mla_layer_decode_step", "mla_ceiling_read", "mla_ceiling_gather", "mla_ceiling_mfma")
 
 
 class MLAConfig(ctypes.Structure):
@@ -78,6 +78,8 @@ def load(path=None):
     lib.mla_ceiling_read.restype = i32
     lib.mla_ceiling_gather.argtypes = [vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, i64, vp]
     lib.mla_ceiling_gather.restype = i32
+    lib.mla_ceiling_mfma.argtypes = [i32, i32, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
+    lib.mla_ceiling_mfma.restype = i32
     lib.mla_free.argtypes = [vp]
     lib.mla_free.restype = None
     lib.mla_status_string.argtypes = [i32]
@@ -102,6 +104,15 @@ def ceiling_read(src, sink, stream=None):
     nbytes = int(src.numel() * src.element_size())
     _check(load().mla_ceiling_read(_ptr(src), nbytes, _ptr(sink), int(sink.numel() * sink.element_size()),
                                    _stream_ptr(stream)), "mla_ceiling_read")
+
+
+def ceiling_mfma(shape, iterations, sink, stream=None):
+    """mla_ceiling_mfma: the matrix cores' issue rate for shape 0 (16x16x32 bf16) or 1 (32x32x16 bf16);
+    returns the launch's flop count."""
+    flops = ctypes.c_double()
+    _check(load().mla_ceiling_mfma(int(shape), int(iterations), _ptr(sink), int(sink.numel() * sink.element_size()),
+                                   ctypes.byref(flops), _stream_ptr(stream)), "mla_ceiling_mfma")
+    return flops.value
 
 
 def status_string(status):

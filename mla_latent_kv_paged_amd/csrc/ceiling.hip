@@ -11,6 +11,11 @@
 //                       LDS stages fed by global_load_lds_dwordx4 two blocks ahead, the same zero-block
 //                       substitution for tokens past the context.  A block is "consumed" by one LDS read
 //                       once it has landed.  No MFMA, no softmax, no partial store.
+//  mfma_loop_kernel     the matrix cores' issue rate for one instruction shape: every wave runs
+//                       independent chains of v_mfma_f32_16x16x32_bf16 (eight) or v_mfma_f32_32x32x16_bf16
+//                       (four) on register operands, four waves per SIMD.  Its counters (MFMA busy cycles
+//                       per active GPU cycle) define a fully issued matrix pipe for that shape, against
+//                       which a kernel's counters are read.
 #include "mla_internal.h"
 
 namespace mla {
@@ -106,6 +111,42 @@ __global__ __launch_bounds__(128) void gather_dma_kernel(DecodeArgs a, uint32_t*
   sink[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = x;
 }
 
+// SHAPE 0: eight chains of v_mfma_f32_16x16x32_bf16; SHAPE 1: four chains of v_mfma_f32_32x32x16_bf16
+template <int SHAPE>
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, uint32_t* sink) {
+  // bf16 operands 1.0 and 2^-10: the sums stay small and finite for any iteration count used here
+  u32x4_t a = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  u32x4_t b = {0x3a803a80u, 0x3a803a80u, 0x3a803a80u, 0x3a803a80u};
+  asm volatile("" : "+v"(a), "+v"(b));
+  float x = 0.f;
+  if constexpr (SHAPE == 0) {
+    f32x4_t acc[kMfmaChains];
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int c = 0; c < kMfmaChains; ++c) acc[c] = mfma32v(a, b, acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c) x += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  } else {
+    f32x16_t acc[kMfmaChains / 2];
+#pragma unroll
+    for (int c = 0; c < kMfmaChains / 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int c = 0; c < kMfmaChains / 2; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                         acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kMfmaChains / 2; ++c) x += acc[c][0] + acc[c][15];
+  }
+  sink[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = __float_as_uint(x);
+}
+
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s) {
   launch(stream_read_kernel, dim3(grid), dim3(256), 0, s, static_cast<const u32x4_t*>(src), bytes / 16, sink);
   return hipGetLastError();
@@ -114,6 +155,14 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
 hipError_t launch_gather_dma(const DecodeArgs& a, uint32_t* sink, hipStream_t s) {
   const int grid = ((a.units + 7) >> 3) << 3;
   launch(gather_dma_kernel, dim3(grid), dim3(128), 0, s, a, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_loop(int shape, int iters, uint32_t* sink, int grid, hipStream_t s) {
+  if (shape == 0)
+    launch(mfma_loop_kernel<0>, dim3(grid), dim3(256), 0, s, iters, sink);
+  else
+    launch(mfma_loop_kernel<1>, dim3(grid), dim3(256), 0, s, iters, sink);
   return hipGetLastError();
 }
 

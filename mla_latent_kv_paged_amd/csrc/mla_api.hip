@@ -774,6 +774,17 @@ mla_status mla_ceiling_read(const void* src, int64_t bytes, void* sink, int64_t 
   return hip_status(launch_stream_read(src, bytes, static_cast<uint32_t*>(sink), kGrid, as_stream(stream)));
 }
 
+mla_status mla_ceiling_mfma(int32_t shape, int32_t iterations, void* sink, int64_t sink_bytes, double* flops,
+                            void* stream) {
+  if (!sink || (shape != 0 && shape != 1) || iterations < 1 || iterations > (1 << 20) ||
+      sink_bytes < int64_t(kMfmaLoopGrid) * 256 * 4)
+    return MLA_EINVAL;
+  // eight 16x16x32 or four 32x32x16 MFMAs per wave and round: 2 x 16 x 16 x 32 x 8 flops either way
+  if (flops) *flops = double(kMfmaLoopGrid) * 4 * double(iterations) * kMfmaChains * (2.0 * 16 * 16 * 32);
+  return hip_status(
+      launch_mfma_loop(shape, iterations, static_cast<uint32_t*>(sink), kMfmaLoopGrid, as_stream(stream)));
+}
+
 mla_status mla_ceiling_gather(mla_ctx* ctx, int32_t batch, int32_t q_len, const void* kv_cache, int32_t num_blocks,
                               const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
                               int32_t max_seq_len, void* sink, int64_t sink_bytes, void* stream) {

@@ -230,6 +230,9 @@ hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s);
 hipError_t launch_layer_pack(const void* src, const void* gamma, void* dst, int64_t rows, int K, hipStream_t s);
 hipError_t launch_proj_gemm(const ProjArgs& a, hipStream_t s);
 // measurement kernels (ceiling.hip)
+constexpr int kMfmaChains = 8;       // independent 16x16x32 MFMA chains per wave in mfma_loop_kernel (32x32x16: half)
+constexpr int kMfmaLoopGrid = 1024;  // its workgroups (256 threads): four waves per SIMD
+hipError_t launch_mfma_loop(int shape, int iters, uint32_t* sink, int grid, hipStream_t s);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
 hipError_t launch_gather_dma(const DecodeArgs& a, uint32_t* sink, hipStream_t s);
 
@@ -238,6 +241,7 @@ hipError_t launch_gather_dma(const DecodeArgs& a, uint32_t* sink, hipStream_t s)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 

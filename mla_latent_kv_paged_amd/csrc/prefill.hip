@@ -11,7 +11,7 @@
 // absorbed form the decode uses: with many query rows per token the expansion pays for itself.
 //
 // Two kernels:
-//  * expand: per (sequence, 256 tokens, head, K or V): W_uk[h] or W_uv[h] (128 x 512) is staged in
+//  * expand: per (sequence, 1,024 tokens, head, K or V): W_uk[h] or W_uv[h] (128 x 512) is staged in
 //    LDS once (XOR-swizzled granules, conflict-free reads), the tokens' latent rows are the
 //    B operand straight from the paged cache; v_mfma_f32_16x16x32_bf16 with the 128 output
 //    dimensions on M and 16 tokens on N, the A operands of the next K step read from LDS while the
