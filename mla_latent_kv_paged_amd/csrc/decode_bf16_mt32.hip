@@ -30,18 +30,12 @@ namespace mla {
 
 namespace {
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr float kReset = 64.f;    // reference-max headroom (log2 units): P <= 2^64
 constexpr int kChunks = 36;       // 1 KB chunks per stage (72 granules x 32 tokens)
 constexpr int kStageBytes = kChunks * 1024;
 constexpr int kIdCap = 2048;      // block ids of one piece held in LDS (a range is <= kIdCap / 2 steps)
-
-__device__ __forceinline__ f32x16_t mfma32x32(u32x4_t a, u32x4_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
 
 // P.C step on one accumulator tile kept in AGPRs (acc is the whole AGPR file; the builtin would
 // let the allocator shuttle it through VGPRs).  The compiler does not see this as an MFMA, so the

@@ -255,6 +255,12 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+// v_mfma_f32_32x32x16_bf16: A lane l = row l % 32, K values 8 (l / 32) .. + 7; B lane l = column l % 32,
+// the same K values; D lane l = column l % 32, rows 8 (R / 4) + 4 (l / 32) + R % 4 in register R
+__device__ __forceinline__ f32x16_t mfma32x32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
 __device__ __forceinline__ f32x4_t mfma32v(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
