@@ -45,8 +45,8 @@ PER_FILE = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
             "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
-def _compile(src, extra, verbose):
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+def _compile(src, extra, verbose, objdir=OBJDIR):
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *COMMON, *PER_FILE.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -59,22 +59,44 @@ def _compile(src, extra, verbose):
     return obj
 
 
-def build(verbose=False, extra_flags=()):
+def build(verbose=False, extra_flags=(), objdir=OBJDIR, lib=LIB):
     """Compile every csrc/*.hip for gfx950 and link libmla.so. Returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags), verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags), verbose, objdir), srcs))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+# AddressSanitizer on the host code only (every flag after -Xarch_host; the device code is built as
+# usual).  The library leaves the sanitizer's symbols to the runtime, which the process preloads.
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+ASAN_OBJDIR = os.path.join(PKG, "_build_asan")
+ASAN_LIB = os.path.join(ASAN_OBJDIR, "libmla_asan.so")
+
+
+def build_asan(verbose=False):
+    """libmla with host-side AddressSanitizer (for CPU tests of the host code). Returns its path."""
+    return build(verbose, ASAN_HOST, ASAN_OBJDIR, ASAN_LIB)
+
+
+def asan_runtime():
+    """Path of the compiler's AddressSanitizer runtime for x86-64, or None."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    p = r.stdout.strip()
+    if r.returncode == 0 and os.path.isabs(p) and os.path.exists(p):
+        return p
+    found = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[-1] if found else None
 
 
 if __name__ == "__main__":

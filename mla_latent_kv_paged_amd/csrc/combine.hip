@@ -82,31 +82,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // r*64 + (c ^ swz(r)) so that 16 lanes reading one granule column hit distinct bank groups.
 __device__ __forceinline__ int o_swz(int r) { return ((r & 7) << 1) | (r >> 3); }
 
-__global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
-  const int h = blockIdx.x;
-  const int r0 = blockIdx.y * 16;
-  const int vq = blockIdx.z;  // part of the 128 output channels (one of v_parts)
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  __shared__ uint4 ohi[16 * 64];
-  __shared__ uint4 olo[16 * 64];
-
-  // output channel tiles of 16: with 4 parts, waves 0 and 1 take one tile each of this
-  // workgroup's 32 channels; with 1 part, every wave takes two tiles of its 32.  The first tile's
-  // W_uv fragments do not depend on the merge, so their loads are issued first.
-  const int ntile = a.v_parts == 1 ? 2 : 1;
-  const int vbase = a.v_parts == 1 ? 32 * w : vq * 32 + (w & 1) * 16;
-  const uint16_t* wuv_h = static_cast<const uint16_t*>(a.W_uv) + int64_t(h) * DV * DC;
-  const uint4* wrow = reinterpret_cast<const uint4*>(wuv_h + int64_t(vbase + (lane & 15)) * DC);
-  const bool gemm_wave = a.v_parts == 1 || w < 2;
-  uint4 wf[16];
-  if (gemm_wave) {
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) wf[ks] = wrow[4 * ks + (lane >> 4)];
-  }
-
-  // merge the partials: wave w owns rows 4w..4w+3, lane owns channels 8*lane..8*lane+7.  Row rr's
-  // partials are base[rr] + j * stride[rr], j < ns[rr] (by split: consecutive slots; by piece:
+// Merge the partials of rows row0 .. row0 + 3 (rows >= n_q contribute nothing) of head h: the lane's
+// channels 8 lane .. 8 lane + 7 of each row's o_lat, as an unevaluated sum of two bf16 values per
+// channel (hi = bf16(o), lo = bf16(o - hi)).
+__device__ __forceinline__ void merge_rows4(const CombineArgs& a, int h, int row0, int lane, uint32_t (&hw)[4][4],
+                                            uint32_t (&lw)[4][4]) {
+  // Row rr's partials are base[rr] + j * stride[rr], j < ns[rr] (by split: consecutive slots; by piece:
   // consecutive pieces of its stream).  They are taken in chunks of 4 up to the largest count
   // among the wave's rows; inside a chunk the loads are unconditional (a row's index is clamped to
   // its last partial and the surplus dropped by selection, never by multiplication).  Chunks are
@@ -118,7 +99,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
     int rq[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int row = r0 + w * 4 + rr;
+      const int row = row0 + rr;
       const int rowc = row < a.n_q ? row : a.n_q - 1;
       rq[rr] = (rowc % a.q_len) * a.H + h;  // row within the sequence
       pt[rr] = a.piece_tbl[(rowc / a.q_len) * a.n_grp + rq[rr] / a.rows_per_piece];
@@ -127,14 +108,14 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
     for (int rr = 0; rr < 4; ++rr) {
       base[rr] = int64_t(pt[rr].x) * a.rows_per_piece + rq[rr] % a.rows_per_piece;
       stride[rr] = a.rows_per_piece;
-      ns[rr] = (r0 + w * 4 + rr < a.n_q) ? pt[rr].y : 0;
+      ns[rr] = (row0 + rr < a.n_q) ? pt[rr].y : 0;
     }
   } else {
     // every split is read (an empty one carries m = -inf and is skipped by selection), so the
     // loads do not wait for the context length
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int row = r0 + w * 4 + rr;
+      const int row = row0 + rr;
       const int rowc = row < a.n_q ? row : a.n_q - 1;
       base[rr] = (int64_t(rowc) * a.H + h) * a.n_split;
       stride[rr] = 1;
@@ -196,18 +177,50 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   }
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int r = w * 4 + rr;
     const float inv = den[rr] > 0.f ? 1.f / den[rr] : 0.f;
-    uint32_t hw[4], lw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float x0 = o[rr][2 * e] * inv, x1 = o[rr][2 * e + 1] * inv;
-      hw[e] = cvt_pk_bf16(x0, x1);
-      lw[e] = cvt_pk_bf16(x0 - __uint_as_float(hw[e] << 16), x1 - __uint_as_float(hw[e] & 0xffff0000u));
+      hw[rr][e] = cvt_pk_bf16(x0, x1);
+      lw[rr][e] = cvt_pk_bf16(x0 - __uint_as_float(hw[rr][e] << 16), x1 - __uint_as_float(hw[rr][e] & 0xffff0000u));
     }
-    const int gi = r * 64 + (lane ^ o_swz(r));
-    ohi[gi] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    olo[gi] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
+  const int h = blockIdx.x;
+  const int r0 = blockIdx.y * 16;
+  const int vq = blockIdx.z;  // part of the 128 output channels (one of v_parts)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  __shared__ uint4 ohi[16 * 64];
+  __shared__ uint4 olo[16 * 64];
+
+  // output channel tiles of 16: with 4 parts, waves 0 and 1 take one tile each of this
+  // workgroup's 32 channels; with 1 part, every wave takes two tiles of its 32.  The first tile's
+  // W_uv fragments do not depend on the merge, so their loads are issued first.
+  const int ntile = a.v_parts == 1 ? 2 : 1;
+  const int vbase = a.v_parts == 1 ? 32 * w : vq * 32 + (w & 1) * 16;
+  const uint16_t* wuv_h = static_cast<const uint16_t*>(a.W_uv) + int64_t(h) * DV * DC;
+  const uint4* wrow = reinterpret_cast<const uint4*>(wuv_h + int64_t(vbase + (lane & 15)) * DC);
+  const bool gemm_wave = a.v_parts == 1 || w < 2;
+  uint4 wf[16];
+  if (gemm_wave) {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) wf[ks] = wrow[4 * ks + (lane >> 4)];
+  }
+
+  // merge the partials: wave w owns rows 4w..4w+3
+  {
+    uint32_t hw[4][4], lw[4][4];
+    merge_rows4(a, h, r0 + w * 4, lane, hw, lw);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = w * 4 + rr;
+      const int gi = r * 64 + (lane ^ o_swz(r));
+      ohi[gi] = make_uint4(hw[rr][0], hw[rr][1], hw[rr][2], hw[rr][3]);
+      olo[gi] = make_uint4(lw[rr][0], lw[rr][1], lw[rr][2], lw[rr][3]);
+    }
   }
   __syncthreads();
   if (a.v_parts != 1 && w >= 2) return;

@@ -45,6 +45,12 @@ def test_status_strings():
 
 def test_invalid_host_arguments_rejected_without_device():
     L, lib = _lib()
+    host_checks(L, lib)
+
+
+def host_checks(L, lib):
+    """Host-side argument validation through the C ABI, with no device involved (also run against the
+    host-AddressSanitizer build of the library by tests/test_host_asan.py)."""
     out = ctypes.c_void_p(123)
     # null config / weights
     assert lib.mla_absorb_weights(None, None, None, None, ctypes.byref(out)) == L.MLA_EINVAL
@@ -65,4 +71,11 @@ def test_invalid_host_arguments_rejected_without_device():
     assert lib.mla_cache_write(None, None, 512, None, 64, None, None, 1, None, 1, None) == L.MLA_EINVAL
     assert lib.mla_decode(None, None, 1, 1, None, 1, None, 1, None, 1, None, None) == L.MLA_EINVAL
     assert lib.mla_set_decode_tuning(None, 1, 0) == L.MLA_EINVAL
+    n = ctypes.c_size_t(7)
+    assert lib.mla_prefill_workspace_size(None, 1, 1, 64, ctypes.byref(n)) == L.MLA_EINVAL
+    assert lib.mla_ceiling_read(None, 16, None, 1 << 20, None) == L.MLA_EINVAL
+    assert lib.mla_ceiling_mfma(2, 10, fake, 1 << 20, None, None) == L.MLA_EINVAL
+    assert lib.mla_ceiling_mfma(0, 0, fake, 1 << 20, None, None) == L.MLA_EINVAL
+    for code in range(-6, 2):
+        assert lib.mla_status_string(code)
     lib.mla_free(None)
