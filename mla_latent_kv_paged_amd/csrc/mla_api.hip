@@ -179,7 +179,11 @@ mla_status hip_status(hipError_t e) {
 // items whose longest context spans max_blocks blocks.  The bf16 kernel holds one workgroup per
 // CU, so the grid is sized to a whole number of workgroups per CU where possible
 // (units * n_split ~ k * CUs); a split is capped so that a few long sequences in a ragged batch
-// do not serialise the tail, and holds at least one block per wave.
+// do not serialise the tail, and holds at least one block per wave.  With few units the splits
+// are kept to at least sqrt(max_blocks) blocks: a split costs a workgroup's start-up and the
+// combine one more partial per row to merge, against blocks that stream at a fraction of that
+// each (at batch 1: about 0.5 us per block, 0.4 us per partial, 6 us per workgroup's start),
+// so the step is shortest near sqrt(max_blocks) blocks per split.
 int choose_split_blocks(const mla_ctx* c, int units, int max_blocks, int waves) {
   const int cus = c->cu_count;
   int n_target;
@@ -189,6 +193,9 @@ int choose_split_blocks(const mla_ctx* c, int units, int max_blocks, int waves) 
     n_target = cus / units;  // floor: units * n_target <= CUs, one round
   if (n_target < 1) n_target = 1;
   int sb = (max_blocks + n_target - 1) / n_target;
+  int sq = 1;
+  while (sq * sq < max_blocks) ++sq;
+  if (sb < sq) sb = sq;
   const int cap = 128 * waves;
   if (sb > cap) sb = cap;
   if (sb < waves) sb = waves;
