@@ -2,13 +2,13 @@
 // against (not part of the compute path).
 //
 //  stream_read_kernel   a plain read of `bytes` contiguous bytes into registers, each workgroup a
-//                       contiguous range read 32 KiB at a time (global_load_dwordx4, eight loads per
-//                       lane in flight), one word per thread written so that the loads are kept: the
-//                       device's streaming-read rate.
+//                       contiguous range read 32 KiB at a time (global_load_dwordx4 with the non-temporal
+//                       hint, eight loads per lane in flight), one word per thread written so that the
+//                       loads are kept: the device's streaming-read rate.
 //  gather_dma_kernel    the 16-row bf16 decode kernel's data movement and nothing else: the same work
 //                       units (sequence, split), the same XCD-contiguous unit order, two waves per
 //                       workgroup striding over the split's blocks, each with a ring of three 18 KiB
-//                       LDS stages fed by global_load_lds_dwordx4 two blocks ahead, the same zero-block
+//                       LDS stages fed by global_load_lds_dwordx4 (non-temporal) two blocks ahead, the same zero-block
 //                       substitution for tokens past the context.  A block is "consumed" by one LDS read
 //                       once it has landed.  No MFMA, no softmax, no partial store.
 //  mfma_loop_kernel     the matrix cores' issue rate for one instruction shape: every wave runs
@@ -29,11 +29,11 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* src, in
   for (; i + 7 * 256 < hi; i += 8 * 256) {
     u32x4_t v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = src[i + k * 256];
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(src + i + k * 256);
 #pragma unroll
     for (int k = 0; k < 8; ++k) x ^= v[k];
   }
-  for (; i < hi; i += 256) x ^= src[i];
+  for (; i < hi; i += 256) x ^= __builtin_nontemporal_load(src + i);
   sink[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(128) void gather_dma_kernel(DecodeArgs a, uint32_t*
       const char* src =
           (ok ? cache + (int64_t(phys) * BLK + trow) * (ROW * 2) : zero + trow * (ROW * 2)) + 16 * lgr;
 #pragma unroll
-      for (int gq = 0; gq < 9; ++gq) dma16(src + 128 * gq, dst + 1024 * (9 * tg + gq));
+      for (int gq = 0; gq < 9; ++gq) dma16_nt(src + 128 * gq, dst + 1024 * (9 * tg + gq));
     }
   };
   const int pre = nwb < kNS - 1 ? nwb : kNS - 1;

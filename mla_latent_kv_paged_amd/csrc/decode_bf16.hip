@@ -165,7 +165,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
       const char* src =
           (ok ? cache + (int64_t(phys) * BLK + trow) * (ROW * 2) : zero + trow * (ROW * 2)) + 16 * lgr;
 #pragma unroll
-      for (int gq = 0; gq < 9; ++gq) dma16(src + 128 * gq, dst + 1024 * (9 * tg + gq));
+      for (int gq = 0; gq < 9; ++gq) dma16_nt(src + 128 * gq, dst + 1024 * (9 * tg + gq));
     }
   };
 

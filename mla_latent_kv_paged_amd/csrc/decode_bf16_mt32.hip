@@ -203,7 +203,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       }
       return x;
     };
-    auto put = [&](const Xfer& x, int c) { dma16(x.src[c / 9] + 128 * (c % 9), x.dst + 1024 * c); };
+    auto put = [&](const Xfer& x, int c) { dma16_nt(x.src[c / 9] + 128 * (c % 9), x.dst + 1024 * c); };
     auto issue = [&](int i, int pa, int pb) {
       const Xfer x = prep(i, pa, pb);
 #pragma unroll

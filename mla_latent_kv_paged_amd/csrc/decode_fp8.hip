@@ -155,15 +155,15 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
     const int pc_last = lane < 16 ? 640 + lane : lane;
     if (vis == BLK * kPieces) {  // the common case: the whole block is visible
 #pragma unroll
-      for (int k = 0; k < 10; ++k) dma16(blk + 16 * (64 * k + lane), dst + 1024 * k);
-      dma16(blk + 16 * pc_last, dst + 10240);
+      for (int k = 0; k < 10; ++k) dma16_nt(blk + 16 * (64 * k + lane), dst + 1024 * k);
+      dma16_nt(blk + 16 * pc_last, dst + 10240);
     } else {
 #pragma unroll
       for (int k = 0; k < 10; ++k) {
         const int pc = 64 * k + lane;
-        dma16((pc < vis ? blk : zero) + 16 * pc, dst + 1024 * k);
+        dma16_nt((pc < vis ? blk : zero) + 16 * pc, dst + 1024 * k);
       }
-      dma16((pc_last < vis ? blk : zero) + 16 * pc_last, dst + 10240);
+      dma16_nt((pc_last < vis ? blk : zero) + 16 * pc_last, dst + 10240);
     }
   };
 
