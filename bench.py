@@ -40,7 +40,7 @@ TRAFFIC = {"lite_b64": ("decode_bf16_lite_b64_s4096_traffic.json", "decode_bf16.
            "ragged": ("decode_bf16_mt32_ragged_b256_q4_traffic.json", "decode_bf16_mt32.hip")}
 TRAFFIC_FP8 = {"lite_b64": ("decode_fp8_lite_b64_s4096_traffic.json", "decode_fp8.hip")}
 # the chunked prefill's attention kernel at the default prefill sizes (4 sequences x 4,096 tokens)
-TRAFFIC_PF = ("prefill_attn_b4_s4096_traffic.json", "prefill.hip")
+TRAFFIC_PF = ("prefill_attn_b4_s4096_traffic.json", "prefill_attn.hip")
 
 
 def parse():
@@ -150,9 +150,10 @@ def mfma_calibration(args):
 
 
 def kernel_source_sha(src):
-    """sha256 of a decode kernel's source followed by the internal header it includes."""
+    """sha256 of a kernel's source followed by the internal headers it includes (the prefill kernels'
+    shared header, then mla_internal.h)."""
     h = hashlib.sha256()
-    for f in (src, "mla_internal.h"):
+    for f in (src,) + (("prefill_common.h",) if src.startswith("prefill") else ()) + ("mla_internal.h",):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
@@ -368,7 +369,7 @@ def prefill_main(args):
                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(fa / (kus["attn"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                         "traffic": prefill_traffic(args),
-                        "kernel": "prefill_attn_kernel",
+                        "kernel": "prefill_attn32_kernel (with the q_pe rotation before it)",
                         "expand_tflops": round(fe / (kus["expand"] * 1e-6) / 1e12, 2)}}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = prefill_cpu_baseline(w)

@@ -292,7 +292,8 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
 
 /* Bytes of workspace mla_prefill needs for `batch` sequences of contexts up to max_seq_len tokens
  * and total_q new tokens: the expanded rows [K_nope | k_pe | V], batch * H * ceil1024(max_seq_len)
- * * 320 bf16 (total_q does not enter at present).  MLA_EINVAL for a null pointer or a size < 1. */
+ * * 320 bf16, then the rotated q_pe, total_q * H * 64 bf16.  MLA_EINVAL for a null pointer or a
+ * size < 1. */
 mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t total_q, int32_t max_seq_len,
                                       size_t* bytes);
 

@@ -42,7 +42,8 @@ def _hipcc():
 # code is the same either way (two waves per SIMD leave no AGPRs), and the expansion kernel (one
 # wave per SIMD) keeps its accumulators in AGPRs, which leaves VGPRs for reading ahead.
 PER_FILE = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-            "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+            "decode_bf16_mt32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+            "prefill_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src, extra, verbose, objdir=OBJDIR):

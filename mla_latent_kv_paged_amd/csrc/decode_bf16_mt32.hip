@@ -37,17 +37,6 @@ constexpr int kChunks = 36;       // 1 KB chunks per stage (72 granules x 32 tok
 constexpr int kStageBytes = kChunks * 1024;
 constexpr int kIdCap = 2048;      // block ids of one piece held in LDS (a range is <= kIdCap / 2 steps)
 
-// P.C step on one accumulator tile kept in AGPRs (acc is the whole AGPR file; the builtin would
-// let the allocator shuttle it through VGPRs).  The compiler does not see this as an MFMA, so the
-// wait states it would add are provided by the callers: an accumulator tile is next touched 16
-// MFMAs later at the earliest, its VALU readers run after a drain (mfma_drain), and the P operand
-// written by VALU is followed by s_nop before the first of these.
-__device__ __forceinline__ void mfma32x32_acc(f32x16_t& acc, u32x4_t a, u32x4_t b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// wait states after the last asm MFMA before VALU reads its accumulator (> 18 for 16 passes)
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
 }  // namespace
 
 template <int T, int NSTAGE>

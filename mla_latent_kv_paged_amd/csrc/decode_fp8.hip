@@ -67,8 +67,7 @@ __device__ __forceinline__ s16x4_t codes4(uint32_t c) {
 __device__ __forceinline__ void mfma16_acc(f32x4_t& acc, s16x4_t a, s16x4_t b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-// wait states after the last asm MFMA before VALU touches its accumulator (more than the 19 of a 16-pass MFMA)
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// (mfma_drain, the wait states after the last asm MFMA before VALU touches its accumulator, is shared)
 
 }  // namespace
 

@@ -250,6 +250,7 @@ mla_status mla_absorb_weights(const mla_config* cfg, const void* kv_b_proj_w, co
   }
   // the static scratch region of this device (mla_decode_noalloc reports a failed lookup)
   if (scratch_address(c->device, &c->scratch) != hipSuccess) c->scratch = nullptr;
+
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, c->device) == hipSuccess && prop.multiProcessorCount > 0)
     c->cu_count = prop.multiProcessorCount;
@@ -714,7 +715,8 @@ mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t
                                       size_t* bytes) {
   if (!ctx || !bytes || batch < 1 || total_q < 1 || max_seq_len < 1) return MLA_EINVAL;
   const int64_t kv = int64_t(batch) * ctx->cfg.num_heads * prefill_tpad(max_seq_len) * (DN + DR + DV) * 2;
-  *bytes = size_t(kv);
+  const int64_t qr = int64_t(total_q) * ctx->cfg.num_heads * DR * 2;  // the rotated q_pe
+  *bytes = size_t(kv + qr);
   return MLA_OK;
 }
 
@@ -755,6 +757,7 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
   pa.W_uk = static_cast<const uint16_t*>(ctx->W_uk);
   pa.W_uv = static_cast<const uint16_t*>(ctx->W_uv);
   pa.kv = reinterpret_cast<uint16_t*>(ws);
+  pa.qpe = reinterpret_cast<uint16_t*>(ws + int64_t(batch) * cf.num_heads * prefill_tpad(max_seq_len) * (DN + DR + DV) * 2);
   pa.out = out;
   hipError_t e;
   {
@@ -763,8 +766,9 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
   }
   if (e != hipSuccess) return hip_status(e);
   {
-    ProfScope ps(ctx, MLA_K_PF_ATTN, s);
-    e = launch_prefill_attn(pa, s);
+    ProfScope ps(ctx, MLA_K_PF_ATTN, s);  // the rotation of q_pe and the attention
+    e = launch_prefill_qprep(pa, s);
+    if (e == hipSuccess) e = launch_prefill_attn(pa, s);
   }
   return hip_status(e);
 }

@@ -144,6 +144,7 @@ struct PrefillArgs {
   const uint16_t* W_uk;        // [H, DN, DC]
   const uint16_t* W_uv;        // [H, DV, DC]
   uint16_t* kv;
+  uint16_t* qpe;               // [total_q, H, DR] bf16: RoPE(q_pe) at the rows' positions (written by the prep)
   void* out;                   // [total_q, H, DV] bf16
   int32_t units;               // work items of the kernel being launched
 };
@@ -215,6 +216,8 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s);
 // fp8: the cache holds FP8 rows (kFp8Row bytes) instead of bf16 rows
 hipError_t launch_prefill_expand(PrefillArgs a, bool fp8, hipStream_t s);
 hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s);
+hipError_t launch_prefill_attn32(PrefillArgs a, hipStream_t s);
+hipError_t launch_prefill_qprep(PrefillArgs a, hipStream_t s);
 // bf16, 32-row tiles (H*q_len a multiple of 32), T in {1, 2, 4} tiles per workgroup; n_rt = tiles of
 // 32 rows per sequence (a multiple of T); units = workgroups, enough that every workgroup's share
 // is at most kMt32MaxSteps steps of two blocks
@@ -357,6 +360,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier ordering LDS only (the wave's own LDS accesses are complete when it arrives).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+
+// acc += a * b (v_mfma_f32_32x32x16_bf16) on an accumulator tile kept in AGPRs (with the builtin the
+// allocator may shuttle it through VGPRs).  The compiler does not see this as an MFMA, so the wait
+// states it would add are the callers': the tile is next touched several MFMAs later, its VALU readers
+// run after a drain (mfma_drain), and operands written by VALU are followed by s_nop before the first
+// of these that reads them.
+__device__ __forceinline__ void mfma32x32_acc(f32x16_t& acc, u32x4_t a, u32x4_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// wait states after the last such MFMA before VALU reads its accumulator (> 18 for 16 passes)
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // acc *= f for an accumulator vector held in AGPRs, element by element where it is called (a plain
 // multiply lets the register allocator keep a VGPR copy of every tile, refreshed each iteration).

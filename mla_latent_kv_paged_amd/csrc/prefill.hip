@@ -10,71 +10,20 @@
 // the cache.  Per (row, token) this costs 2 (192 + 128) flops, against 2 (576 + 512) for the
 // absorbed form the decode uses: with many query rows per token the expansion pays for itself.
 //
-// Two kernels:
-//  * expand: per (sequence, 1,024 tokens, head, K or V): W_uk[h] or W_uv[h] (128 x 512) is staged in
-//    LDS once (XOR-swizzled granules, conflict-free reads), the tokens' latent rows are the
-//    B operand straight from the paged cache; v_mfma_f32_16x16x32_bf16 with the 128 output
-//    dimensions on M and 16 tokens on N, the A operands of the next K step read from LDS while the
-//    current step's MFMAs run.  Part K also copies the tokens' rope keys.  Output rows
-//    [K_nope | k_pe | V] (320 bf16) per (sequence, head, token), rounded to bf16 once.
-//  * attn: one workgroup per (sequence, head, 128 query rows), four waves of 32 rows (two 16-row
-//    tiles, so that every key and value operand read from LDS feeds two MFMAs).  Keys move
-//    HBM -> LDS by DMA in pairs of two 16-token sub-blocks, two pairs ahead, into a ring of four
-//    stages (one barrier per pair).  The stage layout is the decode kernel's (8 x 8 chunks of
-//    16-byte granules, token rows of 40 granules here).  Scores on v_mfma_f32_16x16x32_bf16 (tokens
-//    on M, K = 192); the online softmax is lane-local in the decode kernel's way; P.V takes the two
-//    sub-blocks per v_mfma_f32_16x16x32_bf16 through a K permutation: both operands hold tokens
-//    4g .. 4g+3 of the first sub-block, then of the second, in lane group g (A by two transposed
-//    reads of V, B = the score registers).  The loop is software-pipelined by one pair (the
-//    exponentials and P.V of a pair follow the next pair's score MFMAs).  Pairs past a row's
-//    position are skipped; the diagonal pairs are masked per element.  The queries are prepared as
-//    they are loaded: q_nope scaled by scale * log2(e), RoPE(q_pe) at the row's position in fp64
-//    (the decode's table), both in bf16.  Each XCD takes its query tiles longest first.
-#include "mla_internal.h"
+// The expansion here (the attention, and the rotation of the queries' q_pe it reads, are in
+// prefill_attn.hip): per (sequence, 1,024 tokens, head) one workgroup computes K_nope and V of every token
+// (W_uk[h] and W_uv[h], 128 x 512 each, times the latent row) and copies its rope keys, writing rows
+// [K_nope | k_pe | V] (320 bf16, rounded once) per (sequence, head, token).  Over bf16 cache rows on
+// v_mfma_f32_32x32x16_bf16 with the W rows in registers and the tokens through an LDS ring; over FP8 rows
+// on v_mfma_f32_16x16x32_bf16 with the group scales applied per K group (the kernels below say how).
+#include "prefill_common.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kKV = DN + DR + DV;          // 320 values per expanded token row
-constexpr int kKVBytes = kKV * 2;          // 640
-constexpr int kGQ = kKV / 64;              // 5 granule groups (8 granules of 8 values) per token row
-constexpr int kSubBytes = 16 * kKVBytes;   // a 16-token sub-block in LDS: 2 x 5 chunks of 1 KiB
-constexpr int kPairBytes = 2 * kSubBytes;  // 32 tokens: one stage of the attention kernel's ring
-constexpr int kStages = 4;                 // 80 KiB of LDS: two attention workgroups per CU
-constexpr int kQTile = 128;                // query rows per attention workgroup (32 per wave)
 constexpr int kExpandTokens = kPrefillTokens;  // tokens per expansion workgroup (256 per wave)
 constexpr int kSubPerWave = kExpandTokens / 64;  // 16-token sub-tiles per wave
-constexpr float kMaxSlack = 8.f;           // lazy-rescale slack (log2 units), as in the decode
-
-// chunk length of sequence b, clamped to the launch bound; 0 for an inconsistent prefix sum
-__device__ __forceinline__ int chunk_of(const PrefillArgs& a, int b, int* first) {
-  const int c0 = a.cu_q_lens[b];
-  int n = a.cu_q_lens[b + 1] - c0;
-  if (c0 < 0 || n < 0 || c0 > a.total_q || n > a.total_q - c0) n = 0;
-  *first = c0;
-  return n < a.max_q_len ? n : a.max_q_len;
-}
-
-// maxima without the canonicalising moves that fmaxf puts before each operand (the scores are
-// MFMA results or -inf, never signalling NaNs)
-__device__ __forceinline__ float vmax3(float x, float y, float z) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
-  return r;
-}
-__device__ __forceinline__ float vmax(float x, float y) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
-  return r;
-}
-
-// acc + the two bf16 halves of x, in fp32 (v_dot2c_f32_bf16 against (1, 1)): the row sums are
-// taken over the same bf16 weights that the P.V MFMAs multiply
-__device__ __forceinline__ float add_pk_bf16(uint32_t x, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
-                                         acc, false);
-}
 
 }  // namespace
 
@@ -421,320 +370,6 @@ hipError_t launch_prefill_expand(PrefillArgs a, bool fp8, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------------------------------- attn
-
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char ring_mem[kStages * kPairBytes];
-
-  // workgroup -> (sequence, head, query tile).  Workgroups go to the 8 XCDs in turn (blockIdx % 8)
-  // and each XCD starts its own in blockIdx order.  The (sequence, head) pairs are dealt to the XCDs
-  // in turn (pair bh on XCD bh % 8), so that all query tiles of a pair share one L2, and each XCD
-  // takes its query tiles longest first across all of its pairs: the last to start are the
-  // shortest, and tiles of one rank, which start together, read the same keys at about the same time
-  const int nqt = (a.max_q_len + kQTile - 1) / kQTile;
-  const int nbh = a.batch * a.H;
-  const int nbx = (nbh + 7) >> 3;  // pairs per XCD (at most)
-  const int j = int(blockIdx.x >> 3);
-  const int bh = (j % nbx) * 8 + int(blockIdx.x & 7);
-  if (bh >= nbh || j >= nbx * nqt) return;
-  const int qt = nqt - 1 - j / nbx;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
-  int c0;
-  const int n = chunk_of(a, b, &c0);
-  const int r0 = qt * kQTile;
-  if (r0 >= n) return;  // uniform per workgroup: before any barrier
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15, g = lane >> 4;
-  const int lrow = lane & 7, lgr = lane >> 3;
-  const int ctx = clamp_ctx(a.seq_lens[b], n, a.max_seq_len);
-  const int p0 = ctx - n;  // position of chunk row 0
-  // this wave's rows: r0 + 32 w + 16 rt + r16, rt = 0, 1 (two 16-row tiles); rows past the chunk
-  // compute row n - 1 and are not stored
-  // (computed where it is used rather than held in registers through the loop)
-  auto p_row = [&](int rt) {
-    const int rw = r0 + 32 * w + 16 * rt + r16;
-    return p0 + (rw < n ? rw : n - 1);
-  };
-  const int lw = r0 + 32 * w + 31;
-  const int p_wave = p0 + (lw < n ? lw : n - 1);  // last position among the wave's rows
-  const int fw = r0 + 32 * w;
-  const int p_wmin = p0 + (fw < n ? fw : n - 1);  // first position among them
-  const int lg = r0 + kQTile - 1;
-  const int p_wg = p0 + (lg < n ? lg : n - 1);
-  const int npair = p_wg / 32 + 1;  // key pairs 0 .. npair - 1 (32 tokens each) seen by the workgroup
-
-  const char* kvb = reinterpret_cast<const char*>(a.kv + (int64_t(b) * a.H + h) * a.t_pad * kKV);
-  const char* zero = static_cast<const char*>(a.zero_block);  // >= 640 zero bytes
-  lds_char_t* const ring = (lds_char_t*)ring_mem;
-  // transfer of pair q into stage q % kStages: wave w moves tokens 32 q + 8 w .. + 7 (token group
-  // w % 2 of sub-block w / 2), one chunk of 8 granules per group gq (groups 0..2 hold K, 3..4 V);
-  // rows past the context read the zero block
-  auto issue = [&](int q) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        uint32_t(uintptr_t(ring + (q % kStages) * kPairBytes + (w >> 1) * kSubBytes + 1024 * kGQ * (w & 1))));
-    const int t = 32 * q + 8 * w + lrow;
-    const char* src = (t < ctx ? kvb + int64_t(t) * kKVBytes : zero) + 16 * lgr;
-#pragma unroll
-    for (int gq = 0; gq < kGQ; ++gq) dma16(src + 128 * gq, dst + 1024 * gq);
-  };
-  // stage of pair q, its address held in a VGPR (LDS reads then take constant offsets from it)
-  auto stage = [&](int q) {
-    uint32_t sa = uint32_t(uintptr_t(ring + (q % kStages) * kPairBytes));
-    asm volatile("" : "+v"(sa));
-    return (const lds_char_t*)uintptr_t(sa);
-  };
-
-  // per-lane LDS offsets inside a sub-block: score operand k (token r16, granule 4k + g) at
-  // sc_off + 512 k; transposed read of V tile jj (tokens 4g .. 4g+3, dims 16 jj + r16) at
-  // tr_off + 256 jj (V starts at granule 24: + 3072)
-  const int sc_off = 1024 * kGQ * (r16 >> 3) + 128 * g + 16 * (r16 & 7);
-  const int tr_off = 1024 * kGQ * (g >> 1) + 64 * (g & 1) + 128 * ((r16 >> 1) & 1) + 16 * (r16 >> 2) + 8 * (r16 & 1) +
-                     3072;
-
-  f32x4_t acc[2][8];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc[rt][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  // per row: the score MFMAs' start value nref = -msub (msub = the reference, 0 before the row has
-  // one) and the threshold above which a lane's maximum asks for a new reference (-inf before the
-  // row has one, else the slack); both change only with the reference
-  float nref[2] = {0.f, 0.f}, thr[2] = {-INFINITY, -INFINITY};
-
-  issue(0);
-  if (npair > 1) issue(1);
-
-  // query rows in registers: B operand of score MFMA k (granules 4k + g of row r16 of tile rt),
-  // prepared here: q_nope scaled by scale * log2(e), q_pe rotated in fp64 at the row's position
-  // (the decode's RoPE table) and scaled, both rounded to bf16 once
-  u32x4_t qreg[2][6];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const u32x4_t* qs =
-        reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) + (int64_t(c0 + p_row(rt) - p0) * a.H + h) * QW);
-    u32x4_t raw[6];
-#pragma unroll
-    for (int k = 0; k < 6; ++k) raw[k] = qs[4 * k + g];
-    const int pos = p_row(rt);
-    const bool ok = pos >= 0 && pos <= a.max_position;
-    double2 cs[2][4];
-#pragma unroll
-    for (int k = 4; k < 6; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cs[k - 4][e] = ok ? a.rope[int64_t(pos) * NPAIR + 4 * (4 * k + g - 16) + e] : double2{0.0, 0.0};
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qreg[rt][k][e] = uint32_t(f32_to_bf16(__uint_as_float(raw[k][e] << 16) * a.qscale)) |
-                         (uint32_t(f32_to_bf16(__uint_as_float(raw[k][e] & 0xffff0000u) * a.qscale)) << 16);
-#pragma unroll
-    for (int k = 4; k < 6; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float y0 = __builtin_nanf(""), y1 = __builtin_nanf("");
-        if (ok) {
-          const double x0 = __uint_as_float(raw[k][e] << 16), x1 = __uint_as_float(raw[k][e] & 0xffff0000u);
-          const double2 c = cs[k - 4][e];
-          y0 = float((x0 * c.x - x1 * c.y) * double(a.qscale));
-          y1 = float((x0 * c.y + x1 * c.x) * double(a.qscale));
-        }
-        qreg[rt][k][e] = uint32_t(f32_to_bf16(y0)) | (uint32_t(f32_to_bf16(y1)) << 16);
-      }
-  }
-
-  // the query loads are complete before the loop (the compiler cannot tell them from the transfers
-  // in flight and would otherwise wait for all of them inside it); the first tiles, issued above,
-  // land meanwhile
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int k = 0; k < 6; ++k) asm volatile("" ::"v"(qreg[rt][k]));
-
-  // Pairs q = 0, 1, ...: tokens 32 q .. 32 q + 31 (two 16-token sub-blocks), one per stage of a
-  // ring of four, moved two steps ahead; one barrier per step.  This wave's rows see pairs
-  // 0 .. nq - 1.  Software pipeline, so that the VALU work of one pair runs under the MFMAs of
-  // another inside the wave: the step of pair q issues its score MFMAs interleaved with the
-  // exponentials of pair q - 1, reads pair q - 1's values, then issues pair q - 1's P.V MFMAs
-  // interleaved with pair q's maxima, and ends with pair q's reference check.  Only pair q - 1's
-  // exponents (sv, re-based on the current reference) pass between steps; its values stay in its
-  // stage, which the transfer of pair q + 3 replaces only after the barrier of step q + 1.
-  const int nq = p_wave / 32 + 1;  // <= npair
-  f32x4_t sv[2][2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) sv[rt][0] = sv[rt][1] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  u32x4_t kw[3][2];  // key operands: K slice k (granules 4k + g of token r16, both sub-blocks) in kw[k % 3]
-  u32x4_t vt[8];     // A operands of P.V: V tile jj, tokens of both sub-blocks (K permutation)
-  auto ld_slice = [&](const lds_char_t* sub0, int k) {
-    kw[k % 3][0] = *(const lds_u32x4_t*)(sub0 + sc_off + 512 * k);
-    kw[k % 3][1] = *(const lds_u32x4_t*)(sub0 + kSubBytes + sc_off + 512 * k);
-  };
-  auto ld_vt = [&](const lds_char_t* sub0) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub0 + tr_off + 256 * jj));
-      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sub0 + kSubBytes + tr_off + 256 * jj));
-      const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0), a1 = __builtin_bit_cast(u32x2_t, v1);
-      vt[jj] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-    }
-  };
-  // scores of a pair whose slices 0..2 are in the window; the MFMAs start at -msub, so that they
-  // produce the exponents s - m directly; slices 3..5 are read as 0..2 are consumed
-  auto scores = [&](const lds_char_t* sub0, f32x4_t (&sc)[2][2]) {
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const f32x4_t c0 = f32x4_t{nref[rt], nref[rt], nref[rt], nref[rt]};
-        sc[rt][0] = mfma32v(kw[k % 3][0], qreg[rt][k], k == 0 ? c0 : sc[rt][0]);
-        sc[rt][1] = mfma32v(kw[k % 3][1], qreg[rt][k], k == 0 ? c0 : sc[rt][1]);
-      }
-      if (k < 3) ld_slice(sub0, k + 3);
-    }
-  };
-  // p = exp2(sv) of the pending pair (exp2(-inf) = 0), packed to bf16 in the order of the K
-  // permutation
-  auto exps = [&](u32x4_t (&pb)[2]) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(sv[rt][0][e]);
-        p[4 + e] = __builtin_amdgcn_exp2f(sv[rt][1][e]);
-      }
-      pb[rt] = u32x4_t{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
-                       cvt_pk_bf16(p[6], p[7])};
-    }
-  };
-  // P.V of the pending pair (K = its 32 tokens; one read of V feeds both row tiles), and its row sums
-  auto pv = [&](const u32x4_t (&pb)[2]) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) acc[rt][jj] = mfma32v(vt[jj], pb[rt], acc[rt][jj]);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-      lsum[rt] = add_pk_bf16(pb[rt][3], add_pk_bf16(pb[rt][2], add_pk_bf16(pb[rt][1], add_pk_bf16(pb[rt][0], lsum[rt]))));
-  };
-  // lane (r16, g) holds s - msub for tokens 4g + e of each sub-block, row r16 of each tile.  A pair
-  // wholly visible to every row of the wave (all but the diagonal pairs) needs no mask
-  auto mask = [&](f32x4_t (&sc)[2][2], int tpair) {
-    if (tpair + 31 <= p_wmin) return;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int lim = p_row(rt) - tpair - 4 * g;  // token 4g + e of the pair visible iff e <= lim
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[rt][0][e] = e <= lim ? sc[rt][0][e] : -INFINITY;
-        sc[rt][1][e] = 16 + e <= lim ? sc[rt][1][e] : -INFINITY;
-      }
-    }
-  };
-  auto lane_max = [&](const f32x4_t (&sc)[2][2], float (&ml)[2]) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-      ml[rt] = vmax(vmax3(sc[rt][0][0], sc[rt][0][1], sc[rt][0][2]),
-                    vmax3(vmax3(sc[rt][0][3], sc[rt][1][0], sc[rt][1][1]), sc[rt][1][2], sc[rt][1][3]));
-  };
-  // only the lane's own maximum is compared with the reference; the row maximum is reduced across
-  // the lane groups only when some score passes it by the slack or the row has no reference yet
-  // (the reference, moved only there, stays the same in the four lanes of a row)
-  auto rebase = [&](const f32x4_t (&sc)[2][2], const float (&ml)[2]) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      sv[rt][0] = sc[rt][0];
-      sv[rt][1] = sc[rt][1];
-      if (__any(ml[rt] > thr[rt])) {
-        const float msub = -nref[rt];
-        float mb = fmaxf(ml[rt], __shfl_xor(ml[rt], 16, 64));
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float mn = fmaxf(m[rt], mb + msub);  // -inf only for a row with nothing visible yet
-        if (mn != -INFINITY) {
-          const float alpha = (m[rt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mn);
-          lsum[rt] *= alpha;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) acc[rt][jj] *= alpha;
-          const float d = msub - mn;  // re-base the exponents on the new reference
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[rt][0][e] += d;
-            sv[rt][1][e] += d;
-          }
-          m[rt] = mn;
-          nref[rt] = -mn;
-          thr[rt] = kMaxSlack;
-        }
-      }
-    }
-  };
-  for (int q = 0; q < npair; ++q) {
-    if (q + 1 < npair)
-      wait_vmcnt<kGQ>();  // pair q has landed (pair q + 1 may still be in flight)
-    else
-      wait_vmcnt<0>();
-    lds_barrier();  // every wave's part of pair q has landed; every wave is done with step q - 1
-    if (q + 2 < npair) issue(q + 2);  // into the stage of pair q - 2
-    const lds_char_t* const cur = stage(q);
-    const lds_char_t* const prv = stage(q + kStages - 1);  // pair q - 1
-    if (q < nq) {
-#pragma unroll
-      for (int k = 0; k < 3; ++k) ld_slice(cur, k);
-      f32x4_t sc[2][2];
-      float ml[2];
-      u32x4_t pb[2];
-      scores(cur, sc);
-      exps(pb);
-      // before pair 0 the pending exponents are -inf: its P.V adds exact zeros times this pair's
-      // (finite) values
-      ld_vt(q == 0 ? cur : prv);
-      mask(sc, 32 * q);
-      pv(pb);
-      lane_max(sc, ml);
-      rebase(sc, ml);
-    } else if (q == nq) {
-      u32x4_t pb[2];
-      exps(pb);
-      ld_vt(prv);
-      pv(pb);
-    }
-  }
-  if (nq == npair) {  // the last pair
-    u32x4_t pb[2];
-    exps(pb);
-    ld_vt(stage(npair - 1));
-    pv(pb);
-  }
-
-  // out = acc / l for the rows of the chunk; lane (r16, g) holds dims 16 jj + 4g .. + 3
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    float l = lsum[rt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const int rw = p_row(rt) - p0;  // the row itself where it is one of the chunk's
-    if (r0 + 32 * w + 16 * rt + r16 < n) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(c0 + rw) * a.H + h) * DV + 4 * g;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        *reinterpret_cast<u32x2_t*>(o + 16 * jj) = u32x2_t{cvt_pk_bf16(acc[rt][jj][0] * inv, acc[rt][jj][1] * inv),
-                                                          cvt_pk_bf16(acc[rt][jj][2] * inv, acc[rt][jj][3] * inv)};
-    }
-  }
-}
-
-hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s) {
-  const int64_t nbx = (int64_t(a.batch) * a.H + 7) / 8;
-  const int64_t grid = 8 * nbx * ((a.max_q_len + kQTile - 1) / kQTile);
-  if (grid > 0x7ffffff0) return hipErrorInvalidValue;
-  a.units = int32_t(grid);
-  launch(prefill_attn_kernel, dim3(int(grid)), dim3(256), 0, s, a);  // 80 KiB of LDS: two workgroups per CU
-  return hipGetLastError();
-}
+hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s) { return launch_prefill_attn32(a, s); }
 
 }  // namespace mla
