@@ -103,6 +103,9 @@ __device__ __forceinline__ void merge_rows4(const CombineArgs& a, int h, int row
       const int rowc = row < a.n_q ? row : a.n_q - 1;
       rq[rr] = (rowc % a.q_len) * a.H + h;  // row within the sequence
       pt[rr] = a.piece_tbl[(rowc / a.q_len) * a.n_grp + rq[rr] / a.rows_per_piece];
+      // the same for every lane: kept in scalar registers, and so are the partial addresses below
+      pt[rr].x = __builtin_amdgcn_readfirstlane(pt[rr].x);
+      pt[rr].y = __builtin_amdgcn_readfirstlane(pt[rr].y);
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -123,6 +126,12 @@ __device__ __forceinline__ void merge_rows4(const CombineArgs& a, int h, int row
     }
   }
   const int ns_max = __builtin_amdgcn_readfirstlane(max(max(ns[0], ns[1]), max(ns[2], ns[3])));
+  // a chunk's 16 (m, l) pairs and scales: lane l loads those of row (l / 4) % 4, partial j0 + l % 4, and
+  // they reach every lane by readlane (scalar registers instead of 48 vector registers per chunk)
+  const int lr = (lane >> 2) & 3, lj = lane & 3;
+  const int64_t lbase = lr == 0 ? base[0] : lr == 1 ? base[1] : lr == 2 ? base[2] : base[3];
+  const int lstride = lr == 0 ? stride[0] : lr == 1 ? stride[1] : lr == 2 ? stride[2] : stride[3];
+  const int lns = lr == 0 ? ns[0] : lr == 1 ? ns[1] : lr == 2 ? ns[2] : ns[3];
   float M[4], den[4], o[4][8];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -135,15 +144,24 @@ __device__ __forceinline__ void merge_rows4(const CombineArgs& a, int h, int row
     float2 ml[4][4];
     float ps[4][4];
     u32x4_t vo[4][4];  // fp16 o / ps of channels 8 lane .. 8 lane + 7
+    const int64_t lpi = lbase + int64_t(min(j0 + lj, max(lns - 1, 0))) * lstride;
+    const float2 lml = a.part_ml[lpi];
+    const float lps = a.part_scale[lpi];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int jc = min(j0 + jj, max(ns[rr] - 1, 0));
         const int64_t pi = base[rr] + int64_t(jc) * stride[rr];
-        ml[rr][jj] = a.part_ml[pi];
-        ps[rr][jj] = a.part_scale[pi];
         vo[rr][jj] = *reinterpret_cast<const u32x4_t*>(a.part_o16 + pi * DC + 8 * lane);
+      }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        ml[rr][jj].x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lml.x), 4 * rr + jj));
+        ml[rr][jj].y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lml.y), 4 * rr + jj));
+        ps[rr][jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lps), 4 * rr + jj));
       }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -249,8 +267,98 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   }
 }
 
+// Many rows per head (the wide and multi-token shapes): one workgroup per (head, RW query rows) with RW / 4
+// waves, so that W_uv[h] is read once per RW rows instead of once per 16.  Wave w merges rows 4w .. 4w + 3 as
+// above.  The product out^T[v, n] = sum_c W_uv[h][v, c] o_lat^T[c, n] then runs on v_mfma_f32_32x32x16_bf16
+// with the 512 channels c cut into KQ = RW / 16 parts: wave w takes output channels 32 (w % 4) .. + 31 over
+// channel part w / 4, for every 32-row column tile, on the hi and on the lo half of o_lat.  The parts' fp32
+// sums meet in LDS, are added in part order and stored as bf16, 16 bytes per lane.
+template <int RW>
+__global__ __launch_bounds__(RW * 16) void combine_rows_kernel(CombineArgs a) {
+  constexpr int KQ = RW / 16, NT = RW / 32, NKS = 32 / KQ;  // channel parts, column tiles, K steps per wave
+  constexpr int kRed = DV + 4;  // floats per row of the parts' sums (rows start 16 bytes apart in bank terms)
+  constexpr int kLdsO = 2 * RW * 64 * 16;  // the hi and lo tiles: RW rows of 64 granules of 16 bytes each
+  constexpr int kLdsR = KQ * RW * kRed * 4;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsO > kLdsR ? kLdsO : kLdsR];
+  u32x4_t* ohi = reinterpret_cast<u32x4_t*>(lds);  // granule c of row r at r * 64 + (c ^ (r % 16))
+  u32x4_t* olo = ohi + RW * 64;
+  float* red = reinterpret_cast<float*>(lds);  // [KQ][RW][kRed], after the product
+
+  const int h = blockIdx.x, r0 = blockIdx.y * RW;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vt = w & 3, kq = w >> 2, hf = lane >> 5;
+
+  const uint16_t* wuv_h = static_cast<const uint16_t*>(a.W_uv) + int64_t(h) * DV * DC;
+  const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(wuv_h + int64_t(32 * vt + (lane & 31)) * DC) + 2 * NKS * kq;
+  u32x4_t wf[NKS];
+  {
+    uint32_t hw[4][4], lw[4][4];
+    merge_rows4(a, h, r0 + 4 * w, lane, hw, lw);
+    // the W_uv fragments, issued once the merge's registers are free (their latency overlaps the
+    // barrier): the A operand of K step ks is row 32 vt + lane % 32, channels 16 (kq NKS + ks) + 8 hf .. + 7
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) wf[ks] = wrow[2 * ks + hf];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 4 * w + rr;
+      const int gi = r * 64 + (lane ^ (r & 15));
+      ohi[gi] = u32x4_t{hw[rr][0], hw[rr][1], hw[rr][2], hw[rr][3]};
+      olo[gi] = u32x4_t{lw[rr][0], lw[rr][1], lw[rr][2], lw[rr][3]};
+    }
+  }
+  __syncthreads();
+
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int g = 2 * (NKS * kq + ks) + hf;  // the B operand's granule: the same channels as wf[ks]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = 32 * nt + (lane & 31);
+      const int gi = n * 64 + (g ^ (n & 15));
+      acc[nt] = mfma32x32(wf[ks], ohi[gi], acc[nt]);
+      acc[nt] = mfma32x32(wf[ks], olo[gi], acc[nt]);
+    }
+  }
+  __syncthreads();  // the tiles' memory takes the parts' sums
+
+  // lane holds column n = 32 nt + lane % 32 (a query row) and, in register 4q + i, output channel
+  // 32 vt + 8q + 4 hf + i
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float* dst = red + (kq * RW + 32 * nt + (lane & 31)) * kRed + 32 * vt + 4 * hf;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4_t*>(dst + 8 * q) = f32x4_t{acc[nt][4 * q], acc[nt][4 * q + 1], acc[nt][4 * q + 2],
+                                                          acc[nt][4 * q + 3]};
+  }
+  __syncthreads();
+
+  // thread: row n = tid / 16, output channels 8 (tid % 16) .. + 7
+  const int n = tid >> 4, v0 = 8 * (tid & 15);
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < KQ; ++p) {
+    const float* src = red + (p * RW + n) * kRed + v0;
+    s0 += *reinterpret_cast<const f32x4_t*>(src);
+    s1 += *reinterpret_cast<const f32x4_t*>(src + 4);
+  }
+  const int row = r0 + n;
+  if (row < a.n_q) {
+    uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.H + h) * DV + v0;
+    *reinterpret_cast<u32x4_t*>(out) = u32x4_t{cvt_pk_bf16(s0[0], s0[1]), cvt_pk_bf16(s0[2], s0[3]),
+                                                 cvt_pk_bf16(s1[0], s1[1]), cvt_pk_bf16(s1[2], s1[3])};
+  }
+}
+
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s) {
-  if (bf16) {
+  if (bf16 && a.rows_wg == 64) {
+    launch(combine_rows_kernel<64>, dim3(a.H, (a.n_q + 63) / 64), dim3(64 * 16), 0, s, a);
+  } else if (bf16 && a.rows_wg == 32) {
+    launch(combine_rows_kernel<32>, dim3(a.H, (a.n_q + 31) / 32), dim3(32 * 16), 0, s, a);
+  } else if (bf16) {
     dim3 grid(a.H, (a.n_q + 15) / 16, a.v_parts);
     launch(combine_bf16_kernel, dim3(grid), dim3(256), 0, s, a);
   } else {

@@ -512,9 +512,11 @@ mla_status decode_launch(mla_ctx* ctx, const DecodePlan& pl, const DecodeWs& ws,
   {
     // output channels split over 4 workgroups only when the (head, 16 rows) grid is small
     const int v_parts = int64_t(H) * ((n_q + 15) / 16) >= 2 * ctx->cu_count ? 1 : 4;
+    // 64 rows per workgroup (W_uv read once per 64 rows) once that alone gives every CU a workgroup
+    const int rows_wg = int64_t(H) * ((n_q + 63) / 64) >= ctx->cu_count ? 64 : 16;
     CombineArgs ca{ws.part_acc, reinterpret_cast<const uint16_t*>(ws.part_acc), ws.part_ml, ws.part_scale, seq_lens,
                    max_seq_len, q_len, n_q, H, pl.sb, pl.n_split, ctx->W_uv, ctx->W_uvT, out,
-                   t32 ? ws.piece_tbl : nullptr, 32 * t32, t32 ? pl.n_rt / t32 : 0, v_parts};
+                   t32 ? ws.piece_tbl : nullptr, 32 * t32, t32 ? pl.n_rt / t32 : 0, v_parts, rows_wg};
     ProfScope ps(ctx, MLA_K_COMBINE, s);
     e = launch_combine(ctx->bf16, ca, s);
   }

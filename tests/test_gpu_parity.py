@@ -59,6 +59,12 @@ SMALL = [
     ("ctx_eq_qlen4", lambda: W.custom("edge4", "bf16", 16, [4, 16, 17, 20], q_len=4, seed=10)),
     ("h48_q2_bf16", lambda: W.custom("h48", "bf16", 48, [40, 300, 77], q_len=2, seed=11)),
     ("h32_q1_bf16", lambda: W.custom("h32", "bf16", 32, [33, 200, 517], q_len=1, seed=12)),
+    # enough (head, 64-row) tiles to fill the device: the 64-row combine, by piece and by split, with a
+    # ragged last tile (130 and 1,000 rows)
+    ("rows64_h128_q2", lambda: W.custom("r64", "bf16", 128, [2 + (37 * i) % 400 for i in range(65)], q_len=2,
+                                        seed=13)),
+    ("rows64_h16_b1000", lambda: W.custom("r64s", "bf16", 16, [1 + (53 * i) % 150 for i in range(1000)], q_len=1,
+                                          seed=14)),
 ]
 
 
