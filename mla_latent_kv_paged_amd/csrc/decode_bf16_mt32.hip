@@ -52,8 +52,6 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5;    // lane half: K block of the MFMA operands
-  const int r32 = lane & 31;  // row of the tile (N index) / token of a score operand (M index)
   const int n_grp = a.n_rt / T;  // tile groups per sequence (n_rt = tiles of 32 rows)
   const int n_wg = a.units;
 
@@ -117,13 +115,6 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   lds_char_t* const stages = (lds_char_t*)stage_mem;
   const char* cache = static_cast<const char*>(a.cache);
   const char* zero = static_cast<const char*>(a.zero_block);
-  const int lrow = lane & 7, lgr = lane >> 3;
-  // per-lane LDS offsets.  Score operand k (token r32, granule 2k + h): 9216 (r32 / 8) + 128 h +
-  // 16 (r32 % 8) + 256 k.  Transposed read of K step s, half r, channel tile jt (tokens 16s + 8r +
-  // 4 hh + li / 4, channels 32 jt + 16 cb + 4 (li % 4)): the base below + 18432 s + 9216 r + 512 jt.
-  const int sc_off = 9216 * (r32 >> 3) + 128 * h + 16 * (r32 & 7);
-  const int G = lane >> 4, li = lane & 15;
-  const int tr_off = 128 * (2 * (G & 1) + ((li >> 1) & 1)) + 64 * (G >> 1) + 16 * (li >> 2) + 8 * (li & 1);
   auto stage_addr = [&](int i) { return uint32_t(uintptr_t(stages + (i % NSTAGE) * kStageBytes)); };
 
   // row maximum over both lane halves (lanes l and l ^ 32 hold the same row)
@@ -134,6 +125,20 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
 
   // ---- one piece: steps k0..k1-1 of stream (b, grp), partial under id pid
   auto piece = [&](const int b, const int grp, const int k0, const int k1, const int pid) {
+    // the per-lane values are formed again for each piece from an opaque thread index: kept across the
+    // piece loop they would be spilled (the step loops take every register)
+    int tid_p = int(threadIdx.x);
+    asm volatile("" : "+v"(tid_p));
+    const int lane = tid_p & 63;
+    const int h = lane >> 5;    // lane half: K block of the MFMA operands
+    const int r32 = lane & 31;  // row of the tile (N index) / token of a score operand (M index)
+    const int lrow = lane & 7, lgr = lane >> 3;
+    // per-lane LDS offsets.  Score operand k (token r32, granule 2k + h): 9216 (r32 / 8) + 128 h +
+    // 16 (r32 % 8) + 256 k.  Transposed read of K step s, half r, channel tile jt (tokens 16s + 8r +
+    // 4 hh + li / 4, channels 32 jt + 16 cb + 4 (li % 4)): the base below + 18432 s + 9216 r + 512 jt.
+    const int sc_off = 9216 * (r32 >> 3) + 128 * h + 16 * (r32 & 7);
+    const int G = lane >> 4, li = lane & 15;
+    const int tr_off = 128 * (2 * (G & 1) + ((li >> 1) & 1)) + 64 * (G >> 1) + 16 * (li >> 2) + 8 * (li & 1);
     const int ctx = clamp_ctx(a.seq_lens[b], a.q_len, a.max_seq_len);
     const int nblk = (ctx + BLK - 1) / BLK;
     const int kb0 = 2 * k0;
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
     // stall the barrier that precedes each transfer); nb <= kIdCap by the launch
     {
       const int* bt_row = a.block_table + int64_t(b) * a.bt_stride + kb0;
-      for (int e = int(threadIdx.x); e < nb; e += T * 64) ids_lds[e] = bt_row[e];
+      for (int e = tid_p; e < nb; e += T * 64) ids_lds[e] = bt_row[e];
     }
     lds_barrier();
     // block ids of step i; the second is clamped into the piece (its lanes are masked when the
@@ -199,10 +204,17 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
       for (int c = 0; c < CPW; ++c) put(x, c);
     };
 
+    // zeroed in place in the AGPRs (a zero tile built in VGPRs would be kept, or spilled, across the
+    // pieces)
     f32x16_t acc[16];
 #pragma unroll
     for (int jt = 0; jt < 16; ++jt) {
-      acc[jt] = f32x16_t{};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float z;
+        asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(z));
+        acc[jt][e] = z;
+      }
       asm volatile("" : "+a"(acc[jt]));
     }
     float m = -INFINITY, lsum = 0.f;
