@@ -306,6 +306,7 @@ def prefill_main(args):
     from mla_latent_kv_paged_amd import MLAContext, K_PF_EXPAND, K_PF_ATTN
     from workloads import mla_inputs as W
     B, S = args.pf_batch, args.pf_len
+    fp8 = args.cache == "fp8"
     w = W.custom(f"prefill_b{B}_s{S}", "bf16", 16, [S] * B, q_len=1, seed=1240)
     chunks = [S] * B
 
@@ -315,9 +316,12 @@ def prefill_main(args):
     def dev_i(x):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
 
-    ctx = MLAContext(dev(w.kv_b_proj()), None, num_heads=16, dtype="bf16", rms_eps=w.eps, rope_theta=w.theta,
-                     max_q_tokens=B, max_batch=B, max_position=S, max_seq_len=S)
-    pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ctx = MLAContext(dev(w.kv_b_proj()), None, num_heads=16, dtype="fp8" if fp8 else "bf16", rms_eps=w.eps,
+                     rope_theta=w.theta, max_q_tokens=B, max_batch=B, max_position=S, max_seq_len=S)
+    if fp8:  # e4m3 rows of 656 bytes (mla_cache_write quantises)
+        pool = torch.zeros((w.n_blocks, 16, 1, 656), dtype=torch.uint8, device="cuda")
+    else:
+        pool = torch.full((w.n_blocks, 16, 1, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
     for b in range(B):
         c, k = w.history(b)
         ctx.cache_write(dev(c), dev(k), dev_i(np.arange(S)), dev_i(w.slots(b, 0, S)), pool)
@@ -363,7 +367,8 @@ def prefill_main(args):
            "data": "synthetic (seeded N(0,1) activations, N(0,1/512) kv_b_proj)",
            "config": {"workload": f"prefill_b{B}_s{S}: {B} sequences, each a fresh chunk of {S} tokens, 16 heads, "
                                   "kv_lora_rank 512 + rope 64, naive form (K/V expanded once per chunk)",
-                      "batch": B, "chunk": S, "num_heads": 16},
+                      "batch": B, "chunk": S, "num_heads": 16,
+                      "cache": "fp8 e4m3, 656 B per token (MLA_BF16_FP8)" if fp8 else "bf16"},
            "flops": {"attention": fa, "expansion": fe}, "kernels_us": kus,
            "roofline": {"bound": "mfma", "achieved": round(fa / (kus["attn"] * 1e-6) / 1e12, 2),
                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -371,7 +376,7 @@ def prefill_main(args):
                         "traffic": prefill_traffic(args),
                         "kernel": "prefill_attn32_kernel (with the q_pe rotation before it)",
                         "expand_tflops": round(fe / (kus["expand"] * 1e-6) / 1e12, 2)}}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:  # the oracle's sample is of the bf16 rows
         res["cpu_baseline"] = prefill_cpu_baseline(w)
     ctx.free()
     print(json.dumps(res), flush=True)

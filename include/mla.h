@@ -269,7 +269,7 @@ mla_status mla_layer_decode_step(mla_ctx* ctx, const void* hidden, const int32_t
  * Sequence b's n_b = cu_q_lens[b+1] - cu_q_lens[b] new tokens sit at positions ctx_b - n_b ..
  * ctx_b - 1 and must already be in the cache (mla_cache_write), as for mla_decode.  bf16 contexts
  * (MLA_BF16 and MLA_BF16_FP8) only; over FP8 rows the latent values are the dequantised ones,
- * code x group scale, as in mla_decode.
+ * code x group scale, here rounded once to bf16 (the decode applies the scales to its fp32 results).
  *
  *  q           device bf16 [total_q, H, dn + dr], un-rotated queries, rows in sequence order
  *  cu_q_lens   device int32 [batch + 1], prefix sums of the chunk lengths (cu_q_lens[0] = 0,
@@ -292,8 +292,9 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
 
 /* Bytes of workspace mla_prefill needs for `batch` sequences of contexts up to max_seq_len tokens
  * and total_q new tokens: the expanded rows [K_nope | k_pe | V], batch * H * ceil1024(max_seq_len)
- * * 320 bf16, then the rotated q_pe, total_q * H * 64 bf16.  MLA_EINVAL for a null pointer or a
- * size < 1. */
+ * * 320 bf16, then the rotated q_pe, total_q * H * 64 bf16, then, for an FP8 cache (MLA_BF16_FP8),
+ * the context rows dequantised to bf16, batch * ceil1024(max_seq_len) * 576 bf16.  MLA_EINVAL for a
+ * null pointer or a size < 1. */
 mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t total_q, int32_t max_seq_len,
                                       size_t* bytes);
 

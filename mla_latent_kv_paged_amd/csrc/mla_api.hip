@@ -718,7 +718,8 @@ mla_status mla_prefill_workspace_size(const mla_ctx* ctx, int32_t batch, int32_t
   if (!ctx || !bytes || batch < 1 || total_q < 1 || max_seq_len < 1) return MLA_EINVAL;
   const int64_t kv = int64_t(batch) * ctx->cfg.num_heads * prefill_tpad(max_seq_len) * (DN + DR + DV) * 2;
   const int64_t qr = int64_t(total_q) * ctx->cfg.num_heads * DR * 2;  // the rotated q_pe
-  *bytes = size_t(kv + qr);
+  const int64_t lat = ctx->fp8 ? int64_t(batch) * prefill_tpad(max_seq_len) * ROW * 2 : 0;  // dequantised rows
+  *bytes = size_t(kv + qr + lat);
   return MLA_OK;
 }
 
@@ -760,6 +761,7 @@ mla_status mla_prefill(mla_ctx* ctx, const void* q, const int32_t* cu_q_lens, in
   pa.W_uv = static_cast<const uint16_t*>(ctx->W_uv);
   pa.kv = reinterpret_cast<uint16_t*>(ws);
   pa.qpe = reinterpret_cast<uint16_t*>(ws + int64_t(batch) * cf.num_heads * prefill_tpad(max_seq_len) * (DN + DR + DV) * 2);
+  pa.lat = ctx->fp8 ? pa.qpe + int64_t(total_q) * cf.num_heads * DR : nullptr;
   pa.out = out;
   hipError_t e;
   {

@@ -145,6 +145,7 @@ struct PrefillArgs {
   const uint16_t* W_uv;        // [H, DV, DC]
   uint16_t* kv;
   uint16_t* qpe;               // [total_q, H, DR] bf16: RoPE(q_pe) at the rows' positions (written by the prep)
+  uint16_t* lat;               // FP8 cache: [batch, t_pad, ROW] bf16 rows dequantised from it (else null)
   void* out;                   // [total_q, H, DV] bf16
   int32_t units;               // work items of the kernel being launched
 };
@@ -214,7 +215,7 @@ hipError_t launch_decode(bool bf16, const DecodeArgs& a, int waves, hipStream_t 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 // FP8 cache rows (kFp8Row bytes), 16-row tiles; every H multiple of 16 and every q_len
 hipError_t launch_decode_fp8(const DecodeArgs& a, int waves, hipStream_t s);
-// fp8: the cache holds FP8 rows (kFp8Row bytes) instead of bf16 rows
+// fp8: the cache holds FP8 rows (kFp8Row bytes) instead of bf16 rows; they are first dequantised into a.lat
 hipError_t launch_prefill_expand(PrefillArgs a, bool fp8, hipStream_t s);
 hipError_t launch_prefill_attn(PrefillArgs a, hipStream_t s);
 hipError_t launch_prefill_attn32(PrefillArgs a, hipStream_t s);

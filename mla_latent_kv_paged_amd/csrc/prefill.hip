@@ -13,9 +13,10 @@
 // The expansion here (the attention, and the rotation of the queries' q_pe it reads, are in
 // prefill_attn.hip): per (sequence, 1,024 tokens, head) one workgroup computes K_nope and V of every token
 // (W_uk[h] and W_uv[h], 128 x 512 each, times the latent row) and copies its rope keys, writing rows
-// [K_nope | k_pe | V] (320 bf16, rounded once) per (sequence, head, token).  Over bf16 cache rows on
-// v_mfma_f32_32x32x16_bf16 with the W rows in registers and the tokens through an LDS ring; over FP8 rows
-// on v_mfma_f32_16x16x32_bf16 with the group scales applied per K group (the kernels below say how).
+// [K_nope | k_pe | V] (320 bf16, rounded once) per (sequence, head, token), on v_mfma_f32_32x32x16_bf16 with
+// the W rows in registers and the tokens through an LDS ring.  Over an FP8 cache the context rows are
+// first dequantised to bf16 rows (code x group scale, rounded once) in the workspace, which the same
+// expansion then reads in place of the cache.
 #include "prefill_common.h"
 
 namespace mla {
@@ -85,6 +86,8 @@ __device__ __forceinline__ void expand_body(const PrefillArgs& a, char* smem, in
   const char* cache = static_cast<const char*>(a.cache);
   const char* zero = static_cast<const char*>(a.zero_block);  // >= 1,152 zero bytes
   const int* bt = a.block_table + int64_t(b) * a.bt_stride;
+  // over an FP8 cache: the sequence's dequantised rows, token t at row t (no block table)
+  const char* lat = a.lat ? reinterpret_cast<const char*>(a.lat + int64_t(b) * a.t_pad * ROW) : nullptr;
   char* kvrow0 = reinterpret_cast<char*>(a.kv + (int64_t(b) * a.H + h) * a.t_pad * kKV);
   lds_char_t* const lds = (lds_char_t*)smem;
   lds_char_t* const outl = lds + kXNS * kXStage;
@@ -101,16 +104,18 @@ __device__ __forceinline__ void expand_body(const PrefillArgs& a, char* smem, in
       const int t = 4 * wv + rr;
       const int tok = t0 + kXTok * k + t;
       const int phys = __builtin_amdgcn_readlane(ids, (kXTok * k + t) >> 4 & 63);  // k < nst: no wrap
-      const bool ok = k < nst && tok < ctx && unsigned(phys) < unsigned(a.num_blocks);
-      const char* row = ok ? cache + (int64_t(phys) * BLK + tok % BLK) * (ROW * 2) : zero;
+      const bool ok = k < nst && tok < ctx && (lat || unsigned(phys) < unsigned(a.num_blocks));
+      const char* row = ok ? (lat ? lat + int64_t(tok) * (ROW * 2) : cache + (int64_t(phys) * BLK + tok % BLK) * (ROW * 2))
+                           : zero;
       dma16(row + 16 * (lane ^ (t & 15)), st + t * (DC * 2));
     }
     if constexpr (PART == 0) {  // lane -> token 8 w4 + lane / 8, granule lane % 8 of its rope values
       const int t = 8 * w4 + (lane >> 3);
       const int tok = t0 + kXTok * k + t;
       const int phys = __shfl(ids, (kXTok * k + t) >> 4 & 63, 64);
-      const bool ok = k < nst && tok < ctx && unsigned(phys) < unsigned(a.num_blocks);
-      const char* row = ok ? cache + (int64_t(phys) * BLK + tok % BLK) * (ROW * 2) : zero;
+      const bool ok = k < nst && tok < ctx && (lat || unsigned(phys) < unsigned(a.num_blocks));
+      const char* row = ok ? (lat ? lat + int64_t(tok) * (ROW * 2) : cache + (int64_t(phys) * BLK + tok % BLK) * (ROW * 2))
+                           : zero;
       dma16(row + DC * 2 + 16 * (lane & 7), st + kXLat + 1024 * w4);
     }
   };
@@ -210,163 +215,61 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     expand_body<0>(a, smem, b, h, ck, ctx, wv);
 }
 
-// The expansion over FP8 rows (656 bytes: latent codes, bf16 rope values, four fp32 group scales;
-// mla_cache_write), on v_mfma_f32_16x16x32_bf16 with the 128 output dimensions on M and 16 tokens on N.
-// Every e4m3 value is a bf16 value, so the codes are the MFMA's B operand exactly, and the K steps of
-// each group of 128 channels accumulate apart; the group's tile is then added to the output times that
-// token's group scale (a lane holds one token: one scale per lane), in fp32.  (On the 32x32x16 shape the
-// two accumulator sets of the bf16 kernel's tile do not fit beside the register ring.)  128 KiB of LDS:
-// one workgroup, one wave per SIMD, per CU.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_expand_fp8_kernel(PrefillArgs a) {
-  constexpr int kRowBytes = kFp8Row;  // one cache row
-  constexpr int kRopeOff = DC;        // its rope values (bf16)
-  // W_uk[h] or W_uv[h]: 128 rows of 512 values; granule c (8 values) of row r at slot c ^ (r % 16)
-  __shared__ __attribute__((aligned(16))) char wl[DN * DC * 2];
-  static_assert(DN == DV, "one staging buffer for both parts");
-  const int nck = a.t_pad / kExpandTokens;
-  const int per_xcd = (a.units + 7) >> 3;  // XCD-contiguous units, as in prefill_expand_kernel
-  int u = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
-  if (u >= a.units) return;
-  const int part = u & 1;  // 0: K (W_uk, also the rope keys), 1: V (W_uv)
-  u >>= 1;
-  const int h = u % a.H;
-  u /= a.H;
-  const int ck = u % nck;
-  const int b = u / nck;
-  if (b >= a.batch) return;
+// Over an FP8 cache (rows of 656 bytes: 512 e4m3 codes, 64 bf16 rope values, four fp32 group scales;
+// mla_cache_write): the context rows of each sequence are first dequantised into lat [batch, t_pad, 576] bf16,
+// code x its group's scale in fp32 rounded once to nearest even, the rope values as stored.  Rows past the
+// context are not written (the expansion reads the zero block there); a row of an invalid block id becomes
+// zeros, as the bf16 path reads such a row from the zero block.  Grid (t_pad / 32, batch): four waves of
+// eight tokens, lane l converting codes 8 l .. 8 l + 7 of each token; all loads are issued first.
+__global__ __launch_bounds__(256) void prefill_dequant_fp8_kernel(PrefillArgs a) {
+  const int b = blockIdx.y;
   int c0;
   const int n = chunk_of(a, b, &c0);
   if (n == 0) return;
   const int ctx = clamp_ctx(a.seq_lens[b], n, a.max_seq_len);
-  const int t0 = ck * kExpandTokens;
-  if (t0 >= ctx) return;
-
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15, g = lane >> 4;
-  {  // stage the weight part: wave w moves rows 32w .. 32w+31, one 1 KiB row per transfer
-    const char* W = reinterpret_cast<const char*>((part ? a.W_uv : a.W_uk) + int64_t(h) * DN * DC);
-    const uint32_t base = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_char_t*)wl)));
-#pragma unroll 4
-    for (int rr = 0; rr < 32; ++rr) {
-      const int r = 32 * w + rr;
-      dma16(W + r * (DC * 2) + 16 * (lane ^ (r & 15)), base + r * (DC * 2));
-    }
-    wait_vmcnt<0>();
-    lds_barrier();
-  }
-  const char* cache = static_cast<const char*>(a.cache);
+  const int tb = int(blockIdx.x) * 32 + 8 * (threadIdx.x >> 6);  // the wave's first token, 8 | tb
+  if (tb >= ctx) return;
   const char* zero = static_cast<const char*>(a.zero_block);  // >= 1,152 zero bytes
-  const int* bt = a.block_table + int64_t(b) * a.bt_stride;
-  uint16_t* kvrow0 = a.kv + (int64_t(b) * a.H + h) * a.t_pad * kKV;
-  // A operand of MFMA (dim tile jt, K step s): row 16 jt + r16, granule 4 s + g
-  const lds_char_t* wa = (const lds_char_t*)wl + r16 * (DC * 2);
-
-  // wave w: tokens t0 + 16 kSubPerWave w + 16 st + (lane % 16); the next sub-tile's latent rows are
-  // loaded while the current one is multiplied (two register buffers, the loop unrolled by two)
-  const int tw = t0 + 16 * kSubPerWave * w;
-  // sub-tile st is one paged block: the wave's kSubPerWave block ids, read once (lane st holds id st)
-  static_assert(kSubPerWave <= 64, "one id per lane");
-  const int ids = (lane < kSubPerWave && tw + 16 * lane < ctx) ? bt[tw / BLK + lane] : -1;
-  asm volatile("" ::"v"(ids));  // complete before the row loads
-  // the latent part of one token row: 16 K steps of 8 codes per lane (8 bytes) and the row's four group
-  // scales
-  struct Brow {
-    u32x2_t c[16];
-    f32x4_t sc;
-  };
-  auto load_b = [&](int st, Brow& bq) {
-    const int tb = tw + 16 * st;
-    const int tok = tb + r16;
-    const int phys = __builtin_amdgcn_readlane(ids, st);  // st <= kSubPerWave < 64: -1 past the range
-    const bool ok = tok < ctx && unsigned(phys) < unsigned(a.num_blocks);
-    // rows past the context or of an invalid block read the zero block: no divergent loads, which
-    // would make the compiler wait for every load in flight
-    const char* crow = ok ? cache + (int64_t(phys) * BLK + tok % BLK) * kRowBytes : zero;
+  const int phys = a.block_table[int64_t(b) * a.bt_stride + tb / BLK];  // the wave's eight tokens share a block
+  const bool okb = unsigned(phys) < unsigned(a.num_blocks);
+  const char* base = okb ? static_cast<const char*>(a.cache) + (int64_t(phys) * BLK + tb % BLK) * kFp8Row : zero;
+  const int64_t rstep = okb ? kFp8Row : 0;  // the zero block stands for every row of an invalid block
+  u32x2_t cw[8];
+  float sc[8];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) bq.c[s] = *reinterpret_cast<const u32x2_t*>(crow + 32 * s + 8 * g);
-    bq.sc = *reinterpret_cast<const f32x4_t*>(crow + DC + 2 * DR);
-    return phys;
-  };
-  auto step = [&](int st, const Brow& cb, int phys) {
-    const int tb = tw + 16 * st;
-    const int tok = tb + r16;
-    f32x4_t acc[8];
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // the eight A operands of K step s + 1 are read while the MFMAs of step s run
-    u32x4_t av[2][8];
-    auto load_a = [&](int s, u32x4_t (&d)[8]) {
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt) d[jt] = *(const lds_u32x4_t*)(wa + jt * 16 * (DC * 2) + 16 * ((4 * s + g) ^ r16));
-    };
-    load_a(0, av[0]);
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {  // scale group G: K steps 4G .. 4G + 3
-      f32x4_t gacc[8];
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt) gacc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int s = 4 * G + q;
-        if (s + 1 < 16) load_a(s + 1, av[(s + 1) & 1]);
-        const u32x4_t bv = codes8(cb.c[s]);
-#pragma unroll
-        for (int jt = 0; jt < 8; ++jt) gacc[jt] = mfma32v(av[s & 1][jt], bv, gacc[jt]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt) acc[jt] += cb.sc[G] * gacc[jt];
-    }
-    // D[dim][token]: lane (token r16, g) holds dims 16 jt + 4 g .. + 3
-    if (tok < ctx) {
-      uint16_t* dst = kvrow0 + int64_t(tok) * kKV + (part ? DN + DR : 0) + 4 * g;
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt)
-        *reinterpret_cast<u32x2_t*>(dst + 16 * jt) =
-            u32x2_t{cvt_pk_bf16(acc[jt][0], acc[jt][1]), cvt_pk_bf16(acc[jt][2], acc[jt][3])};
-    }
-    if (part == 0) {  // rope keys of the 16 tokens: lane -> token lane / 4, values 16 (lane % 4) .. + 15
-      const int rt = tb + (lane >> 2);
-      if (rt < ctx) {
-        const bool rok = unsigned(phys) < unsigned(a.num_blocks);
-        const char* src = (rok ? cache + (int64_t(phys) * BLK + rt % BLK) * kRowBytes + kRopeOff : zero) + 32 * (lane & 3);
-        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src);
-        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(kvrow0 + int64_t(rt) * kKV + DN + 16 * (lane & 3));
-        dst[0] = v0;
-        dst[1] = v1;
-      }
-    }
-  };
-  if (tw >= ctx) return;
-  // groups of four sub-tiles; within a group the buffers alternate at compile time, and the
-  // prefetch is unconditional (past the wave's range it reads the zero block: lane kSubPerWave's id
-  // is -1), so that no branch guards a load
-  Brow bq[2];
-  int ph[2];
-  ph[0] = load_b(0, bq[0]);
-  for (int G = 0; G < kSubPerWave / 4; ++G) {
-    if (tw + 64 * G >= ctx) break;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int cur = 4 * G + st;
-      ph[(st + 1) & 1] = load_b(cur + 1, bq[(st + 1) & 1]);
-      if (tw + 16 * cur < ctx) step(cur, bq[st & 1], ph[st & 1]);
-    }
+  for (int i = 0; i < 8; ++i) {
+    cw[i] = *reinterpret_cast<const u32x2_t*>(base + i * rstep + 8 * lane);
+    sc[i] = *reinterpret_cast<const float*>(base + i * rstep + DC + 2 * DR + 4 * (lane >> 4));
   }
+  // rope values: lane -> token lane / 8, granule lane % 8
+  const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(base + (lane >> 3) * rstep + DC + 16 * (lane & 7));
+  uint16_t* lat = a.lat + (int64_t(b) * a.t_pad + tb) * ROW;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (tb + i >= ctx) break;
+    const u32x4_t v = codes8(cw[i]);  // the codes as bf16, exactly
+    u32x4_t y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      y[e] = cvt_pk_bf16(__uint_as_float(v[e] << 16) * sc[i], __uint_as_float(v[e] & 0xffff0000u) * sc[i]);
+    *reinterpret_cast<u32x4_t*>(lat + i * ROW + 8 * lane) = y;
+  }
+  if (tb + (lane >> 3) < ctx) *reinterpret_cast<u32x4_t*>(lat + (lane >> 3) * ROW + DC + 8 * (lane & 7)) = rv;
 }
 
 hipError_t launch_prefill_expand(PrefillArgs a, bool fp8, hipStream_t s) {
-  // bf16: a workgroup per (sequence, chunk, head); FP8: per (sequence, chunk, head, part)
-  const int64_t units = int64_t(a.batch) * (a.t_pad / kExpandTokens) * a.H * (fp8 ? 2 : 1);
-  if (units > 0x7fffffff) return hipErrorInvalidValue;
+  // a workgroup per (sequence, chunk, head)
+  const int64_t units = int64_t(a.batch) * (a.t_pad / kExpandTokens) * a.H;
+  if (units > 0x7fffffff || a.batch > 65535 || (fp8 && !a.lat)) return hipErrorInvalidValue;
   a.units = int32_t(units);
+  if (fp8) {
+    launch(prefill_dequant_fp8_kernel, dim3(a.t_pad / 32, a.batch), dim3(256), 0, s, a);
+  } else {
+    a.lat = nullptr;
+  }
   const int grid = ((a.units + 7) >> 3) << 3;
-  if (fp8)
-    launch(prefill_expand_fp8_kernel, dim3(grid), dim3(256), 0, s, a);
-  else
-    launch(prefill_expand_kernel, dim3(grid), dim3(512), 0, s, a);
+  launch(prefill_expand_kernel, dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -153,8 +153,8 @@ FP8_PREFILL_CASES = [
 @pytest.mark.parametrize("name,heads,ctxs,chunks,gamma_noise", FP8_PREFILL_CASES,
                          ids=[c[0] for c in FP8_PREFILL_CASES])
 def test_prefill_fp8_cache(name, heads, ctxs, chunks, gamma_noise):
-    """Chunked prefill over FP8 rows (the expansion reads codes x group scales) against the oracle's
-    prefill_naive over the same bytes dequantised by the oracle's format decoder."""
+    """Chunked prefill over FP8 rows (dequantised to bf16 rows, code x group scale, before the expansion)
+    against the oracle's prefill_naive over the same bytes dequantised by the oracle's format decoder."""
     w = W.custom("pf8_" + name, "bf16", heads, ctxs, q_len=1, seed=190 + heads, gamma_noise=gamma_noise)
     _say("fp8 prefill", name, "H", heads, "ctx", ctxs, "chunks", chunks)
     run = Fp8Prefill(w)
