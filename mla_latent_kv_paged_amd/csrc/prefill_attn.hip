@@ -16,7 +16,7 @@ namespace {
 // as given and applies the softmax scale to the scores.  Lane -> (row, head, granule of 8 values): eight
 // (row, head) units per wave, so that a wave reads whole 128-byte runs of q_pe; kQpUnits units per
 // workgroup, every load issued before the arithmetic.  Grid y = the sequence.
-constexpr int kQpUnits = 256;
+constexpr int kQpUnits = 128;
 __global__ __launch_bounds__(256) void prefill_qprep_kernel(PrefillArgs a) {
   const int b = blockIdx.y;
   int c0;
