@@ -8,7 +8,8 @@
 // of two ps_j if its largest entry would not fit), merged with the weights 2^(m_j - M) l_j.  A
 // split with m_j = -inf saw no token and weighs nothing.
 //
-// One workgroup per (head, 16 query rows); merged o_lat rows are staged in LDS.
+// One workgroup per (head, 16 query rows), or per (head, 64 query rows) when there are enough of those
+// to fill the chip (combine_rows_kernel, below); merged o_lat rows are staged in LDS.
 // bf16 storage: the projection is a batched MFMA GEMM computed transposed,
 //   out^T[v, n] = sum_c W_uv[h][v, c] o_lat^T[c, n]   (K = 512, 16 steps of 16x16x32 bf16),
 // with o_lat carried as an unevaluated sum of two bf16 values (hi = bf16(o), lo = bf16(o - hi)),
