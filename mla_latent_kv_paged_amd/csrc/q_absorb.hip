@@ -181,28 +181,60 @@ __device__ __forceinline__ void q_absorb_bf16_block(const QAbsorbArgs& a, int c_
         }
     }
     __syncthreads();
-    for (int t = 0; t < ntile; ++t) {
-      const int r = 16 * t + r16;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // all tiles first (lane: query row n, channels c_first + 16 t + 4g .. + 3), packed to bf16
+    uint2 pk[16];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma32v(wlds[r * 16 + ((4 * ks + g) ^ r16)], bq[ks], acc);
-      // lane holds query row n (column), channels c_first + 16 t + 4g .. +3 (rows)
-      if (nv)
-        *reinterpret_cast<uint2*>(orow + 16 * t) =
-            make_uint2(cvt_pk_bf16(acc[0] * a.qscale, acc[1] * a.qscale), cvt_pk_bf16(acc[2] * a.qscale, acc[3] * a.qscale));
+    for (int t = 0; t < 16; ++t) {
+      if (t < ntile) {
+        const int r = 16 * t + r16;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma32v(wlds[r * 16 + ((4 * ks + g) ^ r16)], bq[ks], acc);
+        pk[t] = make_uint2(cvt_pk_bf16(acc[0] * a.qscale, acc[1] * a.qscale), cvt_pk_bf16(acc[2] * a.qscale, acc[3] * a.qscale));
+      }
+    }
+    // then through LDS (every wave is done with W_uk^T), so that the rows are stored 16 contiguous bytes
+    // per lane: whole cache lines, not 8-byte pieces of 16 rows.  Wave w's rows at w * 16 * NC channels,
+    // granule gi of row r16 at gi ^ r16 (the 16 lanes of a granule column hit distinct bank groups)
+    __syncthreads();
+    uint2* ot = reinterpret_cast<uint2*>(wlds) + w * 16 * (NC / 4);  // 4 channels per uint2
+    const int gpr = NC / 8;                                          // 16-byte granules per row (32 or 16)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if (t < ntile) {
+        const int gi = 2 * t + (g >> 1);  // channels 16 t + 4 g: granule 2 t + g / 2, half g % 2
+        ot[r16 * (NC / 4) + 2 * (gi ^ (r16 & (gpr - 1))) + (g & 1)] = pk[t];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done (lgkmcnt(0)); it reads only its own rows
+    const u32x4_t* orl = reinterpret_cast<const u32x4_t*>(ot);
+    for (int e = lane; e < 16 * gpr; e += 64) {
+      const int rr = e / gpr, gi = e % gpr;
+      const int nn = rb * 64 + 16 * w + rr;
+      if (nn < a.n_q)
+        *reinterpret_cast<u32x4_t*>(qcat + (int64_t(nn) * a.H + h) * ROW + c_first + 8 * gi) =
+            orl[rr * gpr + (gi ^ (rr & (gpr - 1)))];
     }
   }
-  // RoPE part: results computed and stored after the GEMM from the values loaded above
+  // RoPE part: results computed and stored after the GEMM from the values loaded above, the thread's
+  // ppt pairs in one store (its 4 ppt contiguous bytes)
   if (rv) {
+    u32x4_t y = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (e < ppt) {
         const double x0 = bf16_to_f32(rq[e] & 0xffffu), x1 = bf16_to_f32(rq[e] >> 16);
         const float y0 = rok ? float((x0 * rc[e].x - x1 * rc[e].y) * double(a.qscale)) : __builtin_nanf("");
         const float y1 = rok ? float((x0 * rc[e].y + x1 * rc[e].x) * double(a.qscale)) : __builtin_nanf("");
-        *reinterpret_cast<uint32_t*>(ro + 2 * e) = cvt_pk_bf16(y0, y1);
+        y[e] = cvt_pk_bf16(y0, y1);
       }
     }
+    if (ppt == 4)
+      *reinterpret_cast<u32x4_t*>(ro) = y;
+    else if (ppt == 2)
+      *reinterpret_cast<u32x2_t*>(ro) = u32x2_t{y[0], y[1]};
+    else
+      *reinterpret_cast<uint32_t*>(ro) = y[0];
   }
 }
 
