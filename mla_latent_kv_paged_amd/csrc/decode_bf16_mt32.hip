@@ -58,7 +58,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   // ---- balanced partition.  Stream (b, grp) = tile group grp of sequence b, L_b steps of two
   // blocks, preceded by kPieceCost units that stand for a piece's setup; streams are ordered
   // (b, grp) and the workgroups take equal contiguous ranges of the concatenated units.  A range
-  // cuts streams into pieces; the piece of stream s done by workgroup g keeps its partial under
+  // cuts streams into pieces; the piece of stream s in range g keeps its partial under
   // id g + s (unique: between consecutive pieces g or s grows), so the pieces of a stream have
   // consecutive ids.
   constexpr int c = kPieceCost;
@@ -75,7 +75,12 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   }
   S *= n_grp;
   const int W = (S + n_wg - 1) / n_wg;
-  const int lo = int(blockIdx.x) * W;
+  // range index of this workgroup: workgroup i runs on XCD i % 8, and each XCD takes a contiguous block of
+  // ranges (when n_wg is a multiple of 8), so that the pieces of one stream, which cut consecutive ranges,
+  // mostly share an L2: their query tile and block ids come from HBM once
+  const int bid = int(blockIdx.x);
+  const int gr = (n_wg & 7) == 0 ? (bid & 7) * (n_wg >> 3) + (bid >> 3) : bid;
+  const int lo = gr * W;
   const int hi = min(lo + W, S);
   // the sequence holding unit lo: the last b whose streams start at or before lo; workgroup 0
   // also records each stream's first piece id and piece count for the combine
@@ -430,7 +435,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
   while (pos < hi) {
     const int st = pos + c;
     const int k0 = max(lo, st) - st, k1 = min(hi, st + Lb) - st;
-    if (k1 > k0) piece(b, grp, k0, k1, int(blockIdx.x) + b * n_grp + grp);
+    if (k1 > k0) piece(b, grp, k0, k1, gr + b * n_grp + grp);
     pos += Lb + c;
     if (++grp == n_grp) {
       grp = 0;
