@@ -357,8 +357,6 @@ __global__ __launch_bounds__(RW * 16) void combine_rows_kernel(CombineArgs a) {
 hipError_t launch_combine(bool bf16, const CombineArgs& a, hipStream_t s) {
   if (bf16 && a.rows_wg == 64) {
     launch(combine_rows_kernel<64>, dim3(a.H, (a.n_q + 63) / 64), dim3(64 * 16), 0, s, a);
-  } else if (bf16 && a.rows_wg == 32) {
-    launch(combine_rows_kernel<32>, dim3(a.H, (a.n_q + 31) / 32), dim3(32 * 16), 0, s, a);
   } else if (bf16) {
     dim3 grid(a.H, (a.n_q + 15) / 16, a.v_parts);
     launch(combine_bf16_kernel, dim3(grid), dim3(256), 0, s, a);

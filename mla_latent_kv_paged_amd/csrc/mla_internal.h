@@ -172,7 +172,7 @@ struct CombineArgs {
   int32_t rows_per_piece;
   int32_t n_grp;
   int32_t v_parts;        // bf16: output channels split over this many workgroups (1 or 4)
-  int32_t rows_wg;        // bf16: query rows per workgroup, 16 (combine_bf16_kernel) or 32 / 64 (combine_rows_kernel)
+  int32_t rows_wg;        // bf16: query rows per workgroup, 16 (combine_bf16_kernel) or 64 (combine_rows_kernel)
 };
 
 // The layer step's projections: Y[M, N] = X[M, K] W[N, K]^T (bf16 in, fp32 accumulation), K a
