@@ -65,6 +65,11 @@ SMALL = [
                                         seed=13)),
     ("rows64_h16_b1000", lambda: W.custom("r64s", "bf16", 16, [1 + (53 * i) % 150 for i in range(1000)], q_len=1,
                                           seed=14)),
+    # other head counts: 64 (two 32-row tiles per query), 96 (three, with two queries per sequence, and
+    # the 64-row combine)
+    ("h64_q1", lambda: W.custom("h64", "bf16", 64, [40, 300, 77, 1000], q_len=1, seed=15)),
+    ("h96_q2_rows64", lambda: W.custom("h96", "bf16", 96, [2 + (29 * i) % 200 for i in range(96)], q_len=2,
+                                       seed=16)),
 ]
 
 
