@@ -32,7 +32,7 @@ def dev_i32(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
 
 
-class GpuRun:
+class DeviceRun:
     """A workload resident on the GPU: context, NaN-poisoned pool, written cache."""
 
     def __init__(self, w: W.Workload, max_ctx=None, per_sequence_upload=False, extra_caps=0):

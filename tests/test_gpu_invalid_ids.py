@@ -12,7 +12,7 @@ from oracle import mla_fp8 as F
 from oracle import mla_oracle as O
 from workloads import mla_inputs as W
 
-from ._harness import GpuRun, compare, dev, dev_i32, oracle_full, oracle_weights
+from ._harness import DeviceRun, compare, dev, dev_i32, oracle_full, oracle_weights
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -60,7 +60,7 @@ def test_decode_out_of_range_ids(heads):
     W_uk, W_uv = oracle_weights(w)
     ref = O.decode_absorbed(w.queries(), _with_zero_block(cache), ref_bt, w.seq_lens, w.q_len, W_uk, W_uv, w.scale,
                             w.theta)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         out = run.ctx.decode(run.q, run.pool, dev_i32(bad), run.sl, run.max_ctx, q_len=w.q_len)
         torch.cuda.synchronize()
@@ -117,9 +117,8 @@ def test_prefill_out_of_range_ids(fp8):
     ref = O.prefill_naive(q, _cu(chunks), _with_zero_block(cache), ref_bt, w.seq_lens, W_uk, W_uv, w.scale, w.theta)
     if fp8:
         ctx, pool = _fp8_ctx(w), torch.from_numpy(pool8).to("cuda")
-        run = None
     else:
-        run = GpuRun(w)
+        run = DeviceRun(w)
         ctx, pool = run.ctx, run.pool
     try:
         out = ctx.prefill(dev(q, "bf16"), dev_i32(_cu(chunks)), pool, dev_i32(bad), dev_i32(w.seq_lens),

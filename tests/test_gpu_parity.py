@@ -10,7 +10,7 @@ import pytest
 from oracle import mla_oracle as O
 from workloads import mla_inputs as W
 
-from ._harness import (GpuRun, bf16_ulp_distance, compare, dev, dev_i32, oracle_all_sequences, oracle_full,
+from ._harness import (DeviceRun, bf16_ulp_distance, compare, dev, dev_i32, oracle_all_sequences, oracle_full,
                        oracle_weights)
 
 torch = pytest.importorskip("torch")
@@ -78,7 +78,7 @@ def test_small_parity(name, make):
     w = make()
     _say(name, w.storage, "H", w.num_heads, "B", w.batch, "q_len", w.q_len, "ctx", list(w.seq_lens[:8]))
     cache_ref, out_ref = oracle_full(w)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         _check_cache(run, cache_ref, w.storage)
         out = run.decode()
@@ -95,7 +95,7 @@ def test_decode_only_from_generator_pool():
     W_uk, W_uv = oracle_weights(w)
     ref = O.decode_absorbed(w.queries(), pool.astype(np.float64), w.block_table, w.seq_lens, w.q_len, W_uk, W_uv,
                             w.scale, w.theta)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         out = run.decode(pool=dev(pool, w.storage))
         compare(out, ref, w.storage, "decode-only")
@@ -179,7 +179,7 @@ def test_large_score_jump(heads, q_len):
                 n_van += d <= -40.0
     assert n_dom > 0 and n_van > 0 and keep.mean() > 0.75, (n_dom, n_van, keep.mean())
 
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         for sb in (64, 5):
             out = run.decode(pool=dev(pool, w.storage), split_blocks=sb)
@@ -276,7 +276,7 @@ def test_split_sweep_and_determinism(storage, heads, q_len):
     w = W.custom("sweep", storage, heads, [4, 37, 200, 513], q_len=q_len, seed=31)
     _say("split sweep", storage, "H", heads, "q_len", q_len)
     _, ref = oracle_full(w)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         for sb in (1, 2, 3, 5, 8, 13, 33, 0):
             out = run.decode(split_blocks=sb)
@@ -295,7 +295,7 @@ def test_16row_kernel_waves_split_sweep(waves):
     w = W.custom("w16", "bf16", 16, [1, 15, 16, 17, 200, 513, 1000, 1500], q_len=1, seed=33)
     _say("16-row kernel", "waves", waves)
     _, ref = oracle_full(w)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         for sb in (1, 2, 3, 5, 8, 13, 33, 96, 0):
             out = run.decode(split_blocks=sb, waves=waves)
@@ -311,7 +311,7 @@ def test_16row_kernel_waves_split_sweep(waves):
 def test_block_table_relabel_invariance():
     w = W.custom("relabel", "bf16", 16, [45, 130], q_len=1, seed=41)
     _say("relabel")
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         base = run.decode()
         perm = np.random.default_rng(3).permutation(w.n_blocks)
@@ -342,7 +342,7 @@ def test_full_size_every_sequence(name, make):
     Both tolerances are applied per sequence and to the whole output."""
     w = make()
     _say(name, "B", w.batch, "sum ctx", w.total_ctx, "every sequence")
-    run = GpuRun(w, per_sequence_upload=True)
+    run = DeviceRun(w, per_sequence_upload=True)
     try:
         out = run.decode()
         shape = run.ctx.last_decode_shape()
@@ -365,7 +365,7 @@ def test_f32_long_context_split_within_workspace():
     every row against the oracle."""
     w = W.custom("f32_long", "f32", 16, [40, 70000], q_len=1, seed=61)
     _say("fp32 long context", list(w.seq_lens))
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         out = run.decode()
         shape = run.ctx.last_decode_shape()
@@ -383,7 +383,7 @@ def test_f32_long_context_split_within_workspace():
 def test_abi_status_codes_on_device():
     from mla_latent_kv_paged_amd import MLAContext, MLAError
     w = W.custom("abi", "bf16", 16, [20, 40], seed=51)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         with pytest.raises(MLAError) as e:      # batch above the cap
             bt = dev_i32(np.zeros((3, 8)))
@@ -408,7 +408,7 @@ def test_profiling_helpers_on_device():
     samples after profiled decodes, and the last launch shape."""
     from mla_latent_kv_paged_amd import K_CACHE_WRITE, K_COMBINE, K_DECODE, K_Q_ABSORB
     w = W.custom("prof", "bf16", 16, [300, 40], seed=52)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         run.ctx.profile_enable(True)
         for _ in range(3):

@@ -15,7 +15,7 @@ from oracle import mla_fp8 as F
 from oracle import mla_oracle as O
 from workloads import mla_inputs as W
 
-from ._harness import GpuRun, compare, dev, dev_i32, oracle_weights
+from ._harness import DeviceRun, compare, dev, dev_i32, oracle_weights
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,7 @@ def test_prefill_parity(name, heads, ctxs, chunks):
     w = W.custom("pf_" + name, "bf16", heads, ctxs, q_len=1, seed=90 + heads)
     _say("prefill", name, "H", heads, "ctx", ctxs, "chunks", chunks)
     ref = _oracle_prefill(w, chunks)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         out = _run_prefill(run, chunks)
         compare(out, ref, "bf16", f"prefill {name}")
@@ -86,7 +86,7 @@ def test_prefill_gamma_and_long_fresh_chunk():
     w = W.custom("pf_long", "bf16", 16, [2048], q_len=1, seed=95, gamma_noise=0.1)
     _say("prefill long fresh chunk 2048, gamma noise")
     ref = _oracle_prefill(w, [2048])
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         compare(_run_prefill(run, [2048]), ref, "bf16", "prefill 2048 fresh")
     finally:
@@ -100,7 +100,7 @@ def test_prefill_one_token_chunks_match_decode():
     w = W.custom("pf_dec", "bf16", 16, [700, 33, 258], q_len=1, seed=96)
     _say("prefill one-token chunks vs decode")
     ref = _oracle_prefill(w, [1, 1, 1])
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         pf = _run_prefill(run, [1, 1, 1])
         dc = run.ctx.decode(dev(w.chunk_queries([1, 1, 1]), "bf16"), run.pool, run.bt, run.sl, run.max_ctx, q_len=1)
@@ -192,7 +192,7 @@ def test_prefill_status_codes():
     context bound, and an fp32 context (unsupported) are refused before any launch."""
     from mla_latent_kv_paged_amd import MLAError, MLAContext
     w = W.custom("pf_err", "bf16", 16, [40], q_len=1, seed=97)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     cu = _cu([8])
     q = dev(w.chunk_queries([8]), "bf16")
     try:
@@ -235,7 +235,7 @@ def test_prefill_full_size_sampled():
     ref_last = O.prefill_naive(q[last_rows], cu_r, cache, w.block_table, w.seq_lens, W_uk, W_uv, w.scale, w.theta)
     ref_first = O.prefill_naive(q[first_rows], cu_r, cache, w.block_table, np.full(B, R), W_uk, W_uv, w.scale,
                                 w.theta)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         out = _run_prefill(run, [S] * B)
         compare(out[torch.from_numpy(last_rows).cuda()], ref_last, "bf16", "prefill full size, last rows")

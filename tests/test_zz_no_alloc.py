@@ -11,7 +11,7 @@ from oracle import mla_fp8 as F
 from oracle import mla_oracle as O
 from workloads import mla_inputs as W
 
-from ._harness import GpuRun, compare, dev, dev_i32, oracle_full, oracle_weights
+from ._harness import DeviceRun, compare, dev, dev_i32, oracle_full, oracle_weights
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -51,7 +51,7 @@ def test_noalloc_matches_decode(label, storage, heads, q_len, first, second):
     w = W.custom(f"na_{label}", storage, heads, first, q_len=q_len, seed=301)
     _say("noalloc", label, "first", first, "second", second)
     cache_oracle, ref_oracle = oracle_full(w)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         a, b = _both(run, w, run.q, run.bt, run.sl, run.max_ctx)
         assert torch.equal(a, b), f"{label}: first call differs from mla_decode"
