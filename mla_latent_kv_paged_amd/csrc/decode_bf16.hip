@@ -25,8 +25,9 @@
 //    and each wave keeps it in registers as the B operand of the score MFMA.
 //  * Scores S^T[16 tok x 16 rows] = C Q^T on v_mfma_f32_16x16x32_bf16: the A operand of MFMA k
 //    (token l%16, granule 4k + l/16) is one ds_read_b128 at a per-lane base + 512 k.  Lane l then
-//    holds row l%16 at tokens 4(l/16)..+3, so the row max needs two cross-lane steps and the
-//    softmax state stays per lane.
+//    holds row l%16 at tokens 4(l/16)..+3, so the softmax state stays per lane; the row max (two
+//    lane-pair steps, v_permlane16_swap and v_permlane32_swap) is formed only when a lane's max passes
+//    the slack.
 //  * P.C on v_mfma_f32_16x16x16_bf16: A = C^T tile jj (16 channels x 16 tokens) from one
 //    ds_read_b64_tr_b16 at a per-lane base + 256 jj; B = P^T is exactly the score registers
 //    rounded to bf16.  The accumulator lands with row r = lane%16 again, so the online-softmax
@@ -241,11 +242,10 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
       sv[t] = (kb * BLK + 4 * g + t < L) ? sc[t] : -INFINITY;
       mb = fmaxf(mb, sv[t]);
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    // lazy rescale: wave-uniform branch taken only when some row's max grew past the slack
+    // lazy rescale: wave-uniform branch taken only when some row's max grew past the slack (some lane's
+    // max did); the row maximum over the row's four lanes is formed only then
     if (__any(mb > m + kMaxSlack)) {
-      const float mn = fmaxf(m, mb);
+      const float mn = fmaxf(m, xor32_max(xor16_max(mb)));
       const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
       lsum *= alpha;
 #pragma unroll
@@ -284,8 +284,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   }
 
   // merge the two waves' states: row max, rescale, fixed-order sum through LDS
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = xor32_add(xor16_add(lsum));
   if (g == 0) {
     m_lds[w][r16] = m;
     l_lds[w][r16] = lsum;
@@ -327,8 +326,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(DecodeArgs a) {
   for (int t = 0; t < kTilesPerWave; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(fin[t][e]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = xor32_max(xor16_max(mx));
   if (g == 0) x_lds[w][r16] = mx;
   __syncthreads();
   const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;

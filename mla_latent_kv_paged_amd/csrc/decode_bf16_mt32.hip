@@ -382,7 +382,7 @@ __global__ __launch_bounds__(T * 64) void decode_bf16_mt32_kernel(DecodeArgs a) 
     // straight from the accumulator layout, a store touches 32 rows with 16 bytes each.  Tile of
     // wave w: 32 rows x 1 KB at w * 32 KB, granule G of row r at slot G ^ r.
     mfma_drain();
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum = xor32_add(lsum);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     // divided by a power of two when the row's largest |o| would not fit fp16 (the row's values
     // sit in lanes r32 and r32 + 32)

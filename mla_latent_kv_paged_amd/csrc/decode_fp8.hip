@@ -239,8 +239,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
       ml = fmaxf(ml, sv[t]);
     }
     if (__any(ml > m + kMaxSlack)) {  // rare: a score rose by more than the slack above m
-      float mb = fmaxf(ml, __shfl_xor(ml, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const float mb = xor32_max(xor16_max(ml));
       const float mn = fmaxf(m, mb);
       if (!__all(m == -INFINITY)) {  // something accumulated: rescale it to the new reference
         const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
@@ -283,8 +282,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
   // merge of the waves: every wave leaves its 32 tiles in the rings, wave w sums tiles
   // TPW w .. TPW w + TPW - 1 over the waves in wave order
   mfma_drain();
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = xor32_add(xor16_add(lsum));
   if (g == 0) {
     m_lds[w][r16] = m;
     l_lds[w][r16] = lsum;
@@ -316,8 +314,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeArgs a) {
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(fin[t][e]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = xor32_max(xor16_max(mx));
   if (g == 0) x_lds[w][r16] = mx;
   __syncthreads();
   float rmx = 0.f;

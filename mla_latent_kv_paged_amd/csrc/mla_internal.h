@@ -374,6 +374,22 @@ __device__ __forceinline__ void mfma32x32_acc(f32x16_t& acc, u32x4_t a, u32x4_t 
 // wait states after the last such MFMA before VALU reads its accumulator (> 18 for 16 passes)
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+// Reductions over the lane pairs (l, l ^ 16) and (l, l ^ 32) of a wave with v_permlane16_swap and
+// v_permlane32_swap (VALU only; a shuffle is an LDS round trip).  Swapping a value with itself leaves
+// lane l holding the pair's two values, so both lanes of a pair compute the same result.
+__device__ __forceinline__ f32x2_t lane_pair16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2_t{__uint_as_float(s[0]), __uint_as_float(s[1])};
+}
+__device__ __forceinline__ f32x2_t lane_pair32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2_t{__uint_as_float(s[0]), __uint_as_float(s[1])};
+}
+__device__ __forceinline__ float xor16_max(float x) { const f32x2_t p = lane_pair16(x); return fmaxf(p[0], p[1]); }
+__device__ __forceinline__ float xor32_max(float x) { const f32x2_t p = lane_pair32(x); return fmaxf(p[0], p[1]); }
+__device__ __forceinline__ float xor16_add(float x) { const f32x2_t p = lane_pair16(x); return p[0] + p[1]; }
+__device__ __forceinline__ float xor32_add(float x) { const f32x2_t p = lane_pair32(x); return p[0] + p[1]; }
+
 // acc *= f for an accumulator vector held in AGPRs, element by element where it is called (a plain
 // multiply lets the register allocator keep a VGPR copy of every tile, refreshed each iteration).
 // The caller drains in-flight MFMAs that write acc before calling.
