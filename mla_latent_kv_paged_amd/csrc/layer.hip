@@ -198,8 +198,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void proj_gemm_small_kernel(ProjAr
     red[w][t][lane] = acc[t];
     if (a.norm) {
       float v = ss[t];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
+      v = xor32_add(xor16_add(v));
       if (g == 0) ssr[w][t][r16] = v;
     }
   }

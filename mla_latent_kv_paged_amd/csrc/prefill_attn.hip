@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if (__any(ml[t] > thr[t])) {
-        const float mn = fmaxf(m[t], fmaxf(ml[t], __shfl_xor(ml[t], 32, 64)));  // -inf: nothing visible yet
+        const float mn = fmaxf(m[t], xor32_max(ml[t]));  // -inf: nothing visible yet
         if (mn != -INFINITY) {
           const float alpha = (m[t] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[t] - mn);
           lsum[t] *= alpha;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   mfma_drain();
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const float l = lsum[t] + __shfl_xor(lsum[t], 32, 64);
+    const float l = xor32_add(lsum[t]);
     const int rw = rw0 + 32 * t + l32;
     if (rw < n) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
